@@ -1,0 +1,214 @@
+"""Throughput of the ternary projection's forward + backward on one MI355X.
+
+One step = for every projection of one layer of the workload: materialize
+(q -> 2-bit tern), forward (Y), input gradient (dX) and weight-side gradients
+(gq, sgrad), all through the C ABI on one stream, inputs already resident in
+HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "ternary_weight_linear_tern_amd", "csrc", "tern_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def kernel_src_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large", choices=["rwkv_small", "mid", "large", "largest"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=24, help="oracle sample: token rows per projection")
+    ap.add_argument("--cpu-cols", type=int, default=6, help="oracle sample: output columns per projection")
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import ternary_weight_linear_tern_amd as tl
+
+    w = synth.WORKLOADS[a.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    t0 = time.time()
+    projs = []
+    for i, (name, n_in, n_out) in enumerate(w.projs):
+        p = synth.workload_inputs(w, i)
+        d = dict(name=name, n_in=n_in, n_out=n_out, X=to_dev(p.X), dY=to_dev(p.dY), q=to_dev(p.q),
+                 scale=to_dev(p.scale), theta=p.theta)
+        d["packed"] = tl.empty_packed(n_in, n_out)
+        d["Y"] = torch.empty((w.T, n_out), dtype=torch.float32, device=dev)
+        d["dX"] = torch.empty((w.T, n_in), dtype=torch.float32, device=dev)
+        d["gq"] = torch.empty((n_in, n_out), dtype=torch.float32, device=dev)
+        d["sgrad"] = torch.empty((n_out,), dtype=torch.float32, device=dev)
+        d["ws"] = tl.empty_workspace(w.T, n_in, n_out, d["X"].dtype)
+        d["host"] = p if not a.no_cpu_baseline else None
+        projs.append(d)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t0:.1f}s: workload {w.name} T={w.T} "
+          f"projections {[(d['name'], d['n_in'], d['n_out']) for d in projs]}", file=sys.stderr, flush=True)
+
+    PARTS = ("materialize", "fwd", "bwd_dx", "bwd_dw")
+
+    def step(evs=None):
+        for j, d in enumerate(projs):
+            if evs is not None:
+                evs[j][0].record(stream)
+            tl.tern_materialize(d["q"], d["theta"], d["packed"], stream)
+            if evs is not None:
+                evs[j][1].record(stream)
+            tl.tern_linear_fwd(d["X"], d["packed"], d["scale"], d["Y"], stream)
+            if evs is not None:
+                evs[j][2].record(stream)
+            tl.tern_linear_bwd_dx(d["dY"], d["packed"], d["scale"], d["dX"], stream=stream)
+            if evs is not None:
+                evs[j][3].record(stream)
+            tl.tern_linear_bwd_dw(d["X"], d["dY"], d["packed"], d["scale"], d["gq"], d["sgrad"], d["ws"],
+                                  stream)
+            if evs is not None:
+                evs[j][4].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: events on the stream every kernel is launched on
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in projs] for _ in range(a.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(a.steps):
+        step(evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / a.steps
+
+    part_ms = {p: 0.0 for p in PARTS}
+    for k in range(a.steps):
+        for j in range(len(projs)):
+            for pi, pname in enumerate(PARTS):
+                part_ms[pname] += evs[k][j][pi].elapsed_time(evs[k][j][pi + 1])
+    part_ms = {k: v / a.steps for k, v in part_ms.items()}  # per step, summed over projections
+
+    flops_step = w.flops
+    gemm_flops = {p: 2.0 * w.T * w.sum_in_out for p in ("fwd", "bwd_dx", "bwd_dw")}
+    tflops = flops_step / (ms_per_step * 1e-3) / 1e12
+    tokens_per_s = w.T / (ms_per_step * 1e-3)
+    dt = w.act
+    peak = PEAK_TFLOPS[dt]
+
+    # dominant kernel: the GEMM entry point with the largest share of the step
+    dom = max(("fwd", "bwd_dx", "bwd_dw"), key=lambda p: part_ms[p])
+    dom_kernels = {"fwd": "gemm_kernel<MODE_FWD>", "bwd_dx": "gemm_kernel<MODE_DX>",
+                   "bwd_dw": "gemm_kernel<MODE_DW> (+ split-K and sgrad reductions)"}[dom]
+    achieved = gemm_flops[dom] / (part_ms[dom] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            ent = tr.get("entries", {}).get(f"{w.name}/{dom}")
+            if ent and tr.get("kernel_src_sha256_16") == kernel_src_hash():
+                traffic = ent["bytes_per_step"]
+        except Exception:  # noqa: BLE001 - a stale or malformed file means no counter data
+            traffic = None
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom_kernels,
+                "flops_per_step": gemm_flops[dom], "ms_per_step": round(part_ms[dom], 4)}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(w, projs, a.cpu_rows, a.cpu_cols)
+
+    line = {
+        "metric": "ternary-linear fwd+bwd TFLOP/s and tokens/s at d=2048; % of MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T,
+                   "projections": [[n, i, o] for n, i, o in w.projs],
+                   "theta": w.theta, "q": w.q_law, "scale": w.scale_law, "act": w.act},
+        "tokens_per_s": round(tokens_per_s, 1),
+        "mfma_frac": round(tflops / peak, 4),
+        "flops_per_step": flops_step,
+        "part_ms_per_step": {k: round(v, 4) for k, v in part_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, projs, n_rows, n_cols):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    n_rows token rows of Y and dX and n_cols output columns of gq / sgrad per
+    projection.  Reported as the oracle's throughput (TFLOP/s) and the tokens/s
+    of a full step at that rate."""
+    import oracle
+    import synth
+
+    o = oracle.get()
+    flops = 0.0
+    t0 = time.perf_counter()
+    for i, d in enumerate(projs):
+        p = d["host"]
+        rows = synth.sample_indices(synth.stream_seed(91, w.config_id, i, 0), n_rows, w.T)
+        cols = synth.sample_indices(synth.stream_seed(91, w.config_id, i, 1), n_cols, d["n_out"])
+        o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows)
+        o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows)
+        o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
+        flops += 2.0 * 2 * rows.size * d["n_in"] * d["n_out"] + 2.0 * w.T * d["n_in"] * cols.size
+    sec = time.perf_counter() - t0
+    rate = flops / sec
+    full_s = w.flops / rate
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": o.num_threads(), "kind": "oracle",
+            "sample": f"{n_rows} token rows of Y and dX and {n_cols} output columns of gq/sgrad per "
+                      f"projection, all {len(projs)} projections of {w.name}; {sec:.1f}s",
+            "seconds": round(sec, 2), "extrapolated_step_s": round(full_s, 1),
+            "tokens_per_s": round(w.T / full_s, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * tern.h -- C ABI of libtern, the MI355X (gfx950) forward and backward of the
+ * SR4 ternary projection.
+ *
+ * The method (page "train_gpu.cu", Foundry cuda_kernels: header comment on the
+ * optimizer split and the "device glue kernels" section):
+ *   - a ternary projection keeps an int4 accumulator q (int8 storage) and a
+ *     per-output-column fp32 scale;
+ *   - tern = sign(q) where |q| >= theta, else 0 (tg_tern_from_q; the trainer
+ *     uses theta = SR4_THETA = 2 and clamps q to +-SR4_Q_CLAMP = 7);
+ *   - W_eff[r, c] = scale[c] * tern[r, c] on a row-major [in, out] matrix
+ *     (tg_apply_scale; rows = input dim, cols = output dim per rows_of);
+ *   - forward Y = X . W_eff; backward dX = dY . W_eff^T, the weight gradient
+ *     G = X^T . dY, gq = G * scale[c] (tg_gq) and the scale gradient
+ *     sgrad[c] = sum_r G[r, c] * tern[r, c] (tg_scale_grad).
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller: contiguous,
+ *     row-major, 16-byte aligned.  The library allocates nothing, frees
+ *     nothing, keeps no state between calls and never synchronises.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued on it in order; results are ready when the caller's
+ *     next synchronisation on that stream returns.
+ *   - Inputs are only read; outputs are fully overwritten (nothing is
+ *     accumulated into them).
+ *   - Return value: TERN_OK (0) or a negative TERN_ERR_* code.  Arguments are
+ *     validated before anything is enqueued; on an error nothing is enqueued.
+ *     A device fault after a successful enqueue surfaces at the caller's next
+ *     synchronisation, as for any HIP launch.
+ *   - Shapes: T (tokens), in, out >= 0; in and out must be multiples of 8 so
+ *     that every activation row starts 16-byte aligned.  Zero sizes are valid
+ *     and give the mathematically right (possibly all-zero) outputs.
+ *   - Outputs may not overlap inputs or each other (TERN_ERR_ALIAS).
+ *   - Non-finite inputs give unspecified (but memory-safe) outputs.
+ */
+#ifndef TERN_H
+#define TERN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define TERN_F32  0  /* IEEE binary32 */
+#define TERN_BF16 1  /* bfloat16 (upper half of a binary32) */
+
+/* status codes */
+#define TERN_OK             0
+#define TERN_ERR_NULL      -1  /* a required pointer is NULL */
+#define TERN_ERR_SHAPE     -2  /* negative size, in or out not a multiple of 8, or too large */
+#define TERN_ERR_THETA     -3  /* theta outside [1, 127] */
+#define TERN_ERR_DTYPE     -4  /* unsupported element type combination */
+#define TERN_ERR_ALIGN     -5  /* a pointer is not 16-byte aligned */
+#define TERN_ERR_WORKSPACE -6  /* workspace missing or smaller than required */
+#define TERN_ERR_ALIAS     -7  /* an output overlaps an input or another output */
+#define TERN_ERR_HIP       -8  /* the HIP runtime refused a launch */
+
+/* Number of uint32 words in the packed ternary form of an [in, out] matrix:
+ * in * ceil(out / 16).  Returns -1 for negative sizes. */
+int64_t tern_packed_words(int64_t in, int64_t out);
+
+/*
+ * tern_materialize -- ternarise q and store it 2-bit packed.
+ *   q           int8 [in, out], read only.  Any int8 value is accepted; the
+ *               dead-zone rule is applied as is (the +-7 clamp belongs to the
+ *               optimizer, not to this step).
+ *   theta       dead-zone threshold, 1 <= theta <= 127 (the trainer uses 2).
+ *   tern_packed uint32 [in, ceil(out/16)], written.  Code of (r, c): 00 = 0,
+ *               01 = +1, 11 = -1 (10 is never written), at bits
+ *               2*(c % 16) .. 2*(c % 16)+1 of word r*ceil(out/16) + c/16, least
+ *               significant bits first; padding codes of a partial last word
+ *               are 00.  One packed buffer serves the forward and the backward
+ *               of the same step.
+ * Errors: NULL, SHAPE, THETA, ALIGN, ALIAS, HIP.
+ */
+int tern_materialize(const int8_t *q, int64_t in, int64_t out, int32_t theta,
+                     uint32_t *tern_packed, void *stream);
+
+/*
+ * tern_linear_fwd -- Y = X . W_eff with W_eff[r, c] = scale[c] * tern[r, c].
+ *   X           [T, in] of act_dtype (TERN_F32 or TERN_BF16).
+ *   tern_packed uint32 [in, ceil(out/16)] from tern_materialize.
+ *   scale       fp32 [out].
+ *   Y           [T, out] of y_dtype: TERN_F32, or TERN_BF16 (round to nearest
+ *               even of the fp32 result) when act_dtype is TERN_BF16.
+ * Arithmetic: products of X with +-1/0 accumulate in fp32 on the matrix cores;
+ * the scale multiplies each fp32 column sum once.
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, HIP.
+ */
+int tern_linear_fwd(const void *X, int32_t act_dtype, const uint32_t *tern_packed,
+                    const float *scale, int64_t T, int64_t in, int64_t out,
+                    void *Y, int32_t y_dtype, void *stream);
+
+/*
+ * tern_linear_bwd_workspace_bytes -- device workspace (bytes) that
+ * tern_linear_bwd needs for these sizes and this activation type.  Returns
+ * 0 for invalid sizes.  The value depends only on its arguments.
+ */
+size_t tern_linear_bwd_workspace_bytes(int64_t T, int64_t in, int64_t out, int32_t act_dtype);
+
+/*
+ * tern_linear_bwd -- all gradients of the projection.
+ *   X, dY       [T, in] and [T, out] of act_dtype (TERN_F32 or TERN_BF16).
+ *   tern_packed, scale  as for tern_linear_fwd.
+ *   dX          [T, in]  = dY . W_eff^T, dx_dtype must be TERN_F32.
+ *   gq          fp32 [in, out] = (X^T . dY)[r, c] * scale[c].
+ *   sgrad       fp32 [out]     = sum_r (X^T . dY)[r, c] * tern[r, c].
+ *   workspace   device scratch of at least
+ *               tern_linear_bwd_workspace_bytes(T, in, out, act_dtype) bytes
+ *               (may be NULL when that is 0).  Its contents on entry are
+ *               ignored and on return are unspecified.
+ * Arithmetic: fp32 accumulation on the matrix cores.  With bf16 activations
+ * the scale is folded into the bf16 B operand of the dX product as
+ * +-bf16(scale[c]) (round to nearest even), since the scale sits on that
+ * product's reduction index.  sgrad is summed in a fixed order (per tile, then
+ * tiles in ascending row order, final sum in f64), so repeated calls on the
+ * same inputs give bitwise-identical results.
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, ALIAS, HIP.
+ */
+int tern_linear_bwd(const void *X, const void *dY, int32_t act_dtype,
+                    const uint32_t *tern_packed, const float *scale,
+                    int64_t T, int64_t in, int64_t out,
+                    void *dX, int32_t dx_dtype, float *gq, float *sgrad,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * tern_linear_bwd_dx -- only the input gradient of tern_linear_bwd:
+ *   dX [T, in] (TERN_F32) = dY . W_eff^T.  Same argument rules; no workspace.
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, HIP.
+ */
+int tern_linear_bwd_dx(const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
+                       const float *scale, int64_t T, int64_t in, int64_t out,
+                       void *dX, int32_t dx_dtype, void *stream);
+
+/*
+ * tern_linear_bwd_dw -- only the weight-side gradients of tern_linear_bwd:
+ *   gq [in, out] and sgrad [out] as defined there, with the same workspace
+ *   (tern_linear_bwd_workspace_bytes).  tern_linear_bwd is exactly
+ *   tern_linear_bwd_dx followed by tern_linear_bwd_dw on the same stream.
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, ALIAS, HIP.
+ */
+int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype,
+                       const uint32_t *tern_packed, const float *scale,
+                       int64_t T, int64_t in, int64_t out,
+                       float *gq, float *sgrad, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *tern_status_str(int status);
+
+/* Library version string (static). */
+const char *tern_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TERN_H */

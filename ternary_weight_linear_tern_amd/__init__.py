@@ -1,0 +1,183 @@
+"""Python binding of libtern, the MI355X forward and backward of the SR4
+ternary projection (C ABI in include/tern.h).
+
+The functions below carry the C entry points' names and only marshal
+arguments: torch tensors (device memory) become raw pointers, the current HIP
+stream becomes the stream handle, and a nonzero status becomes a ``TernError``.
+Every computation runs in the HIP kernels of libtern.so; there is no fallback.
+If the library has not been built, the first call raises.
+
+Build it in-tree with ``python -m ternary_weight_linear_tern_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtern.so")
+
+TERN_F32 = 0
+TERN_BF16 = 1
+
+STATUS = {
+    0: "TERN_OK", -1: "TERN_ERR_NULL", -2: "TERN_ERR_SHAPE", -3: "TERN_ERR_THETA",
+    -4: "TERN_ERR_DTYPE", -5: "TERN_ERR_ALIGN", -6: "TERN_ERR_WORKSPACE", -7: "TERN_ERR_ALIAS",
+    -8: "TERN_ERR_HIP",
+}
+
+# Every symbol include/tern.h declares: name -> (restype, argtypes)
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+SIGNATURES = {
+    "tern_packed_words": (_i64, [_i64, _i64]),
+    "tern_materialize": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
+    "tern_linear_fwd": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp]),
+    "tern_linear_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "tern_linear_bwd": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp,
+                                       _vp, _vp, _sz, _vp]),
+    "tern_linear_bwd_dx": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp]),
+    "tern_linear_bwd_dw": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
+                                          _vp, _sz, _vp]),
+    "tern_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "tern_version": (ctypes.c_char_p, []),
+}
+
+
+class TernError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({tern_status_str(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtern.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m ternary_weight_linear_tern_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libtern must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _act_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TERN_BF16
+    if t.dtype == torch.float32:
+        return TERN_F32
+    raise TypeError(f"activation dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise TernError(fn, rc)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def tern_status_str(status: int) -> str:
+    return lib().tern_status_str(int(status)).decode()
+
+
+def tern_version() -> str:
+    return lib().tern_version().decode()
+
+
+def tern_packed_words(n_in: int, n_out: int) -> int:
+    return int(lib().tern_packed_words(n_in, n_out))
+
+
+def tern_linear_bwd_workspace_bytes(T: int, n_in: int, n_out: int, act_dtype) -> int:
+    code = act_dtype if isinstance(act_dtype, int) else (
+        TERN_BF16 if act_dtype == torch.bfloat16 else TERN_F32)
+    return int(lib().tern_linear_bwd_workspace_bytes(T, n_in, n_out, code))
+
+
+def tern_materialize(q: torch.Tensor, theta: int, tern_packed: torch.Tensor, stream=None) -> None:
+    """q int8 [in, out] -> tern_packed int32/uint32 [in, ceil(out/16)]."""
+    n_in, n_out = q.shape
+    rc = lib().tern_materialize(_ptr(q), n_in, n_out, int(theta), _ptr(tern_packed), _stream(stream))
+    _check("tern_materialize", rc)
+
+
+def tern_linear_fwd(X: torch.Tensor, tern_packed: torch.Tensor, scale: torch.Tensor, Y: torch.Tensor,
+                    stream=None) -> None:
+    """Y [T, out] (fp32 or bf16) = X [T, in] . (scale * tern)."""
+    T, n_in = X.shape
+    n_out = scale.shape[0]
+    rc = lib().tern_linear_fwd(_ptr(X), _act_code(X), _ptr(tern_packed), _ptr(scale), T, n_in, n_out,
+                               _ptr(Y), _act_code(Y), _stream(stream))
+    _check("tern_linear_fwd", rc)
+
+
+def tern_linear_bwd(X, dY, tern_packed, scale, dX, gq, sgrad, workspace, stream=None) -> None:
+    T, n_in = X.shape
+    n_out = scale.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().tern_linear_bwd(_ptr(X), _ptr(dY), _act_code(X), _ptr(tern_packed), _ptr(scale), T,
+                               n_in, n_out, _ptr(dX), _act_code(dX), _ptr(gq), _ptr(sgrad),
+                               _ptr(workspace), ws_bytes, _stream(stream))
+    _check("tern_linear_bwd", rc)
+
+
+def tern_linear_bwd_dx(dY, tern_packed, scale, dX, n_in: int | None = None, stream=None) -> None:
+    T, n_out = dY.shape
+    n_in = dX.shape[1] if n_in is None else n_in
+    rc = lib().tern_linear_bwd_dx(_ptr(dY), _act_code(dY), _ptr(tern_packed), _ptr(scale), T, n_in,
+                                  n_out, _ptr(dX), _act_code(dX), _stream(stream))
+    _check("tern_linear_bwd_dx", rc)
+
+
+def tern_linear_bwd_dw(X, dY, tern_packed, scale, gq, sgrad, workspace, stream=None) -> None:
+    T, n_in = X.shape
+    n_out = scale.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().tern_linear_bwd_dw(_ptr(X), _ptr(dY), _act_code(X), _ptr(tern_packed), _ptr(scale), T,
+                                  n_in, n_out, _ptr(gq), _ptr(sgrad), _ptr(workspace), ws_bytes,
+                                  _stream(stream))
+    _check("tern_linear_bwd_dw", rc)
+
+
+# ---------------------------------------------------------------------------
+# allocation helpers (torch owns the memory; the library never allocates)
+# ---------------------------------------------------------------------------
+
+def empty_packed(n_in: int, n_out: int, device="cuda") -> torch.Tensor:
+    return torch.empty((n_in, (n_out + 15) // 16), dtype=torch.int32, device=device)
+
+
+def empty_workspace(T: int, n_in: int, n_out: int, act_dtype, device="cuda") -> torch.Tensor:
+    nbytes = tern_linear_bwd_workspace_bytes(T, n_in, n_out, act_dtype)
+    return torch.empty((max(nbytes, 16) // 16, 16), dtype=torch.uint8, device=device)

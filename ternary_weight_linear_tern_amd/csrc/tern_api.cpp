@@ -1,0 +1,247 @@
+// tern_api.cpp -- the C ABI of libtern (declared in include/tern.h).
+//
+// Each entry point validates its arguments (HIP-free checks from tern_plan),
+// plans the launches and enqueues them on the caller's stream.  Nothing here
+// allocates, synchronises or keeps state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tern.h"
+#include "tern_kernels.h"
+#include "tern_plan.h"
+
+using namespace tern;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+size_t esize(int32_t dt) { return dt == TERN_BF16 ? 2 : 4; }
+bool act_ok(int32_t dt) { return dt == TERN_F32 || dt == TERN_BF16; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TERN_OK : TERN_ERR_HIP; }
+
+struct Buf {
+    const void *p;
+    size_t n;
+};
+
+// Any output overlapping any other listed buffer?
+bool any_alias(const Buf *outs, int nout, const Buf *ins, int nin) {
+    for (int i = 0; i < nout; i++) {
+        for (int j = i + 1; j < nout; j++)
+            if (ranges_overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return true;
+        for (int j = 0; j < nin; j++)
+            if (ranges_overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return true;
+    }
+    return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tern_version(void) { return "libtern 0.1 (gfx950)"; }
+
+const char *tern_status_str(int status) {
+    switch (status) {
+        case TERN_OK: return "ok";
+        case TERN_ERR_NULL: return "null pointer";
+        case TERN_ERR_SHAPE: return "invalid shape (negative, in/out not a multiple of 8, or too large)";
+        case TERN_ERR_THETA: return "theta outside [1, 127]";
+        case TERN_ERR_DTYPE: return "unsupported element type";
+        case TERN_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case TERN_ERR_WORKSPACE: return "workspace missing or too small";
+        case TERN_ERR_ALIAS: return "output overlaps an input or another output";
+        case TERN_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int64_t tern_packed_words(int64_t in, int64_t out) {
+    if (in < 0 || out < 0) return -1;
+    return in * ((out + 15) / 16);
+}
+
+int tern_materialize(const int8_t *q, int64_t in, int64_t out, int32_t theta, uint32_t *tern_packed,
+                     void *stream) {
+    if (in < 0 || out < 0 || in > kMaxInOut || out > kMaxInOut) return TERN_ERR_SHAPE;
+    if (theta < 1 || theta > 127) return TERN_ERR_THETA;
+    if (in == 0 || out == 0) return TERN_OK;
+    if (!q || !tern_packed) return TERN_ERR_NULL;
+    if (!aligned4(tern_packed)) return TERN_ERR_ALIGN;
+    const size_t qb = (size_t)in * (size_t)out;
+    const size_t pb = (size_t)tern_packed_words(in, out) * 4;
+    if (ranges_overlap(q, qb, tern_packed, pb)) return TERN_ERR_ALIAS;
+    // the 16-byte vector path needs every row of q 16-byte aligned
+    const bool vec = out % 16 == 0 && aligned16(q);
+    return hip_status(launch_materialize(q, in, out, theta, vec, tern_packed, (hipStream_t)stream));
+}
+
+int tern_linear_fwd(const void *X, int32_t act_dtype, const uint32_t *tern_packed, const float *scale,
+                    int64_t T, int64_t in, int64_t out, void *Y, int32_t y_dtype, void *stream) {
+    int rc = validate_shape(T, in, out);
+    if (rc) return rc;
+    if (!act_ok(act_dtype)) return TERN_ERR_DTYPE;
+    if (!(y_dtype == TERN_F32 || (y_dtype == TERN_BF16 && act_dtype == TERN_BF16))) return TERN_ERR_DTYPE;
+    const size_t xb = (size_t)T * in * esize(act_dtype);
+    const size_t yb = (size_t)T * out * esize(y_dtype);
+    const size_t pb = (size_t)tern_packed_words(in, out) * 4;
+    const size_t sb = (size_t)out * 4;
+    if ((xb && !X) || (pb && !tern_packed) || (sb && !scale) || (yb && !Y)) return TERN_ERR_NULL;
+    if ((xb && !aligned16(X)) || (sb && !aligned16(scale)) || (yb && !aligned16(Y)) ||
+        (pb && !aligned4(tern_packed)))
+        return TERN_ERR_ALIGN;
+    const Buf outs[] = {{Y, yb}};
+    const Buf ins[] = {{X, xb}, {tern_packed, pb}, {scale, sb}};
+    if (any_alias(outs, 1, ins, 3)) return TERN_ERR_ALIAS;
+    hipStream_t st = (hipStream_t)stream;
+    if (yb == 0) return TERN_OK;
+    if (in == 0) return hip_status(launch_zero(Y, yb, st));  // empty sum
+
+    const bool bf = act_dtype == TERN_BF16;
+    GemmPlan p = plan_gemm(MODE_FWD, T, in, out, bf);
+    GemmArgs a{};
+    a.act0 = X;
+    a.packed = tern_packed;
+    a.scale = scale;
+    a.out_ptr = Y;
+    a.M = (int)p.M; a.N = (int)p.N; a.K = (int)p.K;
+    a.tiles_m = (int)p.tiles_m; a.tiles_n = (int)p.tiles_n;
+    a.splits = (int)p.splits; a.kps = (int)p.k_per_split;
+    a.in = (int)in; a.out = (int)out; a.wpr = (int)((out + 15) / 16); a.T = (int)T;
+    a.y_bf16 = y_dtype == TERN_BF16;
+    return hip_status(launch_gemm(p, bf, a, st));
+}
+
+size_t tern_linear_bwd_workspace_bytes(int64_t T, int64_t in, int64_t out, int32_t act_dtype) {
+    if (validate_shape(T, in, out) != TERN_OK || !act_ok(act_dtype)) return 0;
+    return plan_bwd(T, in, out, act_dtype == TERN_BF16).total;
+}
+
+namespace {
+
+// Shared argument checks of the backward entry points.  Sizes of absent parts
+// (want_dx / want_dw false) are not checked.
+int check_bwd(const void *X, const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
+              const float *scale, int64_t T, int64_t in, int64_t out, void *dX, int32_t dx_dtype,
+              float *gq, float *sgrad, void *workspace, size_t workspace_bytes, bool want_dx,
+              bool want_dw, BwdLayout &L) {
+    int rc = validate_shape(T, in, out);
+    if (rc) return rc;
+    if (!act_ok(act_dtype) || (want_dx && dx_dtype != TERN_F32)) return TERN_ERR_DTYPE;
+    const bool bf = act_dtype == TERN_BF16;
+    const size_t es = esize(act_dtype);
+    const size_t xb = want_dw ? (size_t)T * in * es : 0, dyb = (size_t)T * out * es;
+    const size_t pb = (size_t)tern_packed_words(in, out) * 4;
+    const size_t sb = (size_t)out * 4;
+    const size_t dxb = want_dx ? (size_t)T * in * 4 : 0;
+    const size_t gqb = want_dw ? (size_t)in * out * 4 : 0, sgb = want_dw ? (size_t)out * 4 : 0;
+    L = plan_bwd(T, in, out, bf);
+    const size_t wsb = want_dw ? L.total : 0;
+    if ((xb && !X) || (dyb && !dY) || (pb && !tern_packed) || (sb && !scale) || (dxb && !dX) ||
+        (gqb && !gq) || (sgb && !sgrad))
+        return TERN_ERR_NULL;
+    if (wsb && !workspace) return TERN_ERR_WORKSPACE;
+    if (workspace_bytes < wsb) return TERN_ERR_WORKSPACE;
+    if ((xb && !aligned16(X)) || (dyb && !aligned16(dY)) || (sb && !aligned16(scale)) ||
+        (dxb && !aligned16(dX)) || (gqb && !aligned16(gq)) || (sgb && !aligned16(sgrad)) ||
+        (pb && !aligned4(tern_packed)) || (wsb && !aligned16(workspace)))
+        return TERN_ERR_ALIGN;
+    const Buf outs[] = {{dX, dxb}, {gq, gqb}, {sgrad, sgb}, {workspace, wsb}};
+    const Buf ins[] = {{X, xb}, {dY, dyb}, {tern_packed, pb}, {scale, sb}};
+    if (any_alias(outs, 4, ins, 4)) return TERN_ERR_ALIAS;
+    return TERN_OK;
+}
+
+GemmArgs args_for(const GemmPlan &p, const uint32_t *tern_packed, const float *scale, int64_t T,
+                  int64_t in, int64_t out) {
+    GemmArgs a{};
+    a.packed = tern_packed;
+    a.scale = scale;
+    a.M = (int)p.M; a.N = (int)p.N; a.K = (int)p.K;
+    a.tiles_m = (int)p.tiles_m; a.tiles_n = (int)p.tiles_n;
+    a.splits = (int)p.splits; a.kps = (int)p.k_per_split;
+    a.in = (int)in; a.out = (int)out; a.wpr = (int)((out + 15) / 16); a.T = (int)T;
+    return a;
+}
+
+hipError_t enqueue_dx(const void *dY, bool bf, const uint32_t *tern_packed, const float *scale, int64_t T,
+                      int64_t in, int64_t out, void *dX, const BwdLayout &L, hipStream_t st) {
+    const size_t dxb = (size_t)T * in * 4;
+    if (dxb == 0) return hipSuccess;
+    if (out == 0) return launch_zero(dX, dxb, st);  // empty sum
+    GemmArgs a = args_for(L.dx, tern_packed, scale, T, in, out);
+    a.act0 = dY;
+    a.out_ptr = dX;
+    return launch_gemm(L.dx, bf, a, st);
+}
+
+hipError_t enqueue_dw(const void *X, const void *dY, bool bf, const uint32_t *tern_packed, const float *scale,
+                      int64_t T, int64_t in, int64_t out, float *gq, float *sgrad, void *workspace,
+                      const BwdLayout &L, hipStream_t st) {
+    if (T == 0 || in == 0 || out == 0) {
+        // G is an empty sum (T == 0) or empty: gq = 0 and sgrad = 0 where they exist
+        hipError_t e = hipSuccess;
+        if ((size_t)in * out) e = launch_zero(gq, (size_t)in * out * 4, st);
+        if (e == hipSuccess && out) e = launch_zero(sgrad, (size_t)out * 4, st);
+        return e;
+    }
+    float *part = (float *)((char *)workspace + L.part_off);
+    GemmArgs a = args_for(L.dw, tern_packed, scale, T, in, out);
+    a.act0 = X;
+    a.act1 = dY;
+    a.part = part;
+    hipError_t e;
+    if (L.dw.splits > 1) {
+        float *ws = (float *)((char *)workspace + L.ws_off);
+        a.out_ptr = ws;
+        e = launch_gemm(L.dw, bf, a, st);
+        if (e == hipSuccess)
+            e = launch_dw_reduce(ws, (int)L.dw.splits, scale, tern_packed, in, out, gq, part, st);
+    } else {
+        a.out_ptr = gq;
+        e = launch_gemm(L.dw, bf, a, st);
+    }
+    if (e == hipSuccess) e = launch_sgrad_reduce(part, L.part_rows, out, sgrad, st);
+    return e;
+}
+
+}  // namespace
+
+int tern_linear_bwd(const void *X, const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
+                    const float *scale, int64_t T, int64_t in, int64_t out, void *dX, int32_t dx_dtype,
+                    float *gq, float *sgrad, void *workspace, size_t workspace_bytes, void *stream) {
+    BwdLayout L;
+    int rc = check_bwd(X, dY, act_dtype, tern_packed, scale, T, in, out, dX, dx_dtype, gq, sgrad,
+                       workspace, workspace_bytes, true, true, L);
+    if (rc) return rc;
+    const bool bf = act_dtype == TERN_BF16;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = enqueue_dx(dY, bf, tern_packed, scale, T, in, out, dX, L, st);
+    if (e == hipSuccess) e = enqueue_dw(X, dY, bf, tern_packed, scale, T, in, out, gq, sgrad, workspace, L, st);
+    return hip_status(e);
+}
+
+int tern_linear_bwd_dx(const void *dY, int32_t act_dtype, const uint32_t *tern_packed, const float *scale,
+                       int64_t T, int64_t in, int64_t out, void *dX, int32_t dx_dtype, void *stream) {
+    BwdLayout L;
+    int rc = check_bwd(nullptr, dY, act_dtype, tern_packed, scale, T, in, out, dX, dx_dtype, nullptr,
+                       nullptr, nullptr, 0, true, false, L);
+    if (rc) return rc;
+    return hip_status(enqueue_dx(dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, dX, L,
+                                 (hipStream_t)stream));
+}
+
+int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
+                       const float *scale, int64_t T, int64_t in, int64_t out, float *gq, float *sgrad,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    BwdLayout L;
+    int rc = check_bwd(X, dY, act_dtype, tern_packed, scale, T, in, out, nullptr, TERN_F32, gq, sgrad,
+                       workspace, workspace_bytes, false, true, L);
+    if (rc) return rc;
+    return hip_status(enqueue_dw(X, dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, gq, sgrad,
+                                 workspace, L, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// tern_plan.cpp -- HIP-free validation and planning (see tern_plan.h).
+#include "tern_plan.h"
+
+#include "../../include/tern.h"
+
+namespace tern {
+
+namespace {
+
+constexpr int64_t kCUs = 256;  // MI355X compute units; one 256-thread workgroup each
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Relative efficiency of a tile shape once the chip is full: the larger wave
+// tiles reuse each LDS fragment more and hide the operand staging better.
+double tile_eff(int t) { return t == TILE_256 ? 1.0 : t == TILE_128 ? 0.55 : 0.25; }
+
+// Fraction of the chip's workgroup slots a grid keeps busy, counting the idle
+// slots of a partial last wave.
+double fill(int64_t grid) {
+    if (grid <= 0) return 1.0;
+    int64_t waves = cdiv(grid, kCUs);
+    return double(grid) / double(waves * kCUs);
+}
+
+}  // namespace
+
+int validate_shape(int64_t T, int64_t in, int64_t out) {
+    if (T < 0 || in < 0 || out < 0) return TERN_ERR_SHAPE;
+    if (in % 8 != 0 || out % 8 != 0) return TERN_ERR_SHAPE;
+    if (in > kMaxInOut || out > kMaxInOut || T > kMaxT) return TERN_ERR_SHAPE;
+    return TERN_OK;
+}
+
+bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+GemmPlan plan_gemm(int mode, int64_t T, int64_t in, int64_t out, bool bf16) {
+    GemmPlan p;
+    p.mode = mode;
+    if (mode == MODE_FWD) { p.M = out; p.N = T; p.K = in; }
+    else if (mode == MODE_DX) { p.M = in; p.N = T; p.K = out; }
+    else { p.M = in; p.N = out; p.K = T; }
+    const int64_t kstep = k_step(bf16);
+    if (p.M <= 0 || p.N <= 0 || p.K <= 0) { p.grid = 0; return p; }
+
+    double best = -1.0;
+    for (int t = TILE_256; t <= TILE_64; t++) {
+        const int64_t bm = tile_bm(t);
+        const int64_t tm = cdiv(p.M, bm), tn = cdiv(p.N, bm);
+        const int64_t tiles = tm * tn;
+        const int64_t ksteps = cdiv(p.K, kstep);
+        // split K only for the weight gradient, whose K (= tokens) is long and
+        // whose output grid (in x out) can be smaller than the chip
+        int64_t max_s = 1;
+        if (mode == MODE_DW) {
+            max_s = ksteps / 8;  // keep >= 8 K steps per split
+            if (max_s < 1) max_s = 1;
+            if (max_s > 32) max_s = 32;
+        }
+        for (int64_t s = 1; s <= max_s; s *= 2) {
+            const int64_t kps = cdiv(ksteps, s) * kstep;
+            const int64_t real_s = cdiv(p.K, kps);
+            const int64_t grid = tiles * real_s;
+            // useful MFMA rate relative to a full chip of 256x256 tiles
+            double rate = tile_eff(t) * fill(grid) * (grid < kCUs ? 1.0 : 1.0);
+            double flops = 2.0 * double(p.M) * double(p.N) * double(p.K);
+            double t_mma = flops / (rate * 2.3e15);
+            // split-K partials: written once, read once, in fp32
+            double t_ws = real_s > 1 ? 2.0 * double(real_s) * double(p.M * p.N) * 4.0 / 5.0e12 : 0.0;
+            // per-workgroup prologue/epilogue, roughly 2 K steps of work
+            double t_edge = double(cdiv(grid, kCUs)) * 2.0 * 2.0 * bm * bm * kstep / (tile_eff(t) * 9.0e12);
+            double score = 1.0 / (t_mma + t_ws + t_edge);
+            if (score > best) {
+                best = score;
+                p.tile = t;
+                p.tiles_m = tm;
+                p.tiles_n = tn;
+                p.splits = real_s;
+                p.k_per_split = kps;
+                p.grid = grid;
+            }
+        }
+    }
+    return p;
+}
+
+BwdLayout plan_bwd(int64_t T, int64_t in, int64_t out, bool bf16) {
+    BwdLayout L;
+    L.dx = plan_gemm(MODE_DX, T, in, out, bf16);
+    L.dw = plan_gemm(MODE_DW, T, in, out, bf16);
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    if (T > 0 && in > 0 && out > 0) {
+        const int64_t bm = tile_bm(L.dw.tile);
+        L.part_rows = L.dw.splits > 1 ? cdiv(in, kReduceRows) : cdiv(in, bm);
+        L.part_off = 0;
+        L.part_bytes = al(size_t(L.part_rows) * size_t(out) * 4);
+        L.ws_off = L.part_bytes;
+        L.ws_bytes = L.dw.splits > 1 ? al(size_t(L.dw.splits) * size_t(in) * size_t(out) * 4) : 0;
+    }
+    L.total = L.part_bytes + L.ws_bytes;
+    return L;
+}
+
+}  // namespace tern

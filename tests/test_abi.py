@@ -1,0 +1,146 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/tern.h
+declares, and rejects bad arguments before touching the GPU.  No call here
+passes validation, so no kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_linear_tern_amd as tl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tern.h")
+
+OK, NULL, SHAPE, THETA, DTYPE, ALIGN, WORKSPACE, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+F32, BF16 = 0, 1
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tern_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tl.LIB_PATH):
+        from ternary_weight_linear_tern_amd import build
+        build.build()
+    return tl.lib()
+
+
+def P(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) >= 9, names
+    for n in names:
+        assert hasattr(L, n), f"libtern.so does not export {n}"
+        assert n in tl.SIGNATURES, f"binding has no signature for {n}"
+
+
+def test_status_strings(L):
+    for code in range(-8, 1):
+        s = tl.tern_status_str(code)
+        assert s and s != "unknown status"
+    assert tl.tern_status_str(-99) == "unknown status"
+    assert "gfx950" in tl.tern_version()
+
+
+def test_packed_words(L):
+    assert tl.tern_packed_words(0, 0) == 0
+    assert tl.tern_packed_words(3, 16) == 3
+    assert tl.tern_packed_words(3, 17) == 6
+    assert tl.tern_packed_words(2, 20) == 4
+    assert tl.tern_packed_words(-1, 4) == -1
+
+
+def test_materialize_rejects(L):
+    s = P(0)
+    m = L.tern_materialize
+    assert m(P(0x10000), 4, 16, 0, P(0x20000), s) == THETA
+    assert m(P(0x10000), 4, 16, 128, P(0x20000), s) == THETA
+    assert m(P(0x10000), -1, 16, 2, P(0x20000), s) == SHAPE
+    assert m(P(0x10000), 4, (1 << 20) + 8, 2, P(0x20000), s) == SHAPE
+    assert m(None, 4, 16, 2, P(0x20000), s) == NULL
+    assert m(P(0x10000), 4, 16, 2, None, s) == NULL
+    assert m(P(0x10000), 4, 16, 2, P(0x20002), s) == ALIGN
+    # q occupies [0x10000, 0x10040); packed [0x10020, 0x10030) overlaps it
+    assert m(P(0x10000), 4, 16, 2, P(0x10020), s) == ALIAS
+    # nothing to do: valid without touching the device
+    assert m(None, 0, 16, 2, None, s) == OK
+    assert m(None, 4, 0, 2, None, s) == OK
+
+
+def test_fwd_rejects(L):
+    s = P(0)
+    f = L.tern_linear_fwd
+    X, pk, sc, Y = P(0x100000), P(0x200000), P(0x300000), P(0x400000)
+    assert f(X, BF16, pk, sc, 64, 12, 64, Y, F32, s) == SHAPE      # in % 8
+    assert f(X, BF16, pk, sc, 64, 64, 20, Y, F32, s) == SHAPE      # out % 8
+    assert f(X, BF16, pk, sc, -1, 64, 64, Y, F32, s) == SHAPE
+    assert f(X, 7, pk, sc, 64, 64, 64, Y, F32, s) == DTYPE
+    assert f(X, F32, pk, sc, 64, 64, 64, Y, BF16, s) == DTYPE     # bf16 Y needs bf16 X
+    assert f(None, BF16, pk, sc, 64, 64, 64, Y, F32, s) == NULL
+    assert f(X, BF16, None, sc, 64, 64, 64, Y, F32, s) == NULL
+    assert f(X, BF16, pk, None, 64, 64, 64, Y, F32, s) == NULL
+    assert f(X, BF16, pk, sc, 64, 64, 64, None, F32, s) == NULL
+    assert f(P(0x100008), BF16, pk, sc, 64, 64, 64, Y, F32, s) == ALIGN
+    assert f(X, BF16, pk, P(0x300004), 64, 64, 64, Y, F32, s) == ALIGN
+    assert f(X, BF16, P(0x200002), sc, 64, 64, 64, Y, F32, s) == ALIGN
+    # Y [64, 64] fp32 = 16 KiB starting inside X [64, 64] bf16 = 8 KiB
+    assert f(X, BF16, pk, sc, 64, 64, 64, P(0x101000), F32, s) == ALIAS
+    assert f(X, BF16, pk, sc, 64, 64, 64, P(0x300000 - 0x100), F32, s) == ALIAS  # Y runs into scale
+    # empty outputs: valid and nothing is enqueued
+    assert f(None, BF16, pk, sc, 0, 64, 64, None, F32, s) == OK
+    assert f(X, BF16, None, None, 64, 64, 0, None, F32, s) == OK
+
+
+def test_bwd_rejects(L):
+    s = P(0)
+    b = L.tern_linear_bwd
+    X, dY, pk, sc = P(0x1000000), P(0x2000000), P(0x3000000), P(0x4000000)
+    dX, gq, sg = P(0x5000000), P(0x6000000), P(0x7000000)
+    T, n_in, n_out = 4096, 2048, 2048
+    need = tl.tern_linear_bwd_workspace_bytes(T, n_in, n_out, BF16)
+    ws = P(0x10000000)
+    assert b(X, dY, BF16, pk, sc, T, n_in, n_out, dX, BF16, gq, sg, ws, need, s) == DTYPE
+    assert b(X, dY, 3, pk, sc, T, n_in, n_out, dX, F32, gq, sg, ws, need, s) == DTYPE
+    assert b(X, dY, BF16, pk, sc, T, 100, n_out, dX, F32, gq, sg, ws, need, s) == SHAPE
+    assert b(None, dY, BF16, pk, sc, T, n_in, n_out, dX, F32, gq, sg, ws, need, s) == NULL
+    assert b(X, dY, BF16, pk, sc, T, n_in, n_out, dX, F32, None, sg, ws, need, s) == NULL
+    assert b(X, dY, BF16, pk, sc, T, n_in, n_out, dX, F32, gq, None, ws, need, s) == NULL
+    if need:
+        assert b(X, dY, BF16, pk, sc, T, n_in, n_out, dX, F32, gq, sg, None, need, s) == WORKSPACE
+        assert b(X, dY, BF16, pk, sc, T, n_in, n_out, dX, F32, gq, sg, ws, need - 1, s) == WORKSPACE
+    assert b(X, dY, BF16, pk, sc, T, n_in, n_out, P(0x5000004), F32, gq, sg, ws, need, s) == ALIGN
+    # gq [2048, 2048] fp32 = 16 MiB from 0x6000000 covers 0x7000000 (sgrad)
+    assert b(X, dY, BF16, pk, sc, T, n_in, n_out, dX, F32, gq, sg, ws, need, s) == ALIAS
+    # dX writes over dY
+    assert b(X, dY, BF16, pk, sc, T, n_in, n_out, P(0x2000000 + 4096), F32, P(0x20000000), sg, ws, need,
+             s) == ALIAS
+
+
+def test_bwd_parts_reject(L):
+    s = P(0)
+    assert L.tern_linear_bwd_dx(P(0x1000), BF16, P(0x2000), P(0x3000), 8, 8, 8, P(0x4000), BF16, s) == DTYPE
+    assert L.tern_linear_bwd_dx(None, BF16, P(0x2000), P(0x3000), 8, 8, 8, P(0x4000), F32, s) == NULL
+    assert L.tern_linear_bwd_dw(P(0x1000), P(0x2000), BF16, P(0x3000), P(0x4000), 8, 8, 12, P(0x5000),
+                                P(0x6000), P(0x7000), 1 << 20, s) == SHAPE
+
+
+def test_workspace_bytes(L):
+    assert tl.tern_linear_bwd_workspace_bytes(-1, 8, 8, BF16) == 0
+    assert tl.tern_linear_bwd_workspace_bytes(8, 12, 8, BF16) == 0
+    assert tl.tern_linear_bwd_workspace_bytes(8, 8, 8, 9) == 0
+    assert tl.tern_linear_bwd_workspace_bytes(0, 64, 64, BF16) == 0
+    for (T, i, o) in [(64, 64, 64), (2048, 512, 512), (16384, 2048, 2048), (32768, 4096, 16384),
+                      (1000, 200, 72)]:
+        for dt in (F32, BF16):
+            w = tl.tern_linear_bwd_workspace_bytes(T, i, o, dt)
+            # always room for at least one row of sgrad partials, 256-byte granular
+            assert w >= 4 * o and w % 256 == 0, (T, i, o, dt, w)
+            assert tl.tern_linear_bwd_workspace_bytes(T, i, o, dt) == w  # pure function

@@ -1,0 +1,322 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
+
+Gates: packing bit-exact; Y, dX, gq and sgrad within rel-L2 2e-3 for bf16
+activations and 1e-5 for fp32.  Small shapes are compared element by element
+in full; the benchmark workloads at full size are compared on seeded samples
+of token rows (Y, dX) and output columns (gq, sgrad) that the oracle computes
+one by one, in the same launch configuration the benchmark uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import ternary_weight_linear_tern_amd as tl
+from gpu_util import DeviceProjection, log, rel_l2, to_dev, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    tl.lib()  # raises if the HIP library is not built
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.get()
+
+
+def check_full(o, p, res, tag):
+    tol = tol_for(p.act)
+    Y = o.linear_fwd(p.X, p.q, p.theta, p.scale)
+    dX = o.linear_dx(p.dY, p.q, p.theta, p.scale)
+    _, gq, sg = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale)
+    want_pk = o.pack(o.tern(p.q, p.theta))
+    assert np.array_equal(res["packed"], want_pk), f"{tag}: packing differs"
+    errs = dict(Y=rel_l2(res["Y"], Y), dX=rel_l2(res["dX"], dX), gq=rel_l2(res["gq"], gq),
+                sgrad=rel_l2(res["sgrad"], sg))
+    log(f"  {tag}: relL2 {errs}")
+    for k, e in errs.items():
+        assert e <= tol, f"{tag}: {k} relL2 {e:.3e} > {tol:.1e}"
+    return errs
+
+
+# ---------------------------------------------------------------------------
+# materialize: bit-exact packing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("theta", [1, 2, 3, 7, 8, 127])
+def test_materialize_all_int8(o, theta):
+    log(f"materialize all int8 values theta={theta}")
+    q = ((np.arange(256 * 64).reshape(256, 64) % 256) - 128).astype(np.int8)
+    qd = to_dev(q)
+    pk = tl.empty_packed(256, 64)
+    tl.tern_materialize(qd, theta, pk)
+    torch.cuda.synchronize()
+    got = pk.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, o.pack(o.tern(q, theta)))
+
+
+@pytest.mark.parametrize("n_in,n_out", [(1, 8), (3, 24), (37, 40), (5, 72), (64, 1000), (17, 16), (9, 4096)])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_materialize_ragged(o, n_in, n_out, aligned):
+    log(f"materialize ragged in={n_in} out={n_out} aligned={aligned}")
+    q = synth.int8_uniform(synth.stream_seed(5, n_in, n_out, 0), (n_in, n_out), -128, 127)
+    flat = torch.zeros(n_in * n_out + 16, dtype=torch.int8, device="cuda")
+    off = 0 if aligned else 3
+    qd = flat[off:off + n_in * n_out].view(n_in, n_out)
+    qd.copy_(to_dev(q))
+    pk = tl.empty_packed(n_in, n_out)
+    for theta in (2, 5):
+        tl.tern_materialize(qd, theta, pk)
+        torch.cuda.synchronize()
+        assert np.array_equal(pk.cpu().numpy().view(np.uint32), o.pack(o.tern(q, theta)))
+
+
+# ---------------------------------------------------------------------------
+# full element-by-element parity on small and ragged shapes
+# ---------------------------------------------------------------------------
+
+SMALL = [(1, 8, 8), (3, 8, 16), (5, 24, 40), (64, 64, 64), (70, 24, 40), (129, 72, 136),
+         (257, 136, 264), (300, 200, 520), (1000, 64, 1024), (96, 1024, 64), (2, 2048, 16),
+         (517, 512, 264)]
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("T,n_in,n_out", SMALL)
+def test_parity_small(o, T, n_in, n_out, act):
+    log(f"parity small T={T} in={n_in} out={n_out} act={act}")
+    p = synth.make_inputs(T, n_in, n_out, act=act, config_id=200 + T % 97, proj_id=n_in + n_out)
+    d = DeviceProjection(p)
+    d.step()
+    check_full(o, p, d.results(), f"T={T} in={n_in} out={n_out} {act}")
+
+
+@pytest.mark.parametrize("q_law,scale_law,theta", [("skewed", "lognormal", 2), ("uniform", "uniform", 1),
+                                                   ("uniform", "lognormal", 6)])
+def test_parity_laws(o, q_law, scale_law, theta):
+    log(f"parity laws {q_law} {scale_law} theta={theta}")
+    p = synth.make_inputs(384, 320, 192, act="bf16", q_law=q_law, scale_law=scale_law, theta=theta,
+                          config_id=301)
+    d = DeviceProjection(p)
+    d.step()
+    check_full(o, p, d.results(), f"{q_law}/{scale_law}/theta={theta}")
+
+
+def test_parity_tiny_config(o):
+    w = synth.WORKLOADS["tiny"]
+    log("parity tiny workload (fp32)")
+    p = synth.workload_inputs(w, 0)
+    d = DeviceProjection(p)
+    d.step()
+    check_full(o, p, d.results(), "tiny")
+
+
+@pytest.mark.parametrize("proj", range(6))
+def test_parity_rwkv_small_full(o, proj):
+    w = synth.WORKLOADS["rwkv_small"]
+    log(f"parity rwkv_small projection {w.projs[proj]} (full)")
+    p = synth.workload_inputs(w, proj)
+    d = DeviceProjection(p)
+    d.step()
+    check_full(o, p, d.results(), f"rwkv_small/{w.projs[proj][0]}")
+
+
+def test_y_bf16_output(o):
+    log("forward with bf16 Y")
+    p = synth.make_inputs(260, 136, 520, act="bf16", config_id=302)
+    d = DeviceProjection(p, y_bf16=True)
+    d.materialize()
+    d.fwd()
+    torch.cuda.synchronize()
+    Yb = d.Y.float().cpu().numpy()
+    Y = o.linear_fwd(p.X, p.q, p.theta, p.scale)
+    assert rel_l2(Yb, Y) <= 2e-3
+    # the bf16 output is the round-to-nearest-even of the fp32 output
+    Yf = torch.empty((p.X.shape[0], 520), dtype=torch.float32, device="cuda")
+    tl.tern_linear_fwd(d.X, d.packed, d.scale, Yf)
+    torch.cuda.synchronize()
+    assert torch.equal(Yf.to(torch.bfloat16).float().cpu(), torch.from_numpy(Yb))
+
+
+# ---------------------------------------------------------------------------
+# exact-arithmetic regime: every partial sum is an exact fp32 integer multiple
+# of the scale's power of two, so any summation order gives the same bits
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("T,n_in,n_out", [(64, 64, 64), (300, 200, 520), (1000, 256, 264)])
+def test_exact_regime_bitwise(o, T, n_in, n_out, act):
+    log(f"exact regime T={T} in={n_in} out={n_out} {act}")
+    base = synth.make_inputs(T, n_in, n_out, act="f32", config_id=400 + n_in)
+    Xi = synth.int8_uniform(synth.stream_seed(11, T, n_in, 0), (T, n_in), -3, 3).astype(np.float32)
+    dYi = synth.int8_uniform(synth.stream_seed(11, T, n_out, 1), (T, n_out), -3, 3).astype(np.float32)
+    k = synth.int8_uniform(synth.stream_seed(11, n_out, 0, 2), (n_out,), 2, 9).astype(np.float32)
+    scale = (2.0 ** -k).astype(np.float32)
+    if act == "bf16":
+        Xi, dYi = synth.to_bf16_bits(Xi), synth.to_bf16_bits(dYi)
+    p = synth.ProjInputs(Xi, dYi, base.q, scale, 2, act)
+    d = DeviceProjection(p)
+    d.step()
+    r = d.results()
+    Y = o.linear_fwd(p.X, p.q, 2, p.scale)
+    dX = o.linear_dx(p.dY, p.q, 2, p.scale)
+    _, gq, sg = o.linear_wgrad(p.X, p.dY, p.q, 2, p.scale)
+    assert np.array_equal(r["Y"].astype(np.float64), Y)
+    assert np.array_equal(r["dX"].astype(np.float64), dX)
+    assert np.array_equal(r["gq"].astype(np.float64), gq)
+    assert np.array_equal(r["sgrad"].astype(np.float64), sg)
+
+
+# ---------------------------------------------------------------------------
+# the benchmark workloads at full size, sampled
+# ---------------------------------------------------------------------------
+
+def sampled_case(o, wname, proj):
+    w = synth.WORKLOADS[wname]
+    name, n_in, n_out = w.projs[proj]
+    log(f"parity {wname}/{name} T={w.T} in={n_in} out={n_out} (full size, sampled)")
+    p = synth.workload_inputs(w, proj)
+    d = DeviceProjection(p)
+    d.step()
+    torch.cuda.synchronize()
+    rows = np.union1d(synth.sample_indices(synth.stream_seed(77, w.config_id, proj, 0), 40, w.T),
+                      [0, w.T - 1])
+    cols = np.union1d(synth.sample_indices(synth.stream_seed(77, w.config_id, proj, 1), 14, n_out),
+                      [0, n_out - 1])
+    rt = torch.from_numpy(rows).cuda()
+    ct = torch.from_numpy(cols).cuda()
+    Yg = d.Y[rt].cpu().numpy()
+    dXg = d.dX[rt].cpu().numpy()
+    gqg = d.gq[:, ct].cpu().numpy()
+    sgg = d.sgrad[ct].cpu().numpy()
+    pk = d.packed.cpu().numpy().view(np.uint32)
+    assert np.array_equal(pk, o.pack(o.tern(p.q, p.theta))), "packing differs"
+    Y = o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows)
+    dX = o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows)
+    _, gq, sg = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
+    errs = dict(Y=rel_l2(Yg, Y), dX=rel_l2(dXg, dX), gq=rel_l2(gqg, gq), sgrad=rel_l2(sgg, sg))
+    log(f"  relL2 {errs}")
+    tol = tol_for(p.act)
+    for k, e in errs.items():
+        assert e <= tol, f"{wname}/{name}: {k} relL2 {e:.3e} > {tol:.1e}"
+
+
+@pytest.mark.parametrize("proj", range(6))
+def test_parity_mid_sampled(o, proj):
+    sampled_case(o, "mid", proj)
+
+
+@pytest.mark.parametrize("proj", range(6))
+def test_parity_large_sampled(o, proj):
+    sampled_case(o, "large", proj)
+
+
+@pytest.mark.parametrize("proj", [0, 4, 5])
+def test_parity_largest_sampled(o, proj):
+    sampled_case(o, "largest", proj)
+
+
+# ---------------------------------------------------------------------------
+# properties
+# ---------------------------------------------------------------------------
+
+def test_bwd_deterministic_and_split_equal():
+    log("determinism: repeated bwd and bwd_dx + bwd_dw")
+    for (T, n_in, n_out) in [(4096, 512, 2048), (2048, 1024, 1024), (777, 264, 136)]:
+        p = synth.make_inputs(T, n_in, n_out, act="bf16", config_id=500)
+        d = DeviceProjection(p)
+        d.step()
+        r1 = d.results()
+        d.bwd()
+        d.fwd()
+        r2 = d.results()
+        for k in ("Y", "dX", "gq", "sgrad"):
+            assert np.array_equal(r1[k], r2[k]), f"{k} differs between identical calls"
+        dX = torch.empty_like(d.dX)
+        gq = torch.empty_like(d.gq)
+        sg = torch.empty_like(d.sgrad)
+        tl.tern_linear_bwd_dx(d.dY, d.packed, d.scale, dX)
+        tl.tern_linear_bwd_dw(d.X, d.dY, d.packed, d.scale, gq, sg, d.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(dX, d.dX) and torch.equal(gq, d.gq) and torch.equal(sg, d.sgrad)
+
+
+def test_zero_sizes():
+    log("zero sizes")
+    dev = "cuda"
+    # T = 0: G is an empty sum, so gq = 0 and sgrad = 0
+    X = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    dY = torch.empty((0, 32), dtype=torch.bfloat16, device=dev)
+    q = torch.ones((64, 32), dtype=torch.int8, device=dev) * 3
+    sc = torch.ones(32, device=dev)
+    pk = tl.empty_packed(64, 32)
+    tl.tern_materialize(q, 2, pk)
+    Y = torch.empty((0, 32), device=dev)
+    tl.tern_linear_fwd(X, pk, sc, Y)
+    dX = torch.empty((0, 64), device=dev)
+    gq = torch.full((64, 32), 7.0, device=dev)
+    sg = torch.full((32,), 7.0, device=dev)
+    ws = tl.empty_workspace(0, 64, 32, torch.bfloat16)
+    tl.tern_linear_bwd(X, dY, pk, sc, dX, gq, sg, ws)
+    torch.cuda.synchronize()
+    assert torch.all(gq == 0) and torch.all(sg == 0)
+    # in = 0: Y = 0 (empty sum over r), sgrad = 0
+    X = torch.empty((16, 0), dtype=torch.bfloat16, device=dev)
+    dY = torch.randn((16, 32), device=dev).to(torch.bfloat16)
+    pk = tl.empty_packed(0, 32)
+    Y = torch.full((16, 32), 7.0, device=dev)
+    tl.tern_linear_fwd(X, pk, sc, Y)
+    dX = torch.empty((16, 0), device=dev)
+    gq = torch.empty((0, 32), device=dev)
+    sg = torch.full((32,), 7.0, device=dev)
+    tl.tern_linear_bwd(X, dY, pk, sc, dX, gq, sg, tl.empty_workspace(16, 0, 32, torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.all(Y == 0) and torch.all(sg == 0)
+    # out = 0: dX = 0 (empty sum over c)
+    X = torch.randn((16, 24), device=dev).to(torch.bfloat16)
+    dY = torch.empty((16, 0), dtype=torch.bfloat16, device=dev)
+    pk = tl.empty_packed(24, 0)
+    sc0 = torch.empty((0,), device=dev)
+    dX = torch.full((16, 24), 7.0, device=dev)
+    gq = torch.empty((24, 0), device=dev)
+    sg = torch.empty((0,), device=dev)
+    Y = torch.empty((16, 0), device=dev)
+    tl.tern_linear_fwd(X, pk, sc0, Y)
+    tl.tern_linear_bwd(X, dY, pk, sc0, dX, gq, sg, tl.empty_workspace(16, 24, 0, torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.all(dX == 0)
+
+
+def test_outputs_stay_in_bounds():
+    """Guard bytes around every output are untouched (ragged shapes)."""
+    log("canaries around outputs")
+    T, n_in, n_out = 333, 200, 136
+    p = synth.make_inputs(T, n_in, n_out, act="bf16", config_id=600)
+    d = DeviceProjection(p)
+    G = 4096  # guard elements on each side
+
+    def guarded(shape, dtype):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * G,), 1234.5, dtype=dtype, device="cuda")
+        return buf, buf[G:G + n].view(shape)
+
+    bY, Y = guarded((T, n_out), torch.float32)
+    bX, dX = guarded((T, n_in), torch.float32)
+    bq, gq = guarded((n_in, n_out), torch.float32)
+    bs, sg = guarded((n_out,), torch.float32)
+    bp = torch.full((n_in * 9 + 2 * G,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    pk = bp[G:G + n_in * 9].view(n_in, 9)
+    tl.tern_materialize(d.q, 2, pk)
+    tl.tern_linear_fwd(d.X, pk, d.scale, Y)
+    tl.tern_linear_bwd(d.X, d.dY, pk, d.scale, dX, gq, sg, d.ws)
+    torch.cuda.synchronize()
+    for b in (bY, bX, bq, bs):
+        assert torch.all(b[:G] == 1234.5) and torch.all(b[-G:] == 1234.5)
+    assert torch.all(bp[:G] == 0x5A5A5A5A) and torch.all(bp[-G:] == 0x5A5A5A5A)
