@@ -112,8 +112,10 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, i
 }
 
 // ---------------------------------------------------------------------------
-// Operand stagers.  Each fetches one K step of its tile into registers
-// (fetch), then writes it to an LDS buffer as K-contiguous rows (commit).
+// Operand stagers.  Each fetches one K step of its tile into one of two
+// register sets (fetch<S>), then writes it to an LDS buffer as K-contiguous
+// rows, one output chunk at a time (commit<S>(j), j < NOUT), so the writes can
+// be spread between the MFMAs of the step being computed.
 // ---------------------------------------------------------------------------
 
 // Rows of a row-major matrix whose K dimension is contiguous: X or dY as the
@@ -121,10 +123,11 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, i
 template <bool BF, int R>
 struct StageDirect {
     static constexpr int CH = R * 8 / NT;
+    static constexpr int NOUT = CH;
     const char *base;   // row 0 of the tile
     int kbytes;         // bytes of K per row
     uint32_t off[CH];
-    u32x4 v[CH];
+    u32x4 v[2][CH];
 
     __device__ __forceinline__ void init(const void *p, int64_t ld_bytes, int rows_valid, int kb) {
         base = (const char *)p;
@@ -136,19 +139,18 @@ struct StageDirect {
             off[i] = row < rows_valid ? (uint32_t)(row * ld_bytes + ch * 16) : OOB;
         }
     }
+    // kbyte0: byte offset of this K step within a row
+    template <int S>
     __device__ __forceinline__ void fetch(int kbyte0) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + kbyte0);
         const bool kin = kbyte0 + (int)(threadIdx.x & 7) * 16 < kbytes;
 #pragma unroll
-        for (int i = 0; i < CH; i++) v[i] = bload128(rs, kin ? off[i] : OOB);
+        for (int i = 0; i < CH; i++) v[S][i] = bload128(rs, kin ? off[i] : OOB);
     }
-    __device__ __forceinline__ void commit(u32x4 *sm) const {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < CH; i++) {
-            const int cid = tid + NT * i;
-            sm[(cid >> 3) * RC + (cid & 7)] = v[i];
-        }
+    template <int S>
+    __device__ __forceinline__ void commit(int j, u32x4 *sm) const {
+        const int cid = (int)threadIdx.x + NT * j;
+        sm[(cid >> 3) * RC + (cid & 7)] = v[S][j];
     }
 };
 
@@ -162,10 +164,11 @@ struct StageTrans {
     static constexpr int MC = BF ? 8 : 4;      // m columns per unit (16 bytes)
     static constexpr int UNITS = 8 * (R / MC); // BK / KR == 8 for both types
     static constexpr int UPT = UNITS >= NT ? UNITS / NT : 1;
+    static constexpr int NOUT = UPT * MC;      // one LDS chunk per m column
     const char *base;   // element (k = 0, m = tile's m0)
     int64_t ld;         // bytes per token row
     uint32_t coff[UPT]; // byte offset of the unit's 16-byte column chunk, or OOB
-    u32x4 v[UPT][KR];
+    u32x4 v[2][UPT][KR];
 
     __device__ __forceinline__ void init(const void *p, int64_t ld_bytes, int cols_valid) {
         base = (const char *)p;
@@ -179,6 +182,7 @@ struct StageTrans {
         }
     }
     // k0: first token of this step, relative to base; krem: tokens left in range
+    template <int S>
     __device__ __forceinline__ void fetch(int64_t k0, int krem) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ld);
         const int kg = threadIdx.x & 7;
@@ -188,40 +192,32 @@ struct StageTrans {
             for (int j = 0; j < KR; j++) {
                 const int kr = kg * KR + j;
                 const uint32_t o = (kr < krem && coff[i] != OOB) ? (uint32_t)(kr * ld) + coff[i] : OOB;
-                v[i][j] = bload128(rs, o);
+                v[S][i][j] = bload128(rs, o);
             }
         }
     }
-    __device__ __forceinline__ void commit(u32x4 *sm) const {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < UPT; i++) {
-            const int u = tid + NT * i;
-            if (u >= UNITS) continue;
-            const int kg = u & 7, mg = u >> 3;
-            if constexpr (BF) {
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                    u32x4 o;
-                    o.x = __builtin_amdgcn_perm(v[i][1][e >> 1], v[i][0][e >> 1], sel);
-                    o.y = __builtin_amdgcn_perm(v[i][3][e >> 1], v[i][2][e >> 1], sel);
-                    o.z = __builtin_amdgcn_perm(v[i][5][e >> 1], v[i][4][e >> 1], sel);
-                    o.w = __builtin_amdgcn_perm(v[i][7][e >> 1], v[i][6][e >> 1], sel);
-                    sm[(mg * 8 + e) * RC + kg] = o;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    u32x4 o;
-                    o.x = v[i][0][e];
-                    o.y = v[i][1][e];
-                    o.z = v[i][2][e];
-                    o.w = v[i][3][e];
-                    sm[(mg * 4 + e) * RC + kg] = o;
-                }
-            }
+    template <int S>
+    __device__ __forceinline__ void commit(int jo, u32x4 *sm) const {
+        const int i = jo / MC, e = jo % MC;
+        const int u = (int)threadIdx.x + NT * i;
+        if constexpr (UNITS < NT) {
+            if (u >= UNITS) return;
         }
+        const int kg = u & 7, mg = u >> 3;
+        u32x4 o;
+        if constexpr (BF) {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            o.x = __builtin_amdgcn_perm(v[S][i][1][e >> 1], v[S][i][0][e >> 1], sel);
+            o.y = __builtin_amdgcn_perm(v[S][i][3][e >> 1], v[S][i][2][e >> 1], sel);
+            o.z = __builtin_amdgcn_perm(v[S][i][5][e >> 1], v[S][i][4][e >> 1], sel);
+            o.w = __builtin_amdgcn_perm(v[S][i][7][e >> 1], v[S][i][6][e >> 1], sel);
+        } else {
+            o.x = v[S][i][0][e];
+            o.y = v[S][i][1][e];
+            o.z = v[S][i][2][e];
+            o.w = v[S][i][3][e];
+        }
+        sm[(mg * MC + e) * RC + kg] = o;
     }
 };
 
@@ -233,10 +229,11 @@ struct StageTernT {
     static constexpr int KR = BF ? 8 : 4;
     static constexpr int UNITS = 8 * (R / 8);
     static constexpr int UPT = UNITS >= NT ? UNITS / NT : 1;
+    static constexpr int NOUT = UPT * 8;       // one LDS chunk per column of the half word
     const char *base;   // word (r = 0, c = tile's m0)
     int64_t ldw;        // bytes per packed row
     uint32_t coff[UPT];
-    uint32_t w[UPT][KR];
+    uint32_t w[2][UPT][KR];
 
     __device__ __forceinline__ void init(const uint32_t *p, int64_t wpr, int words_valid) {
         base = (const char *)p;
@@ -249,6 +246,7 @@ struct StageTernT {
             coff[i] = (act && (cg >> 1) < words_valid) ? (uint32_t)((cg >> 1) * 4) : OOB;
         }
     }
+    template <int S>
     __device__ __forceinline__ void fetch(int64_t k0, int krem) {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ldw);
         const int kg = threadIdx.x & 7;
@@ -258,45 +256,40 @@ struct StageTernT {
             for (int j = 0; j < KR; j++) {
                 const int kr = kg * KR + j;
                 const uint32_t o = (kr < krem && coff[i] != OOB) ? (uint32_t)(kr * ldw) + coff[i] : OOB;
-                w[i][j] = bload32(rs, o);
+                w[S][i][j] = bload32(rs, o);
             }
         }
     }
-    __device__ __forceinline__ void commit(u32x4 *sm) const {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < UPT; i++) {
-            const int u = tid + NT * i;
-            if (u >= UNITS) continue;
-            const int kg = u & 7, cg = u >> 3, half = cg & 1;
-            if constexpr (BF) {
-                // y[d]: this half word of rows 2d (low 16 bits) and 2d + 1 (high)
-                const uint32_t hsel = half ? 0x07060302u : 0x05040100u;
-                uint32_t y[4];
-#pragma unroll
-                for (int d = 0; d < 4; d++) y[d] = __builtin_amdgcn_perm(w[i][2 * d + 1], w[i][2 * d], hsel);
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    u32x4 o;
-                    o.x = tern_pair_bf16((y[0] >> (2 * e)) & 0x00030003u);
-                    o.y = tern_pair_bf16((y[1] >> (2 * e)) & 0x00030003u);
-                    o.z = tern_pair_bf16((y[2] >> (2 * e)) & 0x00030003u);
-                    o.w = tern_pair_bf16((y[3] >> (2 * e)) & 0x00030003u);
-                    sm[(cg * 8 + e) * RC + kg] = o;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const int sh = 2 * (8 * half + e);
-                    f32x4 o;
-                    o.x = code_to_f32((w[i][0] >> sh) & 3u);
-                    o.y = code_to_f32((w[i][1] >> sh) & 3u);
-                    o.z = code_to_f32((w[i][2] >> sh) & 3u);
-                    o.w = code_to_f32((w[i][3] >> sh) & 3u);
-                    sm[(cg * 8 + e) * RC + kg] = __builtin_bit_cast(u32x4, o);
-                }
-            }
+    template <int S>
+    __device__ __forceinline__ void commit(int jo, u32x4 *sm) const {
+        const int i = jo / 8, e = jo % 8;
+        const int u = (int)threadIdx.x + NT * i;
+        if constexpr (UNITS < NT) {
+            if (u >= UNITS) return;
         }
+        const int kg = u & 7, cg = u >> 3, half = cg & 1;
+        u32x4 o;
+        if constexpr (BF) {
+            // y_d: this half word of rows 2d (low 16 bits) and 2d + 1 (high)
+            const uint32_t hsel = half ? 0x07060302u : 0x05040100u;
+            const uint32_t y0 = __builtin_amdgcn_perm(w[S][i][1], w[S][i][0], hsel);
+            const uint32_t y1 = __builtin_amdgcn_perm(w[S][i][3], w[S][i][2], hsel);
+            const uint32_t y2 = __builtin_amdgcn_perm(w[S][i][5], w[S][i][4], hsel);
+            const uint32_t y3 = __builtin_amdgcn_perm(w[S][i][7], w[S][i][6], hsel);
+            o.x = tern_pair_bf16((y0 >> (2 * e)) & 0x00030003u);
+            o.y = tern_pair_bf16((y1 >> (2 * e)) & 0x00030003u);
+            o.z = tern_pair_bf16((y2 >> (2 * e)) & 0x00030003u);
+            o.w = tern_pair_bf16((y3 >> (2 * e)) & 0x00030003u);
+        } else {
+            const int sh = 2 * (8 * half + e);
+            f32x4 f;
+            f.x = code_to_f32((w[S][i][0] >> sh) & 3u);
+            f.y = code_to_f32((w[S][i][1] >> sh) & 3u);
+            f.z = code_to_f32((w[S][i][2] >> sh) & 3u);
+            f.w = code_to_f32((w[S][i][3] >> sh) & 3u);
+            o = __builtin_bit_cast(u32x4, f);
+        }
+        sm[(cg * 8 + e) * RC + kg] = o;
     }
 };
 
@@ -309,13 +302,15 @@ struct StageTernS {
     static constexpr int WPK = BF ? 4 : 2;   // packed words per row per K step
     static constexpr int UNITS = R * WPK;
     static constexpr int UPT = UNITS >= NT ? UNITS / NT : 1;
+    static constexpr int CPU_ = BF ? 2 : 4;  // LDS chunks per unit
+    static constexpr int NOUT = UPT * CPU_;
     const char *base;   // word (r = tile's m0, c = 0)
     const float *scale;
     int64_t wpr;
     int out;
     uint32_t roff[UPT];
-    uint32_t w[UPT];
-    f32x4 s[4];
+    uint32_t w[2][UPT];
+    f32x4 s[2][4];
 
     __device__ __forceinline__ void init(const uint32_t *p, int64_t wpr_, int rows_valid,
                                          const float *sc, int out_) {
@@ -332,119 +327,105 @@ struct StageTernS {
         }
     }
     // k0: first output column of this K step (multiple of 16)
+    template <int S>
     __device__ __forceinline__ void fetch(int k0) {
         const int wq = threadIdx.x % WPK;
         const int wcol = (k0 >> 4) + wq;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)(k0 >> 4) * 4);
         const bool win = wcol < wpr;
 #pragma unroll
-        for (int i = 0; i < UPT; i++) w[i] = bload32(rs, (win && roff[i] != OOB) ? roff[i] + wq * 4 : OOB);
+        for (int i = 0; i < UPT; i++) w[S][i] = bload32(rs, (win && roff[i] != OOB) ? roff[i] + wq * 4 : OOB);
         const int c0 = k0 + 16 * wq;
         const __amdgpu_buffer_rsrc_t rsc = make_rsrc(scale + c0);
 #pragma unroll
         for (int q = 0; q < 4; q++)
-            s[q] = __builtin_bit_cast(f32x4, bload128(rsc, (c0 + 4 * q < out) ? (uint32_t)(16 * q) : OOB));
+            s[S][q] = __builtin_bit_cast(f32x4, bload128(rsc, (c0 + 4 * q < out) ? (uint32_t)(16 * q) : OOB));
     }
-    __device__ __forceinline__ void commit(u32x4 *sm) const {
-        const int tid = threadIdx.x;
-        const int wq = tid % WPK;
+    template <int S>
+    __device__ __forceinline__ void commit(int jo, u32x4 *sm) const {
+        const int i = jo / CPU_, c = jo % CPU_;
+        const int u = (int)threadIdx.x + NT * i;
+        if constexpr (UNITS < NT) {
+            if (u >= UNITS) return;
+        }
+        const int wq = (int)threadIdx.x % WPK, row = u / WPK;
+        u32x4 o;
         if constexpr (BF) {
-            uint32_t s2[8];
+            // two pairs of bf16 scales per f32x4 of scales
+            uint32_t s2[4];
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                f32x2 a = {s[q].x, s[q].y}, b = {s[q].z, s[q].w};
+            for (int q = 0; q < 2; q++) {
+                const f32x4 sq = s[S][2 * c + q];
+                f32x2 a = {sq.x, sq.y}, b = {sq.z, sq.w};
                 s2[2 * q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
                 s2[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2));
             }
-#pragma unroll
-            for (int i = 0; i < UPT; i++) {
-                const int u = tid + NT * i;
-                if (u >= UNITS) continue;
-                const int row = u / WPK;
-                u32x4 o0, o1;
-                o0.x = scaled_pair_bf16(w[i], 0, s2[0]);
-                o0.y = scaled_pair_bf16(w[i], 4, s2[1]);
-                o0.z = scaled_pair_bf16(w[i], 8, s2[2]);
-                o0.w = scaled_pair_bf16(w[i], 12, s2[3]);
-                o1.x = scaled_pair_bf16(w[i], 16, s2[4]);
-                o1.y = scaled_pair_bf16(w[i], 20, s2[5]);
-                o1.z = scaled_pair_bf16(w[i], 24, s2[6]);
-                o1.w = scaled_pair_bf16(w[i], 28, s2[7]);
-                sm[row * RC + 2 * wq] = o0;
-                sm[row * RC + 2 * wq + 1] = o1;
-            }
+            o.x = scaled_pair_bf16(w[S][i], 16 * c + 0, s2[0]);
+            o.y = scaled_pair_bf16(w[S][i], 16 * c + 4, s2[1]);
+            o.z = scaled_pair_bf16(w[S][i], 16 * c + 8, s2[2]);
+            o.w = scaled_pair_bf16(w[S][i], 16 * c + 12, s2[3]);
+            sm[row * RC + 2 * wq + c] = o;
         } else {
-#pragma unroll
-            for (int i = 0; i < UPT; i++) {
-                const int u = tid + NT * i;
-                if (u >= UNITS) continue;
-                const int row = u / WPK;
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    f32x4 o;
-                    o.x = code_to_f32((w[i] >> (8 * q)) & 3u) * s[q].x;
-                    o.y = code_to_f32((w[i] >> (8 * q + 2)) & 3u) * s[q].y;
-                    o.z = code_to_f32((w[i] >> (8 * q + 4)) & 3u) * s[q].z;
-                    o.w = code_to_f32((w[i] >> (8 * q + 6)) & 3u) * s[q].w;
-                    sm[row * RC + 4 * wq + q] = __builtin_bit_cast(u32x4, o);
-                }
-            }
+            const f32x4 sq = s[S][c];
+            f32x4 f;
+            f.x = code_to_f32((w[S][i] >> (8 * c)) & 3u) * sq.x;
+            f.y = code_to_f32((w[S][i] >> (8 * c + 2)) & 3u) * sq.y;
+            f.z = code_to_f32((w[S][i] >> (8 * c + 4)) & 3u) * sq.z;
+            f.w = code_to_f32((w[S][i] >> (8 * c + 6)) & 3u) * sq.w;
+            sm[row * RC + 4 * wq + c] = __builtin_bit_cast(u32x4, f);
         }
     }
 };
 
 // ---------------------------------------------------------------------------
-// MFMA over one staged K step.  Fragment layout of the 32x32 MFMAs: lane l
-// supplies row (l % 32) of A and column (l % 32) of B; bf16 lanes hold 8
-// consecutive K, lanes 0-31 the first 8 and lanes 32-63 the next 8.  For fp32
-// (K = 2 per instruction) lane half h of step j carries K index 16 h + j, the
-// same for both operands, so each lane reads 4 steps with one 16-byte load.
+// MFMA over one quarter of a staged K step (K = 16 bf16 or 8 fp32).  Fragment
+// layout of the 32x32 MFMAs: lane l supplies row (l % 32) of A and column
+// (l % 32) of B; bf16 lanes hold 8 consecutive K, lanes 0-31 the first 8 and
+// lanes 32-63 the next 8.  For fp32 (K = 2 per instruction) lane half h of
+// instruction j carries K index 16 h + j, the same for both operands, so a lane
+// reads 4 instructions' operands with one 16-byte load.
 // ---------------------------------------------------------------------------
 template <bool BF, int BM>
-__device__ __forceinline__ void mma_step(const u32x4 *smA, const u32x4 *smB,
-                                         f32x16 (&acc)[Geo<BM>::FM][Geo<BM>::FN],
-                                         int arow, int brow, int h) {
+__device__ __forceinline__ void mma_quarter(const u32x4 *sm, f32x16 (&acc)[Geo<BM>::FM][Geo<BM>::FN],
+                                            int arow, int brow, int h, int kk) {
     using G = Geo<BM>;
+    const int ch = BF ? 2 * kk + h : 4 * h + kk;
+    u32x4 a[G::FM], b[G::FN];
+#pragma unroll
+    for (int fm = 0; fm < G::FM; fm++) a[fm] = sm[(arow + fm * 32) * RC + ch];
+#pragma unroll
+    for (int fn = 0; fn < G::FN; fn++) b[fn] = sm[(brow + fn * 32) * RC + ch];
     if constexpr (BF) {
 #pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
-            u32x4 a[G::FM], b[G::FN];
+        for (int fm = 0; fm < G::FM; fm++)
 #pragma unroll
-            for (int fm = 0; fm < G::FM; fm++) a[fm] = smA[(arow + fm * 32) * RC + 2 * kk + h];
+            for (int fn = 0; fn < G::FN; fn++)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, a[fm]), __builtin_bit_cast(bf16x8, b[fn]), acc[fm][fn], 0, 0, 0);
+    } else {
 #pragma unroll
-            for (int fn = 0; fn < G::FN; fn++) b[fn] = smB[(brow + fn * 32) * RC + 2 * kk + h];
+        for (int e = 0; e < 4; e++)
 #pragma unroll
             for (int fm = 0; fm < G::FM; fm++)
 #pragma unroll
                 for (int fn = 0; fn < G::FN; fn++)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, a[fm]), __builtin_bit_cast(bf16x8, b[fn]),
-                        acc[fm][fn], 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            f32x4 a[G::FM], b[G::FN];
-#pragma unroll
-            for (int fm = 0; fm < G::FM; fm++)
-                a[fm] = __builtin_bit_cast(f32x4, smA[(arow + fm * 32) * RC + 4 * h + q]);
-#pragma unroll
-            for (int fn = 0; fn < G::FN; fn++)
-                b[fn] = __builtin_bit_cast(f32x4, smB[(brow + fn * 32) * RC + 4 * h + q]);
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-#pragma unroll
-                for (int fm = 0; fm < G::FM; fm++)
-#pragma unroll
-                    for (int fn = 0; fn < G::FN; fn++)
-                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm][e], b[fn][e],
-                                                                           acc[fm][fn], 0, 0, 0);
-        }
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        __builtin_bit_cast(f32x4, a[fm])[e], __builtin_bit_cast(f32x4, b[fn])[e], acc[fm][fn],
+                        0, 0, 0);
     }
 }
 
 // ---------------------------------------------------------------------------
 // The GEMM kernel: MODE_FWD, MODE_DX or MODE_DW (see tern_plan.h for M, N, K).
+//
+// Main loop (two LDS buffers, two register sets), iteration it:
+//   issue the global loads of K step it + 2 into register set it % 2;
+//   for each K quarter: MFMAs on LDS buffer it % 2, interleaved with the
+//   decode and LDS writes of K step it + 1 (register set (it + 1) % 2) into
+//   LDS buffer (it + 1) % 2;
+//   barrier.
+// Steps at or past the end load nothing (out-of-range offsets read zero) and
+// their LDS buffer is never read, so the loop body has no branches.
 // ---------------------------------------------------------------------------
 template <bool BF, int MODE, int BM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -465,7 +446,6 @@ void gemm_kernel(GemmArgs g) {
     const int64_t kend = min((int64_t)g.K, kbeg + g.kps);
     const int nk = (int)((kend - kbeg + BK - 1) / BK);
 
-    // A side (rows m) and B side (rows n) stagers for this mode
     using SA = typename std::conditional<
         MODE == MODE_FWD, StageTernT<BF, BM>,
         typename std::conditional<MODE == MODE_DX, StageTernS<BF, BM>, StageTrans<BF, BM>>::type>::type;
@@ -485,24 +465,34 @@ void gemm_kernel(GemmArgs g) {
         sa.init((const char *)g.act0 + kbeg * g.in * ES + (int64_t)m0 * ES, (int64_t)g.in * ES, mvalid);
         sb.init((const char *)g.act1 + kbeg * g.out * ES + (int64_t)n0 * ES, (int64_t)g.out * ES, nvalid);
     }
+    const int64_t klen = kend - kbeg;
 
-    auto fetch = [&](int it) {
+    auto fetch = [&](auto set_c, int it) {
+        constexpr int S = decltype(set_c)::value;
         const int64_t k0 = (int64_t)it * BK;  // relative to kbeg
-        const int krem = (int)min<int64_t>(BK, kend - kbeg - k0);
+        const int krem = (int)max<int64_t>(-1, min<int64_t>(BK, klen - k0));
         if constexpr (MODE == MODE_FWD) {
-            sa.fetch(k0, krem);
-            sb.fetch((int)(k0 * ES));
+            sa.template fetch<S>(k0, krem);
+            sb.template fetch<S>((int)(k0 * ES));
         } else if constexpr (MODE == MODE_DX) {
-            sa.fetch((int)k0);
-            sb.fetch((int)(k0 * ES));
+            sa.template fetch<S>((int)k0);
+            sb.template fetch<S>((int)(k0 * ES));
         } else {
-            sa.fetch(k0, krem);
-            sb.fetch(k0, krem);
+            sa.template fetch<S>(k0, krem);
+            sb.template fetch<S>(k0, krem);
         }
     };
-    auto commit = [&](int buf) {
-        sa.commit(smem + buf * G::ROWS * RC);
-        sb.commit(smem + (buf * G::ROWS + BM) * RC);
+    // commit the outputs of quarter p (of 4) of register set S into LDS buffer `buf`
+    auto commit_part = [&](auto set_c, int buf, int p) {
+        constexpr int S = decltype(set_c)::value;
+        u32x4 *smA = smem + buf * G::ROWS * RC;
+        u32x4 *smB = smem + (buf * G::ROWS + BM) * RC;
+#pragma unroll
+        for (int j = 0; j < SA::NOUT; j++)
+            if (j % 4 == p) sa.template commit<S>(j, smA);
+#pragma unroll
+        for (int j = 0; j < SB::NOUT; j++)
+            if (j % 4 == p) sb.template commit<S>(j, smB);
     };
 
     f32x16 acc[G::FM][G::FN];
@@ -513,18 +503,55 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int i = 0; i < 16; i++) acc[fm][fn][i] = 0.0f;
 
-    fetch(0);
-    commit(0);
-    __syncthreads();
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     const int arow = wm * G::TM + l32, brow = BM + wn * G::TN + l32;
-    for (int it = 0; it < nk; it++) {
-        const int cur = it & 1;
-        const bool more = it + 1 < nk;
-        if (more) fetch(it + 1);
-        const u32x4 *sm = smem + cur * G::ROWS * RC;
-        mma_step<BF, BM>(sm, sm, acc, arow, brow, h);
-        if (more) commit(cur ^ 1);
+
+    if constexpr (MODE != MODE_DW) {
+        // two register sets: loads run two K steps ahead of the MFMAs
+        fetch(I0{}, 0);
+        fetch(I1{}, 1);
+#pragma unroll
+        for (int p = 0; p < 4; p++) commit_part(I0{}, 0, p);
         __syncthreads();
+
+        // one pipelined K step: compute on LDS buffer CUR, stage register set
+        // 1 - CUR (step it + 1) into the other buffer, refill register set CUR
+        // with step it + 2
+        auto body = [&](auto cur_c, int it) {
+            constexpr int CUR = decltype(cur_c)::value;
+            fetch(std::integral_constant<int, CUR>{}, it + 2);
+            const u32x4 *sm = smem + CUR * G::ROWS * RC;
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++) {
+                mma_quarter<BF, BM>(sm, acc, arow, brow, h, kk);
+                commit_part(std::integral_constant<int, 1 - CUR>{}, 1 - CUR, kk);
+            }
+            __syncthreads();
+        };
+        // pairs of steps keep the register sets static; an odd count runs one
+        // extra step on an all-zero buffer, which adds nothing
+        for (int it = 0; it < nk; it += 2) {
+            body(I0{}, it);
+            body(I1{}, it + 1);
+        }
+    } else {
+        // dW: both operands are transposed while staging, which needs twice
+        // the registers per step; one register set, one step ahead
+        fetch(I0{}, 0);
+#pragma unroll
+        for (int p = 0; p < 4; p++) commit_part(I0{}, 0, p);
+        __syncthreads();
+        for (int it = 0; it < nk; it++) {
+            const int cur = it & 1;
+            fetch(I0{}, it + 1);
+            const u32x4 *sm = smem + cur * G::ROWS * RC;
+#pragma unroll
+            for (int kk = 0; kk < 4; kk++) mma_quarter<BF, BM>(sm, acc, arow, brow, h, kk);
+#pragma unroll
+            for (int p = 0; p < 4; p++) commit_part(I0{}, cur ^ 1, p);
+            __syncthreads();
+        }
     }
 
     // ---- epilogues.  acc[fm][fn][i] is C[m][n] with
@@ -621,6 +648,427 @@ void gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// Pipelined bf16 GEMM for 256 x 256 tiles (the large-problem path).
+//
+// Per workgroup: a persistent loop over output tiles (and K splits).  Per K
+// step of 64:
+//   * activation tiles (X or dY) go from HBM straight into LDS with
+//     buffer_load ... lds (no registers, no VALU); their rows are stored
+//     unpadded with the 16-byte chunk index XOR-swizzled by the row, so the
+//     MFMA fragment reads are conflict-free;
+//   * the ternary operand (forward, dX) is read as packed words into one of two
+//     register sets two steps ahead, decoded with VALU and written to LDS in
+//     four parts spread over the MFMAs of the current step;
+//   * dW reads both operands token-major (their natural layout) and builds the
+//     MFMA fragments with ds_read_b64_tr_b16 transposing reads;
+//   * fragments of K quarter q + 1 are read while the MFMAs of quarter q run;
+//   * one barrier per step; two LDS stages (separate __shared__ arrays).
+// A tile's epilogue stores overlap the next tile's first loads.
+// ---------------------------------------------------------------------------
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int P_BM = 256;                 // tile rows (m) and columns (n)
+constexpr int P_ROWB_A = 144;             // padded LDS row (bytes) of a decoded operand tile
+constexpr int P_A_BYTES = P_BM * P_ROWB_A;        // 36864
+constexpr int P_B_BYTES = P_BM * 128;             // 32768, swizzled 128-byte rows
+constexpr int P_T_BYTES = 64 * 512;               // 32768, [64 k][256] swizzled 512-byte rows
+
+// The two LDS stages.  Forward / dX: decoded operand (A) + activation (B);
+// dW: two token-major activation tiles.  Separate objects per stage let the
+// compiler keep reads of one stage independent of DMA into the other.
+__shared__ __attribute__((aligned(16))) char p_lds0[P_A_BYTES + P_B_BYTES];
+__shared__ __attribute__((aligned(16))) char p_lds1[P_A_BYTES + P_B_BYTES];
+
+template <int S>
+__device__ __forceinline__ char *p_stage() {
+    if constexpr (S == 0) return p_lds0;
+    else return p_lds1;
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void *lds_wave_base, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vm0() {
+    // vmcnt(0), leave expcnt and lgkmcnt at their maxima
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Persistent tile walk: WG b, round j -> logical item; consecutive logical
+// items go to one XCD and are grouped 8 tiles along M.
+__device__ __forceinline__ bool p_item(int j, int total, int tiles_m, int tiles_n, int &tm, int &tn,
+                                       int &sp) {
+    const int G = gridDim.x, b = blockIdx.x;
+    const int L = (G & 7) == 0 ? j * G + (b & 7) * (G >> 3) + (b >> 3) : j * G + b;
+    if (L >= total) return false;
+    const int tiles = tiles_m * tiles_n;
+    sp = L / tiles;
+    const int t = L - sp * tiles;
+    constexpr int GM = 8;
+    const int group = t / (GM * tiles_n);
+    const int first = group * GM;
+    const int gs = min(tiles_m - first, GM);
+    const int within = t - group * GM * tiles_n;
+    tm = first + within % gs;
+    tn = within / gs;
+    return true;
+}
+
+// DMA of one K step of an activation tile whose K is contiguous (forward B = X,
+// dX B = dY): 256 rows x 128 bytes.  Wave w, instruction i writes LDS rows
+// (8w + i) * 8 .. + 7; lane l fills physical chunk l % 8 of row (l / 8) with the
+// logical chunk (l % 8) ^ (row % 8).
+struct DmaRows {
+    uint32_t off[8];  // per instruction: byte offset of the lane's chunk, or OOB
+    __device__ __forceinline__ void init(int64_t ld_bytes, int rows_valid) {
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int row = (8 * w + i) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ (row & 7);
+            off[i] = row < rows_valid ? (uint32_t)(row * ld_bytes + c * 16) : OOB;
+        }
+    }
+    // base: row 0 of the tile, at this step's K offset; kbytes_left: valid
+    // bytes of K from there (>= 128 except on the last step)
+    __device__ __forceinline__ void issue(const char *base, int kbytes_left, char *lds_region) const {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        if (kbytes_left >= 128) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) dma16(rs, lds_region + (8 * w + i) * 1024, off[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int row = (8 * w + i) * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ (row & 7);
+                dma16(rs, lds_region + (8 * w + i) * 1024, c * 16 < kbytes_left ? off[i] : OOB);
+            }
+        }
+    }
+};
+
+// DMA of one K step of a token-major activation tile for dW: 64 token rows x
+// 256 features (512 bytes).  Wave w, instruction i writes rows 2 (8w + i) and
+// 2 (8w + i) + 1; lane l fills physical chunk l % 32 of row (l / 32) with the
+// logical chunk (l % 32) ^ (2 (row % 4)).
+struct DmaTok {
+    uint32_t off[8];
+    __device__ __forceinline__ void init(int64_t ld_bytes, int cols_valid) {
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int row = 2 * (8 * w + i) + (lane >> 5);
+            const int c = (lane & 31) ^ (2 * (row & 3));
+            off[i] = c * 8 < cols_valid ? (uint32_t)(row * ld_bytes + c * 16) : OOB;
+        }
+    }
+    // base: token row 0 of this step; rows_left: tokens in range from there
+    __device__ __forceinline__ void issue(const char *base, int rows_left, char *lds_region) const {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        if (rows_left >= 64) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) dma16(rs, lds_region + (8 * w + i) * 1024, off[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int row = 2 * (8 * w + i) + (lane >> 5);
+                dma16(rs, lds_region + (8 * w + i) * 1024, row < rows_left ? off[i] : OOB);
+            }
+        }
+    }
+};
+
+// Fragment reads of one K quarter (16 of the step's 64) into slot registers.
+// K-contiguous tiles: A rows padded (144 B), B rows swizzled (128 B).
+__device__ __forceinline__ void p_read_kc(const char *st, u32x4 (&a)[4], u32x4 (&b)[4], int arow, int brow,
+                                          int h, int kk) {
+    const int c = 2 * kk + h;
+#pragma unroll
+    for (int f = 0; f < 4; f++) a[f] = *(const u32x4 *)(st + (arow + 32 * f) * P_ROWB_A + c * 16);
+    const int pc = c ^ (brow & 7);
+#pragma unroll
+    for (int f = 0; f < 4; f++) b[f] = *(const u32x4 *)(st + P_A_BYTES + (brow + 32 * f) * 128 + pc * 16);
+}
+
+// Token-major tiles (dW): two transposing reads per fragment.  In a group of
+// 16 lanes, lane s = 4e + q reads 8 bytes at token row k0 + e, feature
+// col0 + 4q; output lane i then holds features col0 + i at tokens k0 .. k0 + 3.
+__device__ __forceinline__ u32x4 p_frag_tr(const char *tile, int krow0, int col) {
+    // krow0: this lane's token row for read 0 (multiple of 4 plus e); col: its
+    // 4-feature column start
+    u32x4 r;
+#pragma unroll
+    for (int rd = 0; rd < 2; rd++) {
+        const int k = krow0 + 4 * rd;
+        const int chunk = (col >> 3) ^ (2 * (k & 3));
+        const char *p = tile + k * 512 + chunk * 16 + (col & 7) * 2;
+        v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16 *)p);
+        const u32x2 u = __builtin_bit_cast(u32x2, v);
+        if (rd == 0) { r.x = u.x; r.y = u.y; } else { r.z = u.x; r.w = u.y; }
+    }
+    return r;
+}
+
+__device__ __forceinline__ void p_read_tok(const char *st, u32x4 (&a)[4], u32x4 (&b)[4], int wm, int wn,
+                                           int lane, int kk) {
+    const int g = (lane & 63) >> 4, s = lane & 15, e = s >> 2, q = s & 3;
+    const int krow0 = 16 * kk + 8 * (g >> 1) + e;
+    const int cofs = 16 * (g & 1) + 4 * q;
+#pragma unroll
+    for (int f = 0; f < 4; f++) a[f] = p_frag_tr(st, krow0, wm * 128 + 32 * f + cofs);
+#pragma unroll
+    for (int f = 0; f < 4; f++) b[f] = p_frag_tr(st + P_T_BYTES, krow0, wn * 128 + 32 * f + cofs);
+}
+
+__device__ __forceinline__ void p_mma(f32x16 (&acc)[4][4], const u32x4 (&a)[4], const u32x4 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_pipe_kernel(GemmArgs g) {
+    using G = Geo<256>;
+    constexpr int BK = 64, ES = 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int arow = wm * 128 + l32, brow = wn * 128 + l32;
+    const int total = g.tiles_m * g.tiles_n * g.splits;
+
+    using SA = typename std::conditional<MODE == MODE_FWD, StageTernT<true, 256>, StageTernS<true, 256>>::type;
+    SA sa;             // forward / dX ternary operand (registers)
+    DmaRows db;        // forward / dX activation operand
+    DmaTok dta, dtb;   // dW operands
+
+    // per-tile geometry, set by begin_tile
+    int tm = 0, tn = 0, sp = 0, m0 = 0, n0 = 0, nk = 0;
+    int64_t kbeg = 0, klen = 0;
+    const char *act_a = nullptr, *act_b = nullptr;
+
+    auto begin_tile = [&](int j) -> bool {
+        if (!p_item(j, total, g.tiles_m, g.tiles_n, tm, tn, sp)) return false;
+        m0 = tm * 256;
+        n0 = tn * 256;
+        kbeg = (int64_t)sp * g.kps;
+        const int64_t kend = min((int64_t)g.K, kbeg + g.kps);
+        klen = kend - kbeg;
+        nk = (int)((klen + BK - 1) / BK);
+        if constexpr (MODE == MODE_FWD) {
+            sa.init(g.packed + m0 / 16, g.wpr, (int)(g.wpr - m0 / 16));
+            act_b = (const char *)g.act0 + (int64_t)n0 * g.in * ES;
+            db.init((int64_t)g.in * ES, g.N - n0);
+        } else if constexpr (MODE == MODE_DX) {
+            sa.init(g.packed + (int64_t)m0 * g.wpr, g.wpr, g.M - m0, g.scale, g.out);
+            act_b = (const char *)g.act0 + (int64_t)n0 * g.out * ES;
+            db.init((int64_t)g.out * ES, g.N - n0);
+        } else {
+            act_a = (const char *)g.act0 + kbeg * g.in * ES + (int64_t)m0 * ES;
+            act_b = (const char *)g.act1 + kbeg * g.out * ES + (int64_t)n0 * ES;
+            dta.init((int64_t)g.in * ES, g.M - m0);
+            dtb.init((int64_t)g.out * ES, g.N - n0);
+        }
+        return true;
+    };
+
+    // DMA of step `it` of the current tile into stage S (activation tiles)
+    auto dma_step = [&](auto s_c, int it) {
+        constexpr int S = decltype(s_c)::value;
+        char *st = p_stage<S>();
+        const int64_t k0 = (int64_t)it * BK;
+        if constexpr (MODE == MODE_FWD || MODE == MODE_DX) {
+            const int kb = (MODE == MODE_FWD ? g.in : g.out) * ES;
+            db.issue(act_b + k0 * ES, (int)max<int64_t>(-1, (int64_t)kb - k0 * ES), st + P_A_BYTES);
+        } else {
+            const int rows_left = (int)max<int64_t>(-1, min<int64_t>(64, klen - k0));
+            dta.issue(act_a + k0 * g.in * ES, rows_left, st);
+            dtb.issue(act_b + k0 * g.out * ES, rows_left, st + P_T_BYTES);
+        }
+    };
+    // register fetch of the ternary operand of step `it` into set S
+    auto fetch_a = [&](auto s_c, int it) {
+        constexpr int S = decltype(s_c)::value;
+        if constexpr (MODE == MODE_FWD) {
+            const int64_t k0 = (int64_t)it * BK;
+            sa.template fetch<S>(k0, (int)max<int64_t>(-1, min<int64_t>(BK, klen - k0)));
+        } else if constexpr (MODE == MODE_DX) {
+            sa.template fetch<S>(it * BK);
+        }
+    };
+    // write part p (of 4) of register set S into stage D
+    auto commit_a = [&](auto s_c, auto d_c, int p) {
+        constexpr int S = decltype(s_c)::value, D = decltype(d_c)::value;
+        if constexpr (MODE == MODE_FWD || MODE == MODE_DX) {
+            u32x4 *smA = (u32x4 *)p_stage<D>();
+#pragma unroll
+            for (int j = 0; j < SA::NOUT; j++)
+                if (j % 4 == p) sa.template commit<S>(j, smA);
+        }
+    };
+    auto read_q = [&](auto s_c, u32x4 (&a)[4], u32x4 (&b)[4], int kk) {
+        constexpr int S = decltype(s_c)::value;
+        if constexpr (MODE == MODE_DW) p_read_tok(p_stage<S>(), a, b, wm, wn, lane, kk);
+        else p_read_kc(p_stage<S>(), a, b, arow, brow, h, kk);
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    f32x16 acc[4][4];
+    u32x4 fa[2][4], fb[2][4];
+
+    // one K step on stage CUR; stages and register sets alternate statically
+    auto body = [&](auto cur_c, int it) {
+        constexpr int CUR = decltype(cur_c)::value;
+        using ICUR = std::integral_constant<int, CUR>;
+        using INXT = std::integral_constant<int, 1 - CUR>;
+        dma_step(INXT{}, it + 1);
+        fetch_a(ICUR{}, it + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            if (kk < 3) read_q(ICUR{}, fa[(kk + 1) & 1], fb[(kk + 1) & 1], kk + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            p_mma(acc, fa[kk & 1], fb[kk & 1]);
+            commit_a(INXT{}, INXT{}, kk);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vm0();
+        __syncthreads();
+        read_q(INXT{}, fa[0], fb[0], 0);
+    };
+
+    // prologue loads of the first tile
+    bool have = begin_tile(0);
+    if (have) {
+        dma_step(I0{}, 0);
+        fetch_a(I0{}, 0);
+        fetch_a(I1{}, 1);
+    }
+    for (int j = 0; have; j++) {
+#pragma unroll
+        for (int p = 0; p < 4; p++) commit_a(I0{}, I0{}, p);
+        wait_vm0();
+        __syncthreads();
+#pragma unroll
+        for (int fm = 0; fm < 4; fm++)
+#pragma unroll
+            for (int fn = 0; fn < 4; fn++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) acc[fm][fn][i] = 0.0f;
+        read_q(I0{}, fa[0], fb[0], 0);
+        for (int it = 0; it < nk; it += 2) {
+            body(I0{}, it);
+            body(I1{}, it + 1);
+        }
+        // the last barrier has passed: both stages are free.  Keep this tile's
+        // coordinates for the epilogue and start the next tile's loads.
+        const int etm = tm, esp = sp, em0 = m0, en0 = n0;
+        have = begin_tile(j + 1);
+        if (have) {
+            dma_step(I0{}, 0);
+            fetch_a(I0{}, 0);
+            fetch_a(I1{}, 1);
+        }
+
+        // ---- epilogue of the finished tile.  acc[fm][fn][i] is C[m][n] with
+        //   m = m0 + wm*128 + fm*32 + 8*(i/4) + 4*h + i%4,  n = n0 + wn*128 + fn*32 + l32
+        const int mw = em0 + wm * 128, nw = en0 + wn * 128;
+        if constexpr (MODE == MODE_FWD || MODE == MODE_DX) {
+            const int ldo = (MODE == MODE_FWD) ? g.out : g.in;
+#pragma unroll
+            for (int fm = 0; fm < 4; fm++) {
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int m = mw + fm * 32 + 8 * q + 4 * h;
+                    if (m >= g.M) continue;
+                    f32x4 sc = {1.0f, 1.0f, 1.0f, 1.0f};
+                    if constexpr (MODE == MODE_FWD) sc = *(const f32x4 *)(g.scale + m);
+#pragma unroll
+                    for (int fn = 0; fn < 4; fn++) {
+                        const int n = nw + fn * 32 + l32;
+                        if (n >= g.N) continue;
+                        f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                                   acc[fm][fn][4 * q + 3]};
+                        if constexpr (MODE == MODE_FWD) v = v * sc;
+                        const int64_t o = (int64_t)n * ldo + m;
+                        if (MODE == MODE_FWD && g.y_bf16) {
+                            f32x2 a2 = {v.x, v.y}, b2 = {v.z, v.w};
+                            u32x2 pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(a2, bf16x2)),
+                                        __builtin_bit_cast(uint32_t, __builtin_convertvector(b2, bf16x2))};
+                            *(u32x2 *)((uint16_t *)g.out_ptr + o) = pk;
+                        } else {
+                            *(f32x4 *)((float *)g.out_ptr + o) = v;
+                        }
+                    }
+                }
+            }
+        } else {
+            float *dst = (float *)g.out_ptr;
+            if (g.splits > 1) {
+                dst += (int64_t)esp * g.M * g.N;
+#pragma unroll
+                for (int fm = 0; fm < 4; fm++)
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const int m = mw + fm * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                        if (m >= g.M) continue;
+#pragma unroll
+                        for (int fn = 0; fn < 4; fn++) {
+                            const int n = nw + fn * 32 + l32;
+                            if (n < g.N) dst[(int64_t)m * g.N + n] = acc[fm][fn][i];
+                        }
+                    }
+            } else {
+                float sc[4], ps[4];
+#pragma unroll
+                for (int fn = 0; fn < 4; fn++) {
+                    const int n = nw + fn * 32 + l32;
+                    sc[fn] = n < g.N ? g.scale[n] : 0.0f;
+                    ps[fn] = 0.0f;
+                }
+#pragma unroll
+                for (int fm = 0; fm < 4; fm++)
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const int m = mw + fm * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                        if (m >= g.M) continue;
+#pragma unroll
+                        for (int fn = 0; fn < 4; fn++) {
+                            const int n = nw + fn * 32 + l32;
+                            if (n >= g.N) continue;
+                            const float gv = acc[fm][fn][i];
+                            dst[(int64_t)m * g.N + n] = gv * sc[fn];
+                            const uint32_t word = g.packed[(int64_t)m * g.wpr + (n >> 4)];
+                            ps[fn] += gv * code_to_f32((word >> (2 * (n & 15))) & 3u);
+                        }
+                    }
+#pragma unroll
+                for (int fn = 0; fn < 4; fn++) ps[fn] += __shfl_xor(ps[fn], 32);
+                // cross-wave sum through a small LDS table of its own (the
+                // stages may already hold the next tile's data)
+                __shared__ float red[2 * 256];
+                if (h == 0) {
+#pragma unroll
+                    for (int fn = 0; fn < 4; fn++) red[wm * 256 + wn * 128 + fn * 32 + l32] = ps[fn];
+                }
+                __syncthreads();
+                if (tid < 256 && en0 + tid < g.N) g.part[(int64_t)etm * g.N + en0 + tid] = red[tid] + red[256 + tid];
+                __syncthreads();
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Small kernels
 // ---------------------------------------------------------------------------
 
@@ -707,9 +1155,31 @@ __global__ __launch_bounds__(256) void zero16_kernel(u32x4 *__restrict__ p, int6
 namespace {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 template <bool BF, int MODE>
 hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)p.grid), block(dev::NT);
+    if constexpr (BF) {
+        if (p.tile == TILE_256) {
+            // persistent: at most one workgroup per compute unit
+            const int64_t cus = device_cus();
+            const dim3 pgrid((unsigned)(p.grid < cus ? p.grid : cus));
+            hipLaunchKernelGGL((dev::gemm_pipe_kernel<MODE>), pgrid, block, 0, st, a);
+            return hipGetLastError();
+        }
+    }
     switch (p.tile) {
         case TILE_256: hipLaunchKernelGGL((dev::gemm_kernel<BF, MODE, 256>), grid, block, 0, st, a); break;
         case TILE_128: hipLaunchKernelGGL((dev::gemm_kernel<BF, MODE, 128>), grid, block, 0, st, a); break;
