@@ -23,6 +23,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "ternary_weight_linear_tern_amd", "csrc", "tern_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+COPY_BYTES = 1 << 30  # calibration copy size
 
 
 def kernel_src_hash() -> str:
@@ -37,8 +38,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large", choices=["rwkv_small", "mid", "large", "largest"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=24, help="oracle sample: token rows per projection")
-    ap.add_argument("--cpu-cols", type=int, default=6, help="oracle sample: output columns per projection")
+    ap.add_argument("--cpu-rows", type=int, default=192, help="oracle sample: token rows per projection")
+    ap.add_argument("--cpu-cols", type=int, default=48, help="oracle sample: output columns per projection")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, copy a 1 GiB buffer 3 times (known bytes, for scaling "
+                         "HBM traffic counters)")
     return ap.parse_args()
 
 
@@ -135,8 +139,9 @@ def main():
 
     # dominant kernel: the GEMM entry point with the largest share of the step
     dom = max(("fwd", "bwd_dx", "bwd_dw"), key=lambda p: part_ms[p])
-    dom_kernels = {"fwd": "gemm_kernel<MODE_FWD>", "bwd_dx": "gemm_kernel<MODE_DX>",
-                   "bwd_dw": "gemm_kernel<MODE_DW> (+ split-K and sgrad reductions)"}[dom]
+    dom_kernels = {"fwd": "gemm_pipe_kernel<MODE_FWD> (tern_linear_fwd)",
+                   "bwd_dx": "gemm_pipe_kernel<MODE_DX> (tern_linear_bwd_dx)",
+                   "bwd_dw": "gemm_pipe_kernel<MODE_DW> + dw_reduce + sgrad_reduce (tern_linear_bwd_dw)"}[dom]
     achieved = gemm_flops[dom] / (part_ms[dom] * 1e-3) / 1e12
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -150,6 +155,17 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom_kernels,
                 "flops_per_step": gemm_flops[dom], "ms_per_step": round(part_ms[dom], 4)}
+
+    if a.copy_calibration:
+        # one elementwise kernel per copy: reads and writes COPY_BYTES once
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.mul(src, 1, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not a.no_cpu_baseline:

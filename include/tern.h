@@ -115,9 +115,10 @@ size_t tern_linear_bwd_workspace_bytes(int64_t T, int64_t in, int64_t out, int32
  * Arithmetic: fp32 accumulation on the matrix cores.  With bf16 activations
  * the scale is folded into the bf16 B operand of the dX product as
  * +-bf16(scale[c]) (round to nearest even), since the scale sits on that
- * product's reduction index.  sgrad is summed in a fixed order (per tile, then
- * tiles in ascending row order, final sum in f64), so repeated calls on the
- * same inputs give bitwise-identical results.
+ * product's reduction index.  sgrad is summed in a fixed order (fp32 within a
+ * row tile, then the row-tile partials in ascending order in f64, in eight
+ * consecutive groups whose sums are added in ascending order), so repeated
+ * calls on the same inputs give bitwise-identical results.
  * Errors: NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, ALIAS, HIP.
  */
 int tern_linear_bwd(const void *X, const void *dY, int32_t act_dtype,

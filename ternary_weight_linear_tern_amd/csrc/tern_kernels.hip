@@ -1105,38 +1105,60 @@ __global__ __launch_bounds__(256) void materialize_kernel(const int8_t *__restri
 }
 
 // Split-K finish of dW: G = sum over splits (ascending), gq = G * scale, and
-// the sgrad partial of a block of kReduceRows rows (ascending r).
+// the sgrad partial of a block of kReduceRows rows (ascending r).  Each thread
+// owns 4 consecutive columns (16-byte loads and stores); a block covers 1024
+// columns of kReduceRows rows.
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ ws, int splits,
                                                         const float *__restrict__ scale,
                                                         const uint32_t *__restrict__ packed, int in,
                                                         int out, int64_t wpr, float *__restrict__ gq,
                                                         float *__restrict__ part) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= out) return;
-    const int r0 = blockIdx.y * 64;
-    const int r1 = min(in, r0 + 64);
-    const float s = scale[c];
+    const int r0 = blockIdx.y * kReduceRows;
+    const int r1 = min(in, r0 + kReduceRows);
+    const f32x4 s = *(const f32x4 *)(scale + c);
     const int64_t plane = (int64_t)in * out;
-    float p = 0.0f;
+    f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int r = r0; r < r1; r++) {
         const int64_t o = (int64_t)r * out + c;
-        float gv = 0.0f;
-        for (int k = 0; k < splits; k++) gv += ws[k * plane + o];
-        gq[o] = gv * s;
-        const uint32_t word = packed[(int64_t)r * wpr + (c >> 4)];
-        p += gv * code_to_f32((word >> (2 * (c & 15))) & 3u);
+        f32x4 gv = *(const f32x4 *)(ws + o);
+        for (int k = 1; k < splits; k++) gv += *(const f32x4 *)(ws + k * plane + o);
+        *(f32x4 *)(gq + o) = gv * s;
+        // the 4 codes of columns c .. c + 3 (c % 4 == 0, so one word holds them)
+        const uint32_t word = packed[(int64_t)r * wpr + (c >> 4)] >> (2 * (c & 15));
+        p.x += gv.x * code_to_f32(word & 3u);
+        p.y += gv.y * code_to_f32((word >> 2) & 3u);
+        p.z += gv.z * code_to_f32((word >> 4) & 3u);
+        p.w += gv.w * code_to_f32((word >> 6) & 3u);
     }
-    part[(int64_t)blockIdx.y * out + c] = p;
+    *(f32x4 *)(part + (int64_t)blockIdx.y * out + c) = p;
 }
 
-// sgrad[c] = sum of the partials in ascending row-block order, in f64.
+// sgrad[c] = sum of the row-block partials in ascending order, in f64, as a
+// fixed two-level sum: 8 consecutive groups of blocks are each summed in
+// ascending order, then the 8 group sums in ascending order.  A block of 256
+// threads serves 32 columns.
 __global__ __launch_bounds__(256) void sgrad_reduce_kernel(const float *__restrict__ part, int nparts,
                                                            int out, float *__restrict__ sgrad) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= out) return;
+    __shared__ double red[8][32];
+    const int cl = threadIdx.x & 31, grp = threadIdx.x >> 5;
+    const int c = blockIdx.x * 32 + cl;
+    const int chunk = (nparts + 7) / 8;
+    const int p0 = grp * chunk, p1 = min(nparts, p0 + chunk);
     double a = 0.0;
-    for (int p = 0; p < nparts; p++) a += (double)part[(int64_t)p * out + c];
-    sgrad[c] = (float)a;
+    if (c < out) {
+#pragma unroll 8
+        for (int p = p0; p < p1; p++) a += (double)part[(int64_t)p * out + c];
+    }
+    red[grp][cl] = a;
+    __syncthreads();
+    if (grp == 0 && c < out) {
+        double s = red[0][cl];
+#pragma unroll
+        for (int g2 = 1; g2 < 8; g2++) s += red[g2][cl];
+        sgrad[c] = (float)s;
+    }
 }
 
 // Zero fill in 16-byte units.
@@ -1216,7 +1238,7 @@ hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int thet
 
 hipError_t launch_dw_reduce(const float *ws, int splits, const float *scale, const uint32_t *packed,
                             int64_t in, int64_t out, float *gq, float *part, hipStream_t st) {
-    const dim3 grid((unsigned)cdiv(out, 256), (unsigned)cdiv(in, kReduceRows)), block(256);
+    const dim3 grid((unsigned)cdiv(out, 1024), (unsigned)cdiv(in, kReduceRows)), block(256);
     hipLaunchKernelGGL(dev::dw_reduce_kernel, grid, block, 0, st, ws, splits, scale, packed, (int)in,
                        (int)out, cdiv(out, 16), gq, part);
     return hipGetLastError();
@@ -1224,7 +1246,7 @@ hipError_t launch_dw_reduce(const float *ws, int splits, const float *scale, con
 
 hipError_t launch_sgrad_reduce(const float *part, int64_t nparts, int64_t out, float *sgrad, hipStream_t st) {
     if (out <= 0) return hipSuccess;
-    const dim3 grid((unsigned)cdiv(out, 256)), block(256);
+    const dim3 grid((unsigned)cdiv(out, 32)), block(256);
     hipLaunchKernelGGL(dev::sgrad_reduce_kernel, grid, block, 0, st, part, (int)nparts, (int)out, sgrad);
     return hipGetLastError();
 }

@@ -1,0 +1,115 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+    python -m ternary_weight_linear_tern_amd.rocprof_summary stats  <kernel_stats.csv> [title]
+    python -m ternary_weight_linear_tern_amd.rocprof_summary traffic <fetch_counter_collection.csv> \\
+        <write_counter_collection.csv> <workload> <dispatch_steps> [kernel_src]
+
+`traffic` attributes FETCH_SIZE / WRITE_SIZE (KiB per dispatch) to the library's
+entry points, scales both by what the same counters read for the calibration
+copy (bench.py --copy-calibration: 1 GiB read + 1 GiB written by one
+elementwise multiply-by-one kernel per copy), divides by the number of profiled steps, and writes
+profiles/traffic_counters.json, which bench.py reports as roofline.traffic
+while the kernel source is unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+COPY_KIB = (1 << 30) / 1024.0
+
+
+def entry_of(kernel: str) -> str | None:
+    k = kernel
+    if "materialize_kernel" in k:
+        return "materialize"
+    if "gemm" in k:
+        if "<0>" in k or ", 0," in k:
+            return "fwd"
+        if "<1>" in k or ", 1," in k:
+            return "bwd_dx"
+        if "<2>" in k or ", 2," in k:
+            return "bwd_dw"
+    if "dw_reduce" in k or "sgrad_reduce" in k:
+        return "bwd_dw"
+    return None
+
+
+def stats(path: str, title: str = "") -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = [f"# {title}" if title else "# kernel stats", "",
+           "| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['TotalDurationNs'])/1e6:.3f} | "
+                   f"{float(r['AverageNs'])/1e3:.1f} | {float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
+                   f"{float(r['Percentage']):.2f} |")
+    return "\n".join(out)
+
+
+def _counter_sums(path: str, counter: str):
+    per_kernel = defaultdict(float)
+    per_kernel_n = defaultdict(int)
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"]
+        per_kernel[name] += float(r["Counter_Value"])
+        per_kernel_n[name] += 1
+    return per_kernel, per_kernel_n
+
+
+def traffic(fetch_csv: str, write_csv: str, workload: str, steps: int, kernel_src: str | None = None):
+    f, fn = _counter_sums(fetch_csv, "FETCH_SIZE")
+    w, wn = _counter_sums(write_csv, "WRITE_SIZE")
+    copy_f = [v / fn[k] for k, v in f.items() if "MulFunctor" in k]
+    copy_w = [v / wn[k] for k, v in w.items() if "MulFunctor" in k]
+    # the calibration copies are the only multiply kernels in the run
+    fscale = COPY_KIB / max(copy_f) if copy_f else 1.0
+    wscale = COPY_KIB / max(copy_w) if copy_w else 1.0
+    ent = defaultdict(lambda: {"fetch_kib": 0.0, "write_kib": 0.0})
+    lines = [f"# HBM traffic per step, {workload} ({steps} profiled steps)", "",
+             f"calibration: 1 GiB copy reads FETCH_SIZE x {fscale:.4f}, WRITE_SIZE x {wscale:.4f}", "",
+             "| kernel | dispatches | FETCH KiB/dispatch | WRITE KiB/dispatch |", "|---|---|---|---|"]
+    for k in sorted(set(f) | set(w)):
+        lines.append(f"| {k[:80]} | {fn.get(k, 0)} | {f.get(k, 0)/max(fn.get(k, 1),1):.0f} | "
+                     f"{w.get(k, 0)/max(wn.get(k, 1),1):.0f} |")
+        e = entry_of(k)
+        if e:
+            ent[e]["fetch_kib"] += f.get(k, 0.0)
+            ent[e]["write_kib"] += w.get(k, 0.0)
+    out = {"kernel_src_sha256_16": None, "entries": {}, "calibration": {"fetch": fscale, "write": wscale}}
+    if kernel_src:
+        out["kernel_src_sha256_16"] = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    lines += ["", "| entry point | HBM read MB/step | HBM write MB/step |", "|---|---|---|"]
+    for e, v in sorted(ent.items()):
+        rd = v["fetch_kib"] * fscale * 1024 / steps
+        wr = v["write_kib"] * wscale * 1024 / steps
+        out["entries"][f"{workload}/{e}"] = {"read_bytes_per_step": rd, "write_bytes_per_step": wr,
+                                             "bytes_per_step": rd + wr}
+        lines.append(f"| {e} | {rd/1e6:.1f} | {wr/1e6:.1f} |")
+    return out, "\n".join(lines)
+
+
+if __name__ == "__main__":
+    cmd = sys.argv[1]
+    if cmd == "stats":
+        print(stats(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
+    elif cmd == "traffic":
+        src = sys.argv[6] if len(sys.argv) > 6 else os.path.join(PKG, "csrc", "tern_kernels.hip")
+        data, text = traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), src)
+        print(text)
+        dst = os.path.join(ROOT, "profiles", "traffic_counters.json")
+        os.makedirs(os.path.dirname(dst), exist_ok=True)
+        old = json.load(open(dst)) if os.path.exists(dst) else {}
+        if old.get("kernel_src_sha256_16") == data["kernel_src_sha256_16"]:
+            old.setdefault("entries", {}).update(data["entries"])
+            data["entries"] = old["entries"]
+        json.dump(data, open(dst, "w"), indent=1)
+    else:
+        raise SystemExit(__doc__)
