@@ -719,7 +719,8 @@ __device__ __forceinline__ bool p_item(int j, int total, int tiles_m, int tiles_
 // DMA of one K step of an activation tile whose K is contiguous (forward B = X,
 // dX B = dY): 256 rows x 128 bytes.  Wave w, instruction i writes LDS rows
 // (8w + i) * 8 .. + 7; lane l fills physical chunk l % 8 of row (l / 8) with the
-// logical chunk (l % 8) ^ (row % 8).
+// logical chunk (l % 8) ^ ((row / 2) % 8).  With that swizzle the 16 rows read by
+// 16 lanes of one fragment load cover all banks of a 256-byte window.
 struct DmaRows {
     uint32_t off[8];  // per instruction: byte offset of the lane's chunk, or OOB
     __device__ __forceinline__ void init(int64_t ld_bytes, int rows_valid) {
@@ -727,7 +728,7 @@ struct DmaRows {
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int row = (8 * w + i) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ (row & 7);
+            const int c = (lane & 7) ^ ((row >> 1) & 7);
             off[i] = row < rows_valid ? (uint32_t)(row * ld_bytes + c * 16) : OOB;
         }
     }
@@ -743,7 +744,7 @@ struct DmaRows {
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const int row = (8 * w + i) * 8 + (lane >> 3);
-                const int c = (lane & 7) ^ (row & 7);
+                const int c = (lane & 7) ^ ((row >> 1) & 7);
                 dma16(rs, lds_region + (8 * w + i) * 1024, c * 16 < kbytes_left ? off[i] : OOB);
             }
         }
@@ -753,7 +754,8 @@ struct DmaRows {
 // DMA of one K step of a token-major activation tile for dW: 64 token rows x
 // 256 features (512 bytes).  Wave w, instruction i writes rows 2 (8w + i) and
 // 2 (8w + i) + 1; lane l fills physical chunk l % 32 of row (l / 32) with the
-// logical chunk (l % 32) ^ (2 (row % 4)).
+// logical chunk (l % 32) ^ (4 (row % 4)), which puts the four token rows of a
+// transposing read in four different 64-byte quarters of a 256-byte window.
 struct DmaTok {
     uint32_t off[8];
     __device__ __forceinline__ void init(int64_t ld_bytes, int cols_valid) {
@@ -761,7 +763,7 @@ struct DmaTok {
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int row = 2 * (8 * w + i) + (lane >> 5);
-            const int c = (lane & 31) ^ (2 * (row & 3));
+            const int c = (lane & 31) ^ (4 * (row & 3));
             off[i] = c * 8 < cols_valid ? (uint32_t)(row * ld_bytes + c * 16) : OOB;
         }
     }
@@ -789,7 +791,7 @@ __device__ __forceinline__ void p_read_kc(const char *st, u32x4 (&a)[4], u32x4 (
     const int c = 2 * kk + h;
 #pragma unroll
     for (int f = 0; f < 4; f++) a[f] = *(const u32x4 *)(st + (arow + 32 * f) * P_ROWB_A + c * 16);
-    const int pc = c ^ (brow & 7);
+    const int pc = c ^ ((brow >> 1) & 7);
 #pragma unroll
     for (int f = 0; f < 4; f++) b[f] = *(const u32x4 *)(st + P_A_BYTES + (brow + 32 * f) * 128 + pc * 16);
 }
@@ -804,7 +806,7 @@ __device__ __forceinline__ u32x4 p_frag_tr(const char *tile, int krow0, int col)
 #pragma unroll
     for (int rd = 0; rd < 2; rd++) {
         const int k = krow0 + 4 * rd;
-        const int chunk = (col >> 3) ^ (2 * (k & 3));
+        const int chunk = (col >> 3) ^ (4 * (k & 3));
         const char *p = tile + k * 512 + chunk * 16 + (col & 7) * 2;
         v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16 *)p);
         const u32x2 u = __builtin_bit_cast(u32x2, v);
