@@ -58,8 +58,16 @@ extern "C" {
 #define TERN_ERR_ALIAS     -7  /* an output overlaps an input or another output */
 #define TERN_ERR_HIP       -8  /* the HIP runtime refused a launch */
 
-/* Number of uint32 words in the packed ternary form of an [in, out] matrix:
- * in * ceil(out / 16).  Returns -1 for negative sizes. */
+/* Number of uint32 words of a packed ternary handle for an [in, out] matrix
+ * (0 if in or out is 0, -1 for negative sizes).  The caller allocates this
+ * many words (4-byte aligned); tern_materialize fills all of them.  Layout:
+ *   words [0, in*ceil(out/16)): the canonical 2-bit matrix (see
+ *       tern_materialize);
+ *   from word ceil(in*ceil(out/16) / 64) * 64: two fragment-ordered copies of
+ *       the same codes, the forward operand (ceil(out/256) * ceil(in/32) * 512
+ *       words) then the dX operand (ceil(in/256) * ceil(out/32) * 512 words),
+ *       ordered for the loads of the 256 x 256 GEMM kernels.  They carry no
+ *       information beyond the canonical matrix. */
 int64_t tern_packed_words(int64_t in, int64_t out);
 
 /*
@@ -68,12 +76,13 @@ int64_t tern_packed_words(int64_t in, int64_t out);
  *               dead-zone rule is applied as is (the +-7 clamp belongs to the
  *               optimizer, not to this step).
  *   theta       dead-zone threshold, 1 <= theta <= 127 (the trainer uses 2).
- *   tern_packed uint32 [in, ceil(out/16)], written.  Code of (r, c): 00 = 0,
- *               01 = +1, 11 = -1 (10 is never written), at bits
- *               2*(c % 16) .. 2*(c % 16)+1 of word r*ceil(out/16) + c/16, least
- *               significant bits first; padding codes of a partial last word
- *               are 00.  One packed buffer serves the forward and the backward
- *               of the same step.
+ *   tern_packed handle of tern_packed_words(in, out) uint32 words, written.
+ *               Canonical part: code of (r, c) 00 = 0, 01 = +1, 11 = -1 (10 is
+ *               never written), at bits 2*(c % 16) .. 2*(c % 16)+1 of word
+ *               r*ceil(out/16) + c/16, least significant bits first; padding
+ *               codes of a partial last word are 00.  The fragment-ordered
+ *               copies that follow are derived from it.  One handle serves the
+ *               forward and the backward of the same step.
  * Errors: NULL, SHAPE, THETA, ALIGN, ALIAS, HIP.
  */
 int tern_materialize(const int8_t *q, int64_t in, int64_t out, int32_t theta,
@@ -82,7 +91,7 @@ int tern_materialize(const int8_t *q, int64_t in, int64_t out, int32_t theta,
 /*
  * tern_linear_fwd -- Y = X . W_eff with W_eff[r, c] = scale[c] * tern[r, c].
  *   X           [T, in] of act_dtype (TERN_F32 or TERN_BF16).
- *   tern_packed uint32 [in, ceil(out/16)] from tern_materialize.
+ *   tern_packed handle written by tern_materialize for these in, out.
  *   scale       fp32 [out].
  *   Y           [T, out] of y_dtype: TERN_F32, or TERN_BF16 (round to nearest
  *               even of the fp32 result) when act_dtype is TERN_BF16.

@@ -126,7 +126,7 @@ def tern_linear_bwd_workspace_bytes(T: int, n_in: int, n_out: int, act_dtype) ->
 
 
 def tern_materialize(q: torch.Tensor, theta: int, tern_packed: torch.Tensor, stream=None) -> None:
-    """q int8 [in, out] -> tern_packed int32/uint32 [in, ceil(out/16)]."""
+    """q int8 [in, out] -> packed ternary handle (see empty_packed)."""
     n_in, n_out = q.shape
     rc = lib().tern_materialize(_ptr(q), n_in, n_out, int(theta), _ptr(tern_packed), _stream(stream))
     _check("tern_materialize", rc)
@@ -175,7 +175,16 @@ def tern_linear_bwd_dw(X, dY, tern_packed, scale, gq, sgrad, workspace, stream=N
 # ---------------------------------------------------------------------------
 
 def empty_packed(n_in: int, n_out: int, device="cuda") -> torch.Tensor:
-    return torch.empty((n_in, (n_out + 15) // 16), dtype=torch.int32, device=device)
+    """A packed ternary handle: tern_packed_words(n_in, n_out) int32 words."""
+    return torch.empty((max(tern_packed_words(n_in, n_out), 1),), dtype=torch.int32, device=device)
+
+
+def packed_canonical(tern_packed: torch.Tensor, n_in: int, n_out: int) -> torch.Tensor:
+    """View of the canonical 2-bit matrix at the start of a packed handle:
+    [n_in, ceil(n_out / 16)] words, code of (r, c) at bits 2 (c % 16) of word
+    (r, c / 16)."""
+    wpr = (n_out + 15) // 16
+    return tern_packed.reshape(-1)[: n_in * wpr].view(n_in, wpr)
 
 
 def empty_workspace(T: int, n_in: int, n_out: int, act_dtype, device="cuda") -> torch.Tensor:

@@ -60,7 +60,7 @@ const char *tern_status_str(int status) {
 
 int64_t tern_packed_words(int64_t in, int64_t out) {
     if (in < 0 || out < 0) return -1;
-    return in * ((out + 15) / 16);
+    return packed_layout(in, out).total;
 }
 
 int tern_materialize(const int8_t *q, int64_t in, int64_t out, int32_t theta, uint32_t *tern_packed,
@@ -75,7 +75,9 @@ int tern_materialize(const int8_t *q, int64_t in, int64_t out, int32_t theta, ui
     if (ranges_overlap(q, qb, tern_packed, pb)) return TERN_ERR_ALIAS;
     // the 16-byte vector path needs every row of q 16-byte aligned
     const bool vec = out % 16 == 0 && aligned16(q);
-    return hip_status(launch_materialize(q, in, out, theta, vec, tern_packed, (hipStream_t)stream));
+    hipError_t e = launch_materialize(q, in, out, theta, vec, tern_packed, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_derive(tern_packed, in, out, (hipStream_t)stream);
+    return hip_status(e);
 }
 
 int tern_linear_fwd(const void *X, int32_t act_dtype, const uint32_t *tern_packed, const float *scale,
@@ -111,6 +113,8 @@ int tern_linear_fwd(const void *X, int32_t act_dtype, const uint32_t *tern_packe
     a.splits = (int)p.splits; a.kps = (int)p.k_per_split;
     a.in = (int)in; a.out = (int)out; a.wpr = (int)((out + 15) / 16); a.T = (int)T;
     a.y_bf16 = y_dtype == TERN_BF16;
+    a.frag = tern_packed + packed_layout(in, out).fwd_off;
+    a.nch = (int)((in + kFragChunk - 1) / kFragChunk);
     return hip_status(launch_gemm(p, bf, a, st));
 }
 
@@ -172,6 +176,8 @@ hipError_t enqueue_dx(const void *dY, bool bf, const uint32_t *tern_packed, cons
     if (dxb == 0) return hipSuccess;
     if (out == 0) return launch_zero(dX, dxb, st);  // empty sum
     GemmArgs a = args_for(L.dx, tern_packed, scale, T, in, out);
+    a.frag = tern_packed + packed_layout(in, out).dx_off;
+    a.nch = (int)((out + kFragChunk - 1) / kFragChunk);
     a.act0 = dY;
     a.out_ptr = dX;
     return launch_gemm(L.dx, bf, a, st);

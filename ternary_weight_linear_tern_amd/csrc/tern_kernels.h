@@ -15,6 +15,7 @@ struct GemmArgs {
     const void *act0;        // FWD: X, DX: dY, DW: X
     const void *act1;        // DW: dY
     const uint32_t *packed;  // tern, 2-bit packed [in][wpr]
+    const uint32_t *frag;    // FWD / DX: this product's fragment-ordered copy of tern
     const float *scale;      // [out]
     void *out_ptr;           // FWD: Y, DX: dX, DW: gq (1 split) or split partials
     float *part;             // DW with 1 split: sgrad partials [tiles_m][out]
@@ -22,11 +23,14 @@ struct GemmArgs {
     int tiles_m, tiles_n, splits, kps;
     int in, out, wpr, T;
     int y_bf16;
+    int nch;                 // FWD / DX: chunks of 32 K per tile in the fragment copy
 };
 
 hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStream_t st);
 hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int theta, bool vec,
                               uint32_t *packed, hipStream_t st);
+// Fragment-ordered copies of the canonical packed words (see PackedLayout).
+hipError_t launch_derive(uint32_t *packed, int64_t in, int64_t out, hipStream_t st);
 hipError_t launch_dw_reduce(const float *ws, int splits, const float *scale, const uint32_t *packed,
                             int64_t in, int64_t out, float *gq, float *part, hipStream_t st);
 hipError_t launch_sgrad_reduce(const float *part, int64_t nparts, int64_t out, float *sgrad,

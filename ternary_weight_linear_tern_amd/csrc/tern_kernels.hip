@@ -1071,6 +1071,347 @@ void gemm_pipe_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// Fragment-ordered copies of the packed ternary matrix, read by the forward
+// and dX GEMMs below.  View the operand as A[m][k] (forward: m = c, k = r;
+// dX: m = r, k = c) in tiles of 256 rows and chunks of 32 K.  The 512 words of
+// (tile, chunk) are ordered (wm, lane, fm): wm = 128-row half, lane = lane of
+// the wave, fm = 32-row MFMA fragment, so one 16-byte load per lane brings a
+// wave all four of its fragments.  Word (wm, lane, fm) holds the 16 codes of
+// row m = 256 tile + 128 wm + 32 fm + lane % 32 at k = 32 chunk + 16 kk +
+// 8 (lane / 32) + e (kk < 2, e < 8), each at bit 2p (e even) or 16 + 2p (e
+// odd) with p = 4 kk + e / 2: one shift and one mask leave the two codes of an
+// MFMA operand dword at bits 0-1 and 16-17.  Codes beyond the matrix are 00.
+// ---------------------------------------------------------------------------
+template <bool DXOP>
+__global__ __launch_bounds__(256) void derive_kernel(const uint32_t *__restrict__ canon, int64_t in,
+                                                     int64_t out, int64_t wpr, int64_t nch,
+                                                     uint32_t *__restrict__ frag, int64_t nwords) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nwords) return;
+    const int64_t tc = i >> 9;
+    const int d = (int)(i & 511);
+    const int64_t tile = tc / nch, chunk = tc - tile * nch;
+    const int wm = d >> 8, lane = (d >> 2) & 63, fm = d & 3;
+    const int64_t m = tile * 256 + wm * 128 + fm * 32 + (lane & 31);
+    const int64_t M = DXOP ? in : out, K = DXOP ? out : in;
+    uint32_t word = 0;
+    if (m < M) {
+#pragma unroll
+        for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const int64_t k = chunk * 32 + kk * 16 + (lane >> 5) * 8 + e;
+                if (k >= K) continue;
+                const int64_t r = DXOP ? m : k, c = DXOP ? k : m;
+                const uint32_t code = (canon[r * wpr + (c >> 4)] >> (2 * (c & 15))) & 3u;
+                const int p = 4 * kk + (e >> 1);
+                word |= code << ((e & 1) ? 16 + 2 * p : 2 * p);
+            }
+    }
+    frag[i] = word;
+}
+
+// ---------------------------------------------------------------------------
+// Forward and dX GEMM without workgroup barriers (bf16, 256 x 256 tiles,
+// persistent).  Each wave computes its 128 x 128 block on its own:
+//   * its 128 activation rows (X or dY) stream into a private ring of four LDS
+//     stages, 32 K per chunk, with direct-to-LDS buffer loads issued three
+//     chunks ahead, together with the chunk's fragment words (and, for dX, the
+//     chunk's 32 scales);
+//   * the ternary operand is decoded from the fragment words straight into
+//     MFMA operand registers: never staged as bf16;
+//   * a wave waits only on its own loads (vmcnt), never on another wave.
+// The two waves that share activation rows (or fragment words) load them from
+// L1.  The forward epilogue multiplies by scale[c] (staged in LDS when the tile
+// starts); the dX operand carries +-bf16(scale[c]).
+// ---------------------------------------------------------------------------
+constexpr int R_KC = 32;                         // K per chunk
+constexpr int R_NST = 4;                         // LDS stages per wave
+constexpr int R_B = 128 * 64;                    // activation rows of a stage: 128 x 64 bytes
+constexpr int R_A = 1024;                        // fragment words of a stage: 64 lanes x 16 bytes
+constexpr int R_S = 256;                         // dX scales of a stage (one 4-byte DMA: 64 x 4 bytes)
+constexpr int R_STAGE = R_B + R_A + R_S;         // 9472
+constexpr int R_ESC = 4 * 512;                   // forward: scales of four tiles x 128 rows
+constexpr int R_WAVE = R_NST * R_STAGE + R_ESC;  // 39936
+__shared__ __attribute__((aligned(16))) char r_lds[4 * R_WAVE];
+
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void *lds_wave_base, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)lds_wave_base, 4, voff, 0, 0, 0);
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding
+// (and fence the compiler on both sides).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Stage rows are 64 bytes (32 K); the 16-byte chunk c of row r sits in slot
+// c ^ ((r / 4) % 4), which makes the 16 rows read by 16 lanes of a fragment
+// load hit 16 different slots of a 256-byte bank window.
+__device__ __forceinline__ void r_read_b(const char *st, u32x4 (&b)[4], int l32, int h, int kk) {
+    const int ps = (2 * kk + h) ^ ((l32 >> 2) & 3);
+#pragma unroll
+    for (int f = 0; f < 4; f++) b[f] = *(const u32x4 *)(st + (f * 32 + l32) * 64 + ps * 16);
+}
+
+// Two ternary codes at bits 0-1 and 16-17 of t (higher bits ignored) times a
+// pair of bf16 scales: p4 is the pair XOR 0x40004000.  Per 16-bit half: bits
+// 14-15 of (t << 14) are (nonzero, negative), which XORed into p4 restore the
+// scale (code 01) or flip its sign (code 11); the mask keeps nonzero codes.
+__device__ __forceinline__ uint32_t r_scaled_pair(uint32_t t, uint32_t p4) {
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 tv = __builtin_bit_cast(s16x2, t);
+    const s16x2 sg = tv << (short)14;
+    const s16x2 nz = (s16x2)(tv << (short)15) >> (short)15;
+    return (p4 ^ __builtin_bit_cast(uint32_t, sg)) & __builtin_bit_cast(uint32_t, nz);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_rd_kernel(GemmArgs g) {
+    static_assert(MODE == MODE_FWD || MODE == MODE_DX, "forward and dX only");
+    constexpr int ES = 2;
+    // vector memory operations per chunk issue: 8 activation + 1 fragment (+ 1 scale)
+    constexpr int OPS = MODE == MODE_DX ? 10 : 9;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
+    const int total = g.tiles_m * g.tiles_n;
+    const int nch = g.nch;
+    const int nch2 = (nch + 1) & ~1;   // chunks per tile, padded to even for the 2-way unroll
+    const int64_t ld = (int64_t)g.K * ES;   // bytes per activation row
+    char *wl = r_lds + wave * R_WAVE;
+    // slot of this lane's 16 bytes in every DMA row group, and its logical chunk
+    const int cb = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
+
+    // ---- issue side: chunk ic of tile ij (coordinates itm, itn); iv false once
+    // the tiles are exhausted (then every load is out of range: no memory
+    // access, zeros into LDS, the same instruction count)
+    int ij = 0, ic = 0, itm = 0, itn = 0, isp = 0;
+    bool iv = p_item(0, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+    const char *ib = nullptr;   // this wave's first activation row of tile ij
+    uint32_t boff[8];           // per DMA instruction: row * ld + cb, or OOB
+    auto set_itile = [&]() __attribute__((always_inline)) {
+        const int n0 = itn * 256 + wn * 128;
+        ib = (const char *)g.act0 + (int64_t)n0 * ld;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int row = 16 * i + (lane >> 2);
+            boff[i] = n0 + row < g.N ? (uint32_t)(row * ld) + (uint32_t)cb : OOB;
+        }
+    };
+    if (iv) set_itile();
+
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        char *st = wl + s * R_STAGE;
+        const int64_t k0 = (int64_t)ic * R_KC;
+        const bool kin = iv && k0 * ES + cb < ld;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(ib + k0 * ES);
+#pragma unroll
+        for (int i = 0; i < 8; i++) dma16(rb, st + i * 1024, kin ? boff[i] : OOB);
+        // chunks past the copy's last one (the count is padded to even) read zeros
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.frag + ((int64_t)itm * nch + ic) * 512 + wm * 256);
+        dma16(ra, st + R_B, (iv && ic < nch) ? (uint32_t)lane * 16u : OOB);
+        if constexpr (MODE == MODE_DX) {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scale + k0);
+            dma4(rs, st + R_B + R_A, (iv && lane < 32 && k0 + lane < g.K) ? (uint32_t)lane * 4u : OOB);
+        } else {
+            if (iv && ic == 0) {
+                // this wave's 128 scales of the tile, for its epilogue
+                const int mb = itm * 256 + wm * 128;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scale + mb);
+                char *esc = wl + R_NST * R_STAGE + (ij & 3) * 512;
+#pragma unroll
+                for (int q = 0; q < 2; q++)
+                    dma4(rs, esc + q * 256, mb + 64 * q + lane < g.M ? (uint32_t)(64 * q + lane) * 4u : OOB);
+            }
+        }
+        if (iv && ++ic == nch2) {
+            ic = 0;
+            ++ij;
+            iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+            if (iv) set_itile();
+        }
+    };
+
+    // ---- compute side: tile cj
+    int cj = 0, ctm = 0, ctn = 0, csp = 0;
+    bool cv = p_item(0, total, g.tiles_m, g.tiles_n, ctm, ctn, csp);
+    int hist = 0;   // bit 0: the previous chunk ended a tile; bit 1: the one before
+
+    f32x16 acc[4][4];
+    u32x4 fa[2];        // fragment words (one dword per fm) of the current / next chunk
+    u32x4 fb0[2][4];    // activation fragments, K quarter 0, of the current / next chunk
+    u32x4 fb1[4];       // K quarter 1 of the current chunk
+    uint32_t p4[2][8];  // dX: bf16 scale pairs ^ 0x40004000 of the current / next chunk
+
+    auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int fm = 0; fm < 4; fm++)
+#pragma unroll
+            for (int fn = 0; fn < 4; fn++)
+#pragma unroll
+                for (int i = 0; i < 16; i++) acc[fm][fn][i] = 0.0f;
+    };
+
+    // fragment words, quarter-0 activation fragments and scales of stage S
+    auto read_ahead = [&](int s, auto sl_c) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sl_c)::value;
+        const char *st = wl + s * R_STAGE;
+        fa[SL] = *(const u32x4 *)(st + R_B + lane * 16);
+        r_read_b(st, fb0[SL], l32, h, 0);
+        if constexpr (MODE == MODE_DX) {
+            const float *sc = (const float *)(st + R_B + R_A);
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++) {
+                const f32x4 lo = *(const f32x4 *)(sc + 16 * kk + 8 * h);
+                const f32x4 hi = *(const f32x4 *)(sc + 16 * kk + 8 * h + 4);
+                const f32x2 v0 = {lo.x, lo.y}, v1 = {lo.z, lo.w}, v2 = {hi.x, hi.y}, v3 = {hi.z, hi.w};
+                p4[SL][4 * kk + 0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2)) ^ 0x40004000u;
+                p4[SL][4 * kk + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2)) ^ 0x40004000u;
+                p4[SL][4 * kk + 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2)) ^ 0x40004000u;
+                p4[SL][4 * kk + 3] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v3, bf16x2)) ^ 0x40004000u;
+            }
+        }
+    };
+
+    // dword j of decoded fragment f (K quarter f / 4, rows fm = f % 4) of
+    // fragment words w4
+    auto dec = [&](const u32x4 &w4, const uint32_t (&pp)[8], int f, int j) __attribute__((always_inline)) {
+        const int kk = f >> 2, fm = f & 3;
+        const uint32_t t = w4[fm] >> (2 * (4 * kk + j));
+        if constexpr (MODE == MODE_FWD) return tern_pair_bf16(t & 0x00030003u);
+        else return r_scaled_pair(t, pp[4 * kk + j]);
+    };
+    constexpr int DEC_OPS = MODE == MODE_FWD ? 4 : 6;   // VALU per decoded dword
+    u32x4 acur;   // decoded fragment whose MFMAs come next (carried across chunks)
+
+    // Epilogue of tile (ctm, ctn): 64 buffer stores per wave whatever the edges
+    // (out-of-range stores get an out-of-range offset), so the vmcnt arithmetic
+    // of the main loop holds.  Lane offsets cover the 4 columns n of the lane;
+    // the row block m goes in the scalar offset.  M is a multiple of 8 and the
+    // 8-row groups are wave-uniform, so the m test is scalar.
+    auto epilogue = [&]() __attribute__((always_inline)) {
+        const int mw = ctm * 256 + wm * 128, nw = ctn * 256 + wn * 128;
+        const int ldo = MODE == MODE_FWD ? g.out : g.in;
+        const bool obf = MODE == MODE_FWD && g.y_bf16;
+        const int esz = obf ? 2 : 4;
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc((const char *)g.out_ptr + ((int64_t)nw * ldo + mw) * esz);
+        uint32_t vo[4];
+#pragma unroll
+        for (int fn = 0; fn < 4; fn++) {
+            const int nl = fn * 32 + l32;
+            vo[fn] = nw + nl < g.N ? (uint32_t)((nl * ldo + 4 * h) * esz) : OOB;
+        }
+        const float *esc = (const float *)(wl + R_NST * R_STAGE + (cj & 3) * 512) + 4 * h;
+        auto rows = [&](auto obf_c) __attribute__((always_inline)) {
+            constexpr bool OBF = decltype(obf_c)::value;
+#pragma unroll
+            for (int fm = 0; fm < 4; fm++) {
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int ml = fm * 32 + 8 * q;
+                    f32x4 sc = {1.0f, 1.0f, 1.0f, 1.0f};
+                    if constexpr (MODE == MODE_FWD) sc = *(const f32x4 *)(esc + ml);
+                    const bool mok = mw + ml < g.M;
+                    const int so = ml * esz;
+#pragma unroll
+                    for (int fn = 0; fn < 4; fn++) {
+                        f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                                   acc[fm][fn][4 * q + 3]};
+                        if constexpr (MODE == MODE_FWD) v = v * sc;
+                        const uint32_t off = mok ? vo[fn] : OOB;
+                        if constexpr (OBF) {
+                            const f32x2 a2 = {v.x, v.y}, b2 = {v.z, v.w};
+                            const u32x2 pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(a2, bf16x2)),
+                                              __builtin_bit_cast(uint32_t, __builtin_convertvector(b2, bf16x2))};
+                            __builtin_amdgcn_raw_buffer_store_b64(pk, ro, off, so, 0);
+                        } else {
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off, so, 0);
+                        }
+                    }
+                }
+            }
+        };
+        if (obf) rows(std::true_type{});
+        else rows(std::false_type{});
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    int sc = 0;   // LDS stage of the current chunk
+
+    // one chunk (register slot SL): issue three chunks ahead, then the eight
+    // fragments (K quarter, 32 rows) of 4 MFMAs each.  The next fragment is
+    // decoded one dword per MFMA while the current one multiplies (the first
+    // fragment of the next chunk during the last one of this chunk); halfway,
+    // wait for the next chunk's loads and read its first fragments.
+    auto chunk = [&](auto sl_c) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sl_c)::value, SL1 = SL ^ 1;
+        issue((sc + 3) & 3);
+        r_read_b(wl + sc * R_STAGE, fb1, l32, h, 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < 8; f++) {
+            if (f == 4) {
+                // loads issued after the next chunk's: the two later chunk
+                // issues, plus 64 epilogue stores if a tile ended since
+                if (hist) wait_vm<63>();
+                else wait_vm<2 * OPS>();
+                read_ahead((sc + 1) & 3, std::integral_constant<int, SL1>{});
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const int fm = f & 3;
+            u32x4 anx;
+#pragma unroll
+            for (int fn = 0; fn < 4; fn++) {
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, acur), __builtin_bit_cast(bf16x8, f < 4 ? fb0[SL][fn] : fb1[fn]),
+                    acc[fm][fn], 0, 0, 0);
+                anx[fn] = f < 7 ? dec(fa[SL], p4[SL], f + 1, fn) : dec(fa[SL1], p4[SL1], 0, fn);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, DEC_OPS, 0);  // then the decode
+            }
+            acur = anx;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sc = (sc + 1) & 3;
+        hist = (hist << 1) & 3;
+    };
+
+    // prologue: three chunks in flight, then the first one's fragments
+    issue(0);
+    issue(1);
+    issue(2);
+    wait_vm<2 * OPS>();
+    read_ahead(0, I0{});
+#pragma unroll
+    for (int j = 0; j < 4; j++) acur[j] = dec(fa[0], p4[0], 0, j);
+    zero_acc();
+    // tiles, then their chunks (the issue side runs three chunks ahead, across
+    // tile boundaries)
+    while (cv) {
+        for (int c = 0; c < nch2; c += 2) {
+            chunk(I0{});
+            chunk(I1{});
+        }
+        epilogue();
+        zero_acc();
+        ++cj;
+        cv = p_item(cj, total, g.tiles_m, g.tiles_n, ctm, ctn, csp);
+        hist |= 1;
+    }
+    // the last issues were out-of-range loads still writing zeros into this
+    // wave's stages: drain them (and the stores) before the workgroup ends
+    wait_vm<0>();
+}
+
+// ---------------------------------------------------------------------------
 // Small kernels
 // ---------------------------------------------------------------------------
 
@@ -1200,7 +1541,10 @@ hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
             // persistent: at most one workgroup per compute unit
             const int64_t cus = device_cus();
             const dim3 pgrid((unsigned)(p.grid < cus ? p.grid : cus));
-            hipLaunchKernelGGL((dev::gemm_pipe_kernel<MODE>), pgrid, block, 0, st, a);
+            if constexpr (MODE == MODE_DW)
+                hipLaunchKernelGGL((dev::gemm_pipe_kernel<MODE>), pgrid, block, 0, st, a);
+            else
+                hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE>), pgrid, block, 0, st, a);
             return hipGetLastError();
         }
     }
@@ -1235,6 +1579,17 @@ hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int thet
         hipLaunchKernelGGL((dev::materialize_kernel<true>), grid, block, 0, st, q, out, wpr, theta, packed, nwords);
     else
         hipLaunchKernelGGL((dev::materialize_kernel<false>), grid, block, 0, st, q, out, wpr, theta, packed, nwords);
+    return hipGetLastError();
+}
+
+hipError_t launch_derive(uint32_t *packed, int64_t in, int64_t out, hipStream_t st) {
+    const PackedLayout L = packed_layout(in, out);
+    if (L.total == 0) return hipSuccess;
+    const int64_t wpr = cdiv(out, 16);
+    hipLaunchKernelGGL((dev::derive_kernel<false>), dim3((unsigned)cdiv(L.fwd_words, 256)), dim3(256), 0, st,
+                       packed, in, out, wpr, cdiv(in, kFragChunk), packed + L.fwd_off, L.fwd_words);
+    hipLaunchKernelGGL((dev::derive_kernel<true>), dim3((unsigned)cdiv(L.dx_words, 256)), dim3(256), 0, st,
+                       packed, in, out, wpr, cdiv(out, kFragChunk), packed + L.dx_off, L.dx_words);
     return hipGetLastError();
 }
 

@@ -32,6 +32,18 @@ int validate_shape(int64_t T, int64_t in, int64_t out) {
     return TERN_OK;
 }
 
+PackedLayout packed_layout(int64_t in, int64_t out) {
+    PackedLayout L;
+    if (in <= 0 || out <= 0) return L;
+    L.canon_words = in * cdiv(out, 16);
+    L.fwd_off = cdiv(L.canon_words, 64) * 64;   // 256-byte aligned copies
+    L.fwd_words = cdiv(out, kFragTileRows) * cdiv(in, kFragChunk) * kFragWords;
+    L.dx_off = L.fwd_off + L.fwd_words;
+    L.dx_words = cdiv(in, kFragTileRows) * cdiv(out, kFragChunk) * kFragWords;
+    L.total = L.dx_off + L.dx_words;
+    return L;
+}
+
 bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
     uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;

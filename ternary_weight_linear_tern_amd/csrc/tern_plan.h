@@ -59,6 +59,25 @@ constexpr int64_t kMaxT = (int64_t(1) << 31) - 1;
 
 int validate_shape(int64_t T, int64_t in, int64_t out);
 
+// Layout of a packed ternary handle (in uint32 words).  The canonical 2-bit
+// matrix comes first; two fragment-ordered copies of it follow, one for the
+// forward operand (rows m = output columns, K = input rows) and one for the dX
+// operand (rows m = input rows, K = output columns).  Each copy holds, per
+// tile of 256 rows and chunk of 32 K, 512 words in the order the 256 x 256
+// GEMMs load them (one 16-byte load per lane and chunk).
+constexpr int64_t kFragTileRows = 256;
+constexpr int64_t kFragChunk = 32;
+constexpr int64_t kFragWords = 512;   // words per (tile, chunk)
+
+struct PackedLayout {
+    int64_t canon_words = 0;           // in * ceil(out / 16)
+    int64_t fwd_off = 0, fwd_words = 0;
+    int64_t dx_off = 0, dx_words = 0;
+    int64_t total = 0;
+};
+
+PackedLayout packed_layout(int64_t in, int64_t out);
+
 // True if [a, a + na) and [b, b + nb) overlap (empty ranges never overlap).
 bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb);
 

@@ -76,5 +76,6 @@ class DeviceProjection:
     def results(self) -> dict:
         torch.cuda.synchronize()
         Y = self.Y.float() if self.Y.dtype == torch.bfloat16 else self.Y
-        return dict(packed=self.packed.cpu().numpy().view(np.uint32), Y=Y.cpu().numpy(),
+        pk = tl.packed_canonical(self.packed, self.n_in, self.n_out)
+        return dict(packed=pk.cpu().numpy().view(np.uint32), Y=Y.cpu().numpy(),
                     dX=self.dX.cpu().numpy(), gq=self.gq.cpu().numpy(), sgrad=self.sgrad.cpu().numpy())

@@ -50,12 +50,25 @@ def test_status_strings(L):
     assert "gfx950" in tl.tern_version()
 
 
+def _layout_words(n_in, n_out):
+    """The handle layout of include/tern.h: canonical words, then the forward
+    and dX fragment copies (512 words per 256-row tile and 32-wide K chunk),
+    the first copy starting on a 64-word boundary."""
+    if n_in == 0 or n_out == 0:
+        return 0
+    cd = lambda a, b: -(-a // b)
+    canon = n_in * cd(n_out, 16)
+    return cd(canon, 64) * 64 + (cd(n_out, 256) * cd(n_in, 32) + cd(n_in, 256) * cd(n_out, 32)) * 512
+
+
 def test_packed_words(L):
     assert tl.tern_packed_words(0, 0) == 0
-    assert tl.tern_packed_words(3, 16) == 3
-    assert tl.tern_packed_words(3, 17) == 6
-    assert tl.tern_packed_words(2, 20) == 4
+    assert tl.tern_packed_words(0, 32) == 0
     assert tl.tern_packed_words(-1, 4) == -1
+    assert tl.tern_packed_words(3, 16) == 64 + 512 + 512
+    assert tl.tern_packed_words(256, 256) == 4096 + (8 + 8) * 512
+    for n_in, n_out in [(3, 17), (2, 20), (136, 264), (2048, 8192), (4096, 16384)]:
+        assert tl.tern_packed_words(n_in, n_out) == _layout_words(n_in, n_out), (n_in, n_out)
 
 
 def test_materialize_rejects(L):

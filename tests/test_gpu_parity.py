@@ -59,7 +59,7 @@ def test_materialize_all_int8(o, theta):
     pk = tl.empty_packed(256, 64)
     tl.tern_materialize(qd, theta, pk)
     torch.cuda.synchronize()
-    got = pk.cpu().numpy().view(np.uint32)
+    got = tl.packed_canonical(pk, 256, 64).cpu().numpy().view(np.uint32)
     assert np.array_equal(got, o.pack(o.tern(q, theta)))
 
 
@@ -76,7 +76,8 @@ def test_materialize_ragged(o, n_in, n_out, aligned):
     for theta in (2, 5):
         tl.tern_materialize(qd, theta, pk)
         torch.cuda.synchronize()
-        assert np.array_equal(pk.cpu().numpy().view(np.uint32), o.pack(o.tern(q, theta)))
+        got = tl.packed_canonical(pk, n_in, n_out).cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, o.pack(o.tern(q, theta)))
 
 
 # ---------------------------------------------------------------------------
@@ -196,7 +197,7 @@ def sampled_case(o, wname, proj):
     dXg = d.dX[rt].cpu().numpy()
     gqg = d.gq[:, ct].cpu().numpy()
     sgg = d.sgrad[ct].cpu().numpy()
-    pk = d.packed.cpu().numpy().view(np.uint32)
+    pk = tl.packed_canonical(d.packed, n_in, n_out).cpu().numpy().view(np.uint32)
     assert np.array_equal(pk, o.pack(o.tern(p.q, p.theta))), "packing differs"
     Y = o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows)
     dX = o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows)
@@ -311,8 +312,9 @@ def test_outputs_stay_in_bounds():
     bX, dX = guarded((T, n_in), torch.float32)
     bq, gq = guarded((n_in, n_out), torch.float32)
     bs, sg = guarded((n_out,), torch.float32)
-    bp = torch.full((n_in * 9 + 2 * G,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
-    pk = bp[G:G + n_in * 9].view(n_in, 9)
+    npk = tl.tern_packed_words(n_in, n_out)
+    bp = torch.full((npk + 2 * G,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    pk = bp[G:G + npk]
     tl.tern_materialize(d.q, 2, pk)
     tl.tern_linear_fwd(d.X, pk, d.scale, Y)
     tl.tern_linear_bwd(d.X, d.dY, pk, d.scale, dX, gq, sg, d.ws)
