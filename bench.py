@@ -139,8 +139,8 @@ def main():
 
     # dominant kernel: the GEMM entry point with the largest share of the step
     dom = max(("fwd", "bwd_dx", "bwd_dw"), key=lambda p: part_ms[p])
-    dom_kernels = {"fwd": "gemm_pipe_kernel<MODE_FWD> (tern_linear_fwd)",
-                   "bwd_dx": "gemm_pipe_kernel<MODE_DX> (tern_linear_bwd_dx)",
+    dom_kernels = {"fwd": "gemm_rd_kernel<MODE_FWD> (tern_linear_fwd)",
+                   "bwd_dx": "gemm_rd_kernel<MODE_DX> (tern_linear_bwd_dx)",
                    "bwd_dw": "gemm_pipe_kernel<MODE_DW> + dw_reduce + sgrad_reduce (tern_linear_bwd_dw)"}[dom]
     achieved = gemm_flops[dom] / (part_ms[dom] * 1e-3) / 1e12
     traffic = None

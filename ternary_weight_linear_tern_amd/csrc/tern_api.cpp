@@ -195,6 +195,7 @@ hipError_t enqueue_dw(const void *X, const void *dY, bool bf, const uint32_t *te
     }
     float *part = (float *)((char *)workspace + L.part_off);
     GemmArgs a = args_for(L.dw, tern_packed, scale, T, in, out);
+    a.frag = tern_packed + packed_layout(in, out).fwd_off;   // tern codes for the sgrad partials
     a.act0 = X;
     a.act1 = dY;
     a.part = part;

@@ -648,44 +648,30 @@ void gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined bf16 GEMM for 256 x 256 tiles (the large-problem path).
-//
-// Per workgroup: a persistent loop over output tiles (and K splits).  Per K
-// step of 64:
-//   * activation tiles (X or dY) go from HBM straight into LDS with
-//     buffer_load ... lds (no registers, no VALU); their rows are stored
-//     unpadded with the 16-byte chunk index XOR-swizzled by the row, so the
-//     MFMA fragment reads are conflict-free;
-//   * the ternary operand (forward, dX) is read as packed words into one of two
-//     register sets two steps ahead, decoded with VALU and written to LDS in
-//     four parts spread over the MFMAs of the current step;
-//   * dW reads both operands token-major (their natural layout) and builds the
-//     MFMA fragments with ds_read_b64_tr_b16 transposing reads;
-//   * fragments of K quarter q + 1 are read while the MFMAs of quarter q run;
-//   * one barrier per step; two LDS stages (separate __shared__ arrays).
-// A tile's epilogue stores overlap the next tile's first loads.
+// dW GEMM (bf16, 256 x 256 tiles, persistent, split-K): G[r][c] = sum over
+// tokens t of X[t][r] dY[t][c].  Both operands are token-major.  They stream
+// into a four-stage LDS ring in chunks of 32 tokens with direct-to-LDS buffer
+// loads issued three chunks ahead (across tile and split boundaries), and the
+// MFMA fragments come from ds_read_b64_tr_b16 transposing reads.  One barrier
+// per chunk; the MFMAs of a chunk's second K quarter run after the barrier,
+// while the next chunk's first fragments load.
+// Epilogue, one split: gq = G * scale[c], and the tile's per-column sum of
+// G * tern over its 256 rows (fixed order) into the partial table; several
+// splits: the split's raw G, summed by dw_reduce_kernel.
 // ---------------------------------------------------------------------------
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int P_BM = 256;                 // tile rows (m) and columns (n)
-constexpr int P_ROWB_A = 144;             // padded LDS row (bytes) of a decoded operand tile
-constexpr int P_A_BYTES = P_BM * P_ROWB_A;        // 36864
-constexpr int P_B_BYTES = P_BM * 128;             // 32768, swizzled 128-byte rows
-constexpr int P_T_BYTES = 64 * 512;               // 32768, [64 k][256] swizzled 512-byte rows
-
-// The two LDS stages.  Forward / dX: decoded operand (A) + activation (B);
-// dW: two token-major activation tiles.  Separate objects per stage let the
-// compiler keep reads of one stage independent of DMA into the other.
-__shared__ __attribute__((aligned(16))) char p_lds0[P_A_BYTES + P_B_BYTES];
-__shared__ __attribute__((aligned(16))) char p_lds1[P_A_BYTES + P_B_BYTES];
-
-template <int S>
-__device__ __forceinline__ char *p_stage() {
-    if constexpr (S == 0) return p_lds0;
-    else return p_lds1;
-}
+constexpr int W_KC = 64;                 // tokens per chunk
+constexpr int W_NST = 2;                 // LDS stages
+constexpr int W_AHEAD = W_NST - 1;       // chunks issued ahead of the one computed
+constexpr int W_Q = W_KC / 16;           // MFMA K quarters per chunk
+constexpr int W_DR = W_KC / 8;           // DMA instructions per wave per operand and chunk
+constexpr int W_OP = W_KC * 512;         // one operand of a stage: W_KC tokens x 256 features
+constexpr int W_STAGE = 2 * W_OP;
+__shared__ __attribute__((aligned(16))) char w_lds[W_NST * W_STAGE];
+__shared__ float w_red[2 * 256];         // cross-wave sgrad partials of a tile
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void *lds_wave_base, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)lds_wave_base, 16, voff, 0, 0, 0);
@@ -716,89 +702,35 @@ __device__ __forceinline__ bool p_item(int j, int total, int tiles_m, int tiles_
     return true;
 }
 
-// DMA of one K step of an activation tile whose K is contiguous (forward B = X,
-// dX B = dY): 256 rows x 128 bytes.  Wave w, instruction i writes LDS rows
-// (8w + i) * 8 .. + 7; lane l fills physical chunk l % 8 of row (l / 8) with the
-// logical chunk (l % 8) ^ ((row / 2) % 8).  With that swizzle the 16 rows read by
-// 16 lanes of one fragment load cover all banks of a 256-byte window.
-struct DmaRows {
-    uint32_t off[8];  // per instruction: byte offset of the lane's chunk, or OOB
-    __device__ __forceinline__ void init(int64_t ld_bytes, int rows_valid) {
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int row = (8 * w + i) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ ((row >> 1) & 7);
-            off[i] = row < rows_valid ? (uint32_t)(row * ld_bytes + c * 16) : OOB;
-        }
-    }
-    // base: row 0 of the tile, at this step's K offset; kbytes_left: valid
-    // bytes of K from there (>= 128 except on the last step)
-    __device__ __forceinline__ void issue(const char *base, int kbytes_left, char *lds_region) const {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-        if (kbytes_left >= 128) {
-#pragma unroll
-            for (int i = 0; i < 8; i++) dma16(rs, lds_region + (8 * w + i) * 1024, off[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int row = (8 * w + i) * 8 + (lane >> 3);
-                const int c = (lane & 7) ^ ((row >> 1) & 7);
-                dma16(rs, lds_region + (8 * w + i) * 1024, c * 16 < kbytes_left ? off[i] : OOB);
-            }
-        }
-    }
-};
-
-// DMA of one K step of a token-major activation tile for dW: 64 token rows x
-// 256 features (512 bytes).  Wave w, instruction i writes rows 2 (8w + i) and
-// 2 (8w + i) + 1; lane l fills physical chunk l % 32 of row (l / 32) with the
-// logical chunk (l % 32) ^ (4 (row % 4)), which puts the four token rows of a
-// transposing read in four different 64-byte quarters of a 256-byte window.
+// DMA of one chunk of a token-major operand: W_KC token rows x 256 features
+// (512 bytes).  Wave w, instruction i (< W_DR) writes rows 2 (W_DR w + i) and
+// + 1; lane l fills physical chunk l % 32 of row (l / 32) with the logical chunk
+// (l % 32) ^ (4 (row % 4)), which puts the four token rows of a transposing read
+// in four different 64-byte quarters of a 256-byte window.
 struct DmaTok {
-    uint32_t off[8];
-    __device__ __forceinline__ void init(int64_t ld_bytes, int cols_valid) {
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t off[W_DR];   // per instruction: byte offset of the lane's chunk, or OOB
+    int row[W_DR];
+    __device__ __forceinline__ void init(int64_t ld_bytes, int cols_valid, int wave) {
+        const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int row = 2 * (8 * w + i) + (lane >> 5);
-            const int c = (lane & 31) ^ (4 * (row & 3));
-            off[i] = c * 8 < cols_valid ? (uint32_t)(row * ld_bytes + c * 16) : OOB;
+        for (int i = 0; i < W_DR; i++) {
+            row[i] = 2 * (W_DR * wave + i) + (lane >> 5);
+            const int c = (lane & 31) ^ (4 * (row[i] & 3));
+            off[i] = c * 8 < cols_valid ? (uint32_t)(row[i] * ld_bytes + c * 16) : OOB;
         }
     }
-    // base: token row 0 of this step; rows_left: tokens in range from there
-    __device__ __forceinline__ void issue(const char *base, int rows_left, char *lds_region) const {
+    // base: token row 0 of this chunk; rows_left: tokens in range from there
+    __device__ __forceinline__ void issue(const char *base, int rows_left, char *lds_region, int wave) const {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-        if (rows_left >= 64) {
 #pragma unroll
-            for (int i = 0; i < 8; i++) dma16(rs, lds_region + (8 * w + i) * 1024, off[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int row = 2 * (8 * w + i) + (lane >> 5);
-                dma16(rs, lds_region + (8 * w + i) * 1024, row < rows_left ? off[i] : OOB);
-            }
-        }
+        for (int i = 0; i < W_DR; i++)
+            dma16(rs, lds_region + (W_DR * wave + i) * 1024, row[i] < rows_left ? off[i] : OOB);
     }
 };
 
-// Fragment reads of one K quarter (16 of the step's 64) into slot registers.
-// K-contiguous tiles: A rows padded (144 B), B rows swizzled (128 B).
-__device__ __forceinline__ void p_read_kc(const char *st, u32x4 (&a)[4], u32x4 (&b)[4], int arow, int brow,
-                                          int h, int kk) {
-    const int c = 2 * kk + h;
-#pragma unroll
-    for (int f = 0; f < 4; f++) a[f] = *(const u32x4 *)(st + (arow + 32 * f) * P_ROWB_A + c * 16);
-    const int pc = c ^ ((brow >> 1) & 7);
-#pragma unroll
-    for (int f = 0; f < 4; f++) b[f] = *(const u32x4 *)(st + P_A_BYTES + (brow + 32 * f) * 128 + pc * 16);
-}
-
-// Token-major tiles (dW): two transposing reads per fragment.  In a group of
-// 16 lanes, lane s = 4e + q reads 8 bytes at token row k0 + e, feature
-// col0 + 4q; output lane i then holds features col0 + i at tokens k0 .. k0 + 3.
+// Token-major tiles: two transposing reads per fragment.  In a group of 16
+// lanes, lane s = 4e + q reads 8 bytes at token row k0 + e, feature col0 + 4q;
+// output lane i then holds features col0 + i at tokens k0 .. k0 + 3.
 __device__ __forceinline__ u32x4 p_frag_tr(const char *tile, int krow0, int col) {
     // krow0: this lane's token row for read 0 (multiple of 4 plus e); col: its
     // 4-feature column start
@@ -815,15 +747,17 @@ __device__ __forceinline__ u32x4 p_frag_tr(const char *tile, int krow0, int col)
     return r;
 }
 
-__device__ __forceinline__ void p_read_tok(const char *st, u32x4 (&a)[4], u32x4 (&b)[4], int wm, int wn,
-                                           int lane, int kk) {
+// Fragments of K quarter kk (16 tokens) of a stage: X^T rows wm * 128 .. and
+// dY^T columns wn * 128 ..
+__device__ __forceinline__ void w_read_q(const char *st, u32x4 (&a)[4], u32x4 (&b)[4], int wm, int wn,
+                                         int lane, int kk) {
     const int g = (lane & 63) >> 4, s = lane & 15, e = s >> 2, q = s & 3;
     const int krow0 = 16 * kk + 8 * (g >> 1) + e;
     const int cofs = 16 * (g & 1) + 4 * q;
 #pragma unroll
     for (int f = 0; f < 4; f++) a[f] = p_frag_tr(st, krow0, wm * 128 + 32 * f + cofs);
 #pragma unroll
-    for (int f = 0; f < 4; f++) b[f] = p_frag_tr(st + P_T_BYTES, krow0, wn * 128 + 32 * f + cofs);
+    for (int f = 0; f < 4; f++) b[f] = p_frag_tr(st + W_OP, krow0, wn * 128 + 32 * f + cofs);
 }
 
 __device__ __forceinline__ void p_mma(f32x16 (&acc)[4][4], const u32x4 (&a)[4], const u32x4 (&b)[4]) {
@@ -835,239 +769,207 @@ __device__ __forceinline__ void p_mma(f32x16 (&acc)[4][4], const u32x4 (&a)[4], 
                 __builtin_bit_cast(bf16x8, a[i]), __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
 }
 
-template <int MODE>
+// Workgroup barrier after an explicit wait: vmcnt(N) (this wave's loads up to
+// all but its N latest are complete) and lgkmcnt(0).  Unlike __syncthreads it
+// does not wait for every outstanding load.
+template <int N>
+__device__ __forceinline__ void w_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_pipe_kernel(GemmArgs g) {
-    using G = Geo<256>;
-    constexpr int BK = 64, ES = 2;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+void gemm_dw_kernel(GemmArgs g) {
+    constexpr int ES = 2;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, h = lane >> 5;
-    const int arow = wm * 128 + l32, brow = wn * 128 + l32;
     const int total = g.tiles_m * g.tiles_n * g.splits;
+    const int64_t lda = (int64_t)g.in * ES, ldb = (int64_t)g.out * ES;   // bytes per token row
 
-    using SA = typename std::conditional<MODE == MODE_FWD, StageTernT<true, 256>, StageTernS<true, 256>>::type;
-    SA sa;             // forward / dX ternary operand (registers)
-    DmaRows db;        // forward / dX activation operand
-    DmaTok dta, dtb;   // dW operands
-
-    // per-tile geometry, set by begin_tile
-    int tm = 0, tn = 0, sp = 0, m0 = 0, n0 = 0, nk = 0;
-    int64_t kbeg = 0, klen = 0;
-    const char *act_a = nullptr, *act_b = nullptr;
-
-    auto begin_tile = [&](int j) -> bool {
-        if (!p_item(j, total, g.tiles_m, g.tiles_n, tm, tn, sp)) return false;
-        m0 = tm * 256;
-        n0 = tn * 256;
+    // chunks of item (tile, split) sp: its tokens, rounded up to an even count
+    auto item_chunks = [&](int sp, int64_t &kbeg, int64_t &klen) __attribute__((always_inline)) {
         kbeg = (int64_t)sp * g.kps;
-        const int64_t kend = min((int64_t)g.K, kbeg + g.kps);
-        klen = kend - kbeg;
-        nk = (int)((klen + BK - 1) / BK);
-        if constexpr (MODE == MODE_FWD) {
-            sa.init(g.packed + m0 / 16, g.wpr, (int)(g.wpr - m0 / 16));
-            act_b = (const char *)g.act0 + (int64_t)n0 * g.in * ES;
-            db.init((int64_t)g.in * ES, g.N - n0);
-        } else if constexpr (MODE == MODE_DX) {
-            sa.init(g.packed + (int64_t)m0 * g.wpr, g.wpr, g.M - m0, g.scale, g.out);
-            act_b = (const char *)g.act0 + (int64_t)n0 * g.out * ES;
-            db.init((int64_t)g.out * ES, g.N - n0);
-        } else {
-            act_a = (const char *)g.act0 + kbeg * g.in * ES + (int64_t)m0 * ES;
-            act_b = (const char *)g.act1 + kbeg * g.out * ES + (int64_t)n0 * ES;
-            dta.init((int64_t)g.in * ES, g.M - m0);
-            dtb.init((int64_t)g.out * ES, g.N - n0);
-        }
-        return true;
+        klen = min((int64_t)g.K, kbeg + g.kps) - kbeg;
+        const int n = (int)((klen + W_KC - 1) / W_KC);
+        return (n + 1) & ~1;
     };
 
-    // DMA of step `it` of the current tile into stage S (activation tiles)
-    auto dma_step = [&](auto s_c, int it) {
-        constexpr int S = decltype(s_c)::value;
-        char *st = p_stage<S>();
-        const int64_t k0 = (int64_t)it * BK;
-        if constexpr (MODE == MODE_FWD || MODE == MODE_DX) {
-            const int kb = (MODE == MODE_FWD ? g.in : g.out) * ES;
-            db.issue(act_b + k0 * ES, (int)max<int64_t>(-1, (int64_t)kb - k0 * ES), st + P_A_BYTES);
-        } else {
-            const int rows_left = (int)max<int64_t>(-1, min<int64_t>(64, klen - k0));
-            dta.issue(act_a + k0 * g.in * ES, rows_left, st);
-            dtb.issue(act_b + k0 * g.out * ES, rows_left, st + P_T_BYTES);
-        }
+    // ---- issue side: chunk ic of item ij; iv false once the items run out
+    // (every load then is out of range: zeros into LDS, no memory access)
+    int ij = 0, ic = 0, itm = 0, itn = 0, isp = 0, inch = 0;
+    int64_t ikbeg = 0, iklen = 0;
+    const char *ia = nullptr, *ib = nullptr;
+    DmaTok da, db;
+    bool iv = p_item(0, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+    auto set_itile = [&]() __attribute__((always_inline)) {
+        inch = item_chunks(isp, ikbeg, iklen);
+        ia = (const char *)g.act0 + ikbeg * lda + (int64_t)itm * 256 * ES;
+        ib = (const char *)g.act1 + ikbeg * ldb + (int64_t)itn * 256 * ES;
+        da.init(lda, g.M - itm * 256, wave);
+        db.init(ldb, g.N - itn * 256, wave);
     };
-    // register fetch of the ternary operand of step `it` into set S
-    auto fetch_a = [&](auto s_c, int it) {
-        constexpr int S = decltype(s_c)::value;
-        if constexpr (MODE == MODE_FWD) {
-            const int64_t k0 = (int64_t)it * BK;
-            sa.template fetch<S>(k0, (int)max<int64_t>(-1, min<int64_t>(BK, klen - k0)));
-        } else if constexpr (MODE == MODE_DX) {
-            sa.template fetch<S>(it * BK);
+    if (iv) set_itile();
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        char *st = w_lds + s * W_STAGE;
+        const int64_t k0 = (int64_t)ic * W_KC;
+        const int rows_left = iv ? (int)max<int64_t>(0, min<int64_t>(W_KC, iklen - k0)) : 0;
+        da.issue(ia + k0 * lda, rows_left, st, wave);
+        db.issue(ib + k0 * ldb, rows_left, st + W_OP, wave);
+        if (iv && ++ic == inch) {
+            ic = 0;
+            ++ij;
+            iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+            if (iv) set_itile();
         }
-    };
-    // write part p (of 4) of register set S into stage D
-    auto commit_a = [&](auto s_c, auto d_c, int p) {
-        constexpr int S = decltype(s_c)::value, D = decltype(d_c)::value;
-        if constexpr (MODE == MODE_FWD || MODE == MODE_DX) {
-            u32x4 *smA = (u32x4 *)p_stage<D>();
-#pragma unroll
-            for (int j = 0; j < SA::NOUT; j++)
-                if (j % 4 == p) sa.template commit<S>(j, smA);
-        }
-    };
-    auto read_q = [&](auto s_c, u32x4 (&a)[4], u32x4 (&b)[4], int kk) {
-        constexpr int S = decltype(s_c)::value;
-        if constexpr (MODE == MODE_DW) p_read_tok(p_stage<S>(), a, b, wm, wn, lane, kk);
-        else p_read_kc(p_stage<S>(), a, b, arow, brow, h, kk);
     };
 
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
+    // ---- compute side: item cj
+    int cj = 0, ctm = 0, ctn = 0, csp = 0;
+    int64_t ckbeg = 0, cklen = 0;
+    bool cv = p_item(0, total, g.tiles_m, g.tiles_n, ctm, ctn, csp);
+    int cnch = cv ? item_chunks(csp, ckbeg, cklen) : 0;
 
     f32x16 acc[4][4];
-    u32x4 fa[2][4], fb[2][4];
+    u32x4 f0a[2][4], f0b[2][4];   // K quarter 0 fragments of the current / next chunk
+    int sc = 0;                   // LDS stage of the current chunk
 
-    // one K step on stage CUR; stages and register sets alternate statically
-    auto body = [&](auto cur_c, int it) {
-        constexpr int CUR = decltype(cur_c)::value;
-        using ICUR = std::integral_constant<int, CUR>;
-        using INXT = std::integral_constant<int, 1 - CUR>;
-        dma_step(INXT{}, it + 1);
-        fetch_a(ICUR{}, it + 2);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
-            if (kk < 3) read_q(ICUR{}, fa[(kk + 1) & 1], fb[(kk + 1) & 1], kk + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            p_mma(acc, fa[kk & 1], fb[kk & 1]);
-            commit_a(INXT{}, INXT{}, kk);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        wait_vm0();
-        __syncthreads();
-        read_q(INXT{}, fa[0], fb[0], 0);
-    };
-
-    // prologue loads of the first tile
-    bool have = begin_tile(0);
-    if (have) {
-        dma_step(I0{}, 0);
-        fetch_a(I0{}, 0);
-        fetch_a(I1{}, 1);
-    }
-    for (int j = 0; have; j++) {
-#pragma unroll
-        for (int p = 0; p < 4; p++) commit_a(I0{}, I0{}, p);
-        wait_vm0();
-        __syncthreads();
+    auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int fm = 0; fm < 4; fm++)
 #pragma unroll
             for (int fn = 0; fn < 4; fn++)
 #pragma unroll
                 for (int i = 0; i < 16; i++) acc[fm][fn][i] = 0.0f;
-        read_q(I0{}, fa[0], fb[0], 0);
-        for (int it = 0; it < nk; it += 2) {
-            body(I0{}, it);
-            body(I1{}, it + 1);
-        }
-        // the last barrier has passed: both stages are free.  Keep this tile's
-        // coordinates for the epilogue and start the next tile's loads.
-        const int etm = tm, esp = sp, em0 = m0, en0 = n0;
-        have = begin_tile(j + 1);
-        if (have) {
-            dma_step(I0{}, 0);
-            fetch_a(I0{}, 0);
-            fetch_a(I1{}, 1);
-        }
+    };
 
-        // ---- epilogue of the finished tile.  acc[fm][fn][i] is C[m][n] with
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // one chunk (fragment slot SL): issue W_AHEAD chunks ahead; run K quarters
+    // 0 .. W_Q - 2, reading each next quarter's fragments during the current
+    // one's MFMAs; wait for the next chunk's loads in every wave (each wave's
+    // loads issued after them: its later chunk issues, 2 W_DR each), pass the
+    // barrier, read the next chunk's quarter 0 fragments, and run the last
+    // quarter's MFMAs (its fragments are already in registers).
+    auto chunk = [&](auto sl_c) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sl_c)::value, SL1 = SL ^ 1;
+        issue((sc + W_AHEAD) % W_NST);
+        const char *st = w_lds + sc * W_STAGE;
+        u32x4 qa[2][4], qb[2][4];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < W_Q - 1; q++) {
+            w_read_q(st, qa[(q + 1) & 1], qb[(q + 1) & 1], wm, wn, lane, q + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q == 0) p_mma(acc, f0a[SL], f0b[SL]);
+            else p_mma(acc, qa[q & 1], qb[q & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        w_barrier<(W_AHEAD - 1) * 2 * W_DR>();
+        sc = (sc + 1) % W_NST;
+        w_read_q(w_lds + sc * W_STAGE, f0a[SL1], f0b[SL1], wm, wn, lane, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        p_mma(acc, qa[(W_Q - 1) & 1], qb[(W_Q - 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // prologue: W_AHEAD chunks in flight; the first one's quarter 0 fragments
+#pragma unroll
+    for (int a = 0; a < W_AHEAD; a++) issue(a);
+    w_barrier<(W_AHEAD - 1) * 2 * W_DR>();
+    w_read_q(w_lds, f0a[0], f0b[0], wm, wn, lane, 0);
+    zero_acc();
+    while (cv) {
+        for (int c = 0; c < cnch; c += 2) {
+            chunk(I0{});
+            chunk(I1{});
+        }
+        // ---- epilogue of item (ctm, ctn, csp).  acc[fm][fn][i] is C[m][n] with
         //   m = m0 + wm*128 + fm*32 + 8*(i/4) + 4*h + i%4,  n = n0 + wn*128 + fn*32 + l32
-        const int mw = em0 + wm * 128, nw = en0 + wn * 128;
-        if constexpr (MODE == MODE_FWD || MODE == MODE_DX) {
-            const int ldo = (MODE == MODE_FWD) ? g.out : g.in;
+        const int mw = ctm * 256 + wm * 128, nw = ctn * 256 + wn * 128;
+        // buffer stores over this wave's 128 x 128 block: the lane offset holds
+        // its column and 4h rows, the scalar offset the row group.  M is a
+        // multiple of 8, so the 8-row test is wave-uniform.
+        float *dst = (float *)g.out_ptr + (g.splits > 1 ? (int64_t)csp * g.M * g.N : 0);
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(dst + (int64_t)mw * g.N + nw);
+        uint32_t vo[4];
 #pragma unroll
-            for (int fm = 0; fm < 4; fm++) {
+        for (int fn = 0; fn < 4; fn++)
+            vo[fn] = nw + fn * 32 + l32 < g.N ? (uint32_t)((4 * h * g.N + fn * 32 + l32) * 4) : OOB;
+        // One split: gq = G * scale[c] and the sgrad partial.  Several splits:
+        // the raw G partial (scale 1 makes the store exact), no sgrad partial.
+        const bool split = g.splits > 1;
+        // tern codes of this lane's 64 rows x 4 columns, from the forward
+        // fragment-ordered copy (its rows are the columns c, its K the rows r):
+        // per 32-row fragment fm, the 16 bytes of each 8-row half hf hold the
+        // lane's four columns.  Pre-shifted by 4h, row 8 (i / 4) + 4h + i % 4
+        // of the fragment sits at a bit offset fixed by i.
+        const int nchf = (g.M + 31) >> 5;
+        u32x4 tw[4][2];
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const int m = mw + fm * 32 + 8 * q + 4 * h;
-                    if (m >= g.M) continue;
-                    f32x4 sc = {1.0f, 1.0f, 1.0f, 1.0f};
-                    if constexpr (MODE == MODE_FWD) sc = *(const f32x4 *)(g.scale + m);
+        for (int fm = 0; fm < 4; fm++) {
+            const int sch = ctm * 8 + wm * 4 + fm;
 #pragma unroll
-                    for (int fn = 0; fn < 4; fn++) {
-                        const int n = nw + fn * 32 + l32;
-                        if (n >= g.N) continue;
-                        f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
-                                   acc[fm][fn][4 * q + 3]};
-                        if constexpr (MODE == MODE_FWD) v = v * sc;
-                        const int64_t o = (int64_t)n * ldo + m;
-                        if (MODE == MODE_FWD && g.y_bf16) {
-                            f32x2 a2 = {v.x, v.y}, b2 = {v.z, v.w};
-                            u32x2 pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(a2, bf16x2)),
-                                        __builtin_bit_cast(uint32_t, __builtin_convertvector(b2, bf16x2))};
-                            *(u32x2 *)((uint16_t *)g.out_ptr + o) = pk;
-                        } else {
-                            *(f32x4 *)((float *)g.out_ptr + o) = v;
-                        }
-                    }
-                }
+            for (int hf = 0; hf < 2; hf++) {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                tw[fm][hf] = (!split && sch < nchf)
+                                 ? *(const u32x4 *)(g.frag + ((int64_t)(ctn * nchf + sch) * 512 +
+                                                              (wn * 64 + hf * 32 + l32) * 4))
+                                 : z;
+                tw[fm][hf] >>= (uint32_t)(4 * h);
             }
-        } else {
-            float *dst = (float *)g.out_ptr;
-            if (g.splits > 1) {
-                dst += (int64_t)esp * g.M * g.N;
+        }
+        float scv[4], ps[4];
 #pragma unroll
-                for (int fm = 0; fm < 4; fm++)
+        for (int fn = 0; fn < 4; fn++) {
+            const int n = nw + fn * 32 + l32;
+            scv[fn] = split ? 1.0f : (n < g.N ? g.scale[n] : 0.0f);
+            ps[fn] = 0.0f;
+        }
 #pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int m = mw + fm * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                        if (m >= g.M) continue;
+        for (int fm = 0; fm < 4; fm++)
 #pragma unroll
-                        for (int fn = 0; fn < 4; fn++) {
-                            const int n = nw + fn * 32 + l32;
-                            if (n < g.N) dst[(int64_t)m * g.N + n] = acc[fm][fn][i];
-                        }
-                    }
-            } else {
-                float sc[4], ps[4];
+            for (int i = 0; i < 16; i++) {
+                const int rg = fm * 32 + 8 * (i >> 2);   // row group within the block
+                if (mw + rg >= g.M) continue;
+                const int so = (rg + (i & 3)) * g.N * 4;
+                // k = 16 kk + 8 hf + e within the fragment, e = 4h + i % 4
+                const int kk = i >> 3, hf = (i >> 2) & 1;
+                const int pos = ((i & 1) ? 16 : 0) + 8 * kk + 2 * ((i & 3) >> 1);
 #pragma unroll
                 for (int fn = 0; fn < 4; fn++) {
-                    const int n = nw + fn * 32 + l32;
-                    sc[fn] = n < g.N ? g.scale[n] : 0.0f;
-                    ps[fn] = 0.0f;
+                    const float gv = acc[fm][fn][i];
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gv * scv[fn]), ro, vo[fn], so,
+                                                          0);
+                    ps[fn] += gv * code_to_f32((tw[fm][hf][fn] >> pos) & 3u);
                 }
-#pragma unroll
-                for (int fm = 0; fm < 4; fm++)
-#pragma unroll
-                    for (int i = 0; i < 16; i++) {
-                        const int m = mw + fm * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-                        if (m >= g.M) continue;
-#pragma unroll
-                        for (int fn = 0; fn < 4; fn++) {
-                            const int n = nw + fn * 32 + l32;
-                            if (n >= g.N) continue;
-                            const float gv = acc[fm][fn][i];
-                            dst[(int64_t)m * g.N + n] = gv * sc[fn];
-                            const uint32_t word = g.packed[(int64_t)m * g.wpr + (n >> 4)];
-                            ps[fn] += gv * code_to_f32((word >> (2 * (n & 15))) & 3u);
-                        }
-                    }
-#pragma unroll
-                for (int fn = 0; fn < 4; fn++) ps[fn] += __shfl_xor(ps[fn], 32);
-                // cross-wave sum through a small LDS table of its own (the
-                // stages may already hold the next tile's data)
-                __shared__ float red[2 * 256];
-                if (h == 0) {
-#pragma unroll
-                    for (int fn = 0; fn < 4; fn++) red[wm * 256 + wn * 128 + fn * 32 + l32] = ps[fn];
-                }
-                __syncthreads();
-                if (tid < 256 && en0 + tid < g.N) g.part[(int64_t)etm * g.N + en0 + tid] = red[tid] + red[256 + tid];
-                __syncthreads();
             }
+        if (!split) {
+#pragma unroll
+            for (int fn = 0; fn < 4; fn++) ps[fn] += __shfl_xor(ps[fn], 32);
+            // cross-wave sum (the tile's two row halves) through a table of its own
+            if (h == 0) {
+#pragma unroll
+                for (int fn = 0; fn < 4; fn++) w_red[wm * 256 + wn * 128 + fn * 32 + l32] = ps[fn];
+            }
+            __syncthreads();
+            const int n0 = ctn * 256;
+            if (tid < 256 && n0 + tid < g.N) g.part[(int64_t)ctm * g.N + n0 + tid] = w_red[tid] + w_red[256 + tid];
+            __syncthreads();
         }
+        zero_acc();
+        ++cj;
+        cv = p_item(cj, total, g.tiles_m, g.tiles_n, ctm, ctn, csp);
+        if (cv) cnch = item_chunks(csp, ckbeg, cklen);
     }
+    // the last issues were out-of-range loads still writing zeros into the
+    // stages: drain them before the workgroup ends
+    wait_vm0();
 }
 
 // ---------------------------------------------------------------------------
@@ -1542,7 +1444,7 @@ hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
             const int64_t cus = device_cus();
             const dim3 pgrid((unsigned)(p.grid < cus ? p.grid : cus));
             if constexpr (MODE == MODE_DW)
-                hipLaunchKernelGGL((dev::gemm_pipe_kernel<MODE>), pgrid, block, 0, st, a);
+                hipLaunchKernelGGL(dev::gemm_dw_kernel, pgrid, block, 0, st, a);
             else
                 hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE>), pgrid, block, 0, st, a);
             return hipGetLastError();

@@ -27,7 +27,7 @@ COPY_KIB = (1 << 30) / 1024.0
 
 def entry_of(kernel: str) -> str | None:
     k = kernel
-    if "materialize_kernel" in k:
+    if "materialize_kernel" in k or "derive_kernel" in k:
         return "materialize"
     if "gemm" in k:
         if "<0>" in k or ", 0," in k:
