@@ -38,8 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large", choices=["rwkv_small", "mid", "large", "largest"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=192, help="oracle sample: token rows per projection")
-    ap.add_argument("--cpu-cols", type=int, default=48, help="oracle sample: output columns per projection")
+    ap.add_argument("--cpu-rows", type=int, default=3072, help="oracle sample: token rows per projection")
+    ap.add_argument("--cpu-cols", type=int, default=768, help="oracle sample: output columns per projection")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy a 1 GiB buffer 3 times (known bytes, for scaling "
                          "HBM traffic counters)")
@@ -141,7 +141,7 @@ def main():
     dom = max(("fwd", "bwd_dx", "bwd_dw"), key=lambda p: part_ms[p])
     dom_kernels = {"fwd": "gemm_rd_kernel<MODE_FWD> (tern_linear_fwd)",
                    "bwd_dx": "gemm_rd_kernel<MODE_DX> (tern_linear_bwd_dx)",
-                   "bwd_dw": "gemm_pipe_kernel<MODE_DW> + dw_reduce + sgrad_reduce (tern_linear_bwd_dw)"}[dom]
+                   "bwd_dw": "gemm_dw_kernel + dw_reduce + sgrad_reduce (tern_linear_bwd_dw)"}[dom]
     achieved = gemm_flops[dom] / (part_ms[dom] * 1e-3) / 1e12
     traffic = None
     if os.path.exists(TRAFFIC_FILE):

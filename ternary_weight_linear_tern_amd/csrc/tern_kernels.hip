@@ -984,33 +984,53 @@ void gemm_dw_kernel(GemmArgs g) {
 // odd) with p = 4 kk + e / 2: one shift and one mask leave the two codes of an
 // MFMA operand dword at bits 0-1 and 16-17.  Codes beyond the matrix are 00.
 // ---------------------------------------------------------------------------
+// One workgroup writes D_G chunks of one tile of a copy.  Both copies read a
+// block of the canonical words staged in LDS: for the dX operand, the tile's
+// 256 rows m = r x the chunks' 2 D_G words of columns k = c; for the forward
+// operand, the chunks' 32 D_G rows k = r x the tile's 16 words of columns m = c.
+constexpr int D_G = 2;   // chunks per workgroup
 template <bool DXOP>
 __global__ __launch_bounds__(256) void derive_kernel(const uint32_t *__restrict__ canon, int64_t in,
                                                      int64_t out, int64_t wpr, int64_t nch,
-                                                     uint32_t *__restrict__ frag, int64_t nwords) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= nwords) return;
-    const int64_t tc = i >> 9;
-    const int d = (int)(i & 511);
-    const int64_t tile = tc / nch, chunk = tc - tile * nch;
-    const int wm = d >> 8, lane = (d >> 2) & 63, fm = d & 3;
-    const int64_t m = tile * 256 + wm * 128 + fm * 32 + (lane & 31);
-    const int64_t M = DXOP ? in : out, K = DXOP ? out : in;
-    uint32_t word = 0;
-    if (m < M) {
+                                                     uint32_t *__restrict__ frag) {
+    // block rows x words (+1 word per row against bank conflicts)
+    constexpr int BR = DXOP ? 256 : 32 * D_G, BW = DXOP ? 2 * D_G : 16;
+    __shared__ uint32_t blk[BR][BW + 1];
+    const int t = threadIdx.x;
+    const int64_t tile = blockIdx.x, sg = blockIdx.y;
+    const int64_t r0 = DXOP ? tile * 256 : sg * (32 * D_G);   // first canonical row
+    const int64_t w0 = DXOP ? sg * (2 * D_G) : tile * 16;     // first canonical word column
 #pragma unroll
-        for (int kk = 0; kk < 2; kk++)
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const int64_t k = chunk * 32 + kk * 16 + (lane >> 5) * 8 + e;
-                if (k >= K) continue;
-                const int64_t r = DXOP ? m : k, c = DXOP ? k : m;
-                const uint32_t code = (canon[r * wpr + (c >> 4)] >> (2 * (c & 15))) & 3u;
-                const int p = 4 * kk + (e >> 1);
-                word |= code << ((e & 1) ? 16 + 2 * p : 2 * p);
-            }
+    for (int idx = t; idx < BR * BW; idx += 256) {
+        const int row = idx / BW, w = idx % BW;
+        const int64_t r = r0 + row, wc = w0 + w;
+        blk[row][w] = (r < in && wc < wpr) ? canon[r * wpr + wc] : 0u;
     }
-    frag[i] = word;
+    __syncthreads();
+    const int64_t M = DXOP ? in : out, K = DXOP ? out : in;
+#pragma unroll
+    for (int o = t; o < 512 * D_G; o += 256) {
+        const int sl = o >> 9, d = o & 511;            // chunk within the group, word within the chunk
+        const int64_t chunk = sg * D_G + sl;
+        if (chunk >= nch) continue;
+        const int wm = d >> 8, lane = (d >> 2) & 63, fm = d & 3;
+        const int ml = wm * 128 + fm * 32 + (lane & 31);  // row within the tile
+        uint32_t word = 0;
+        if (tile * 256 + ml < M) {
+#pragma unroll
+            for (int kk = 0; kk < 2; kk++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    const int kl = sl * 32 + kk * 16 + (lane >> 5) * 8 + e;   // k within the group
+                    if (sg * (32 * D_G) + kl >= K) continue;
+                    const int br = DXOP ? ml : kl, bc = DXOP ? kl : ml;    // block row, block column
+                    const uint32_t code = (blk[br][bc >> 4] >> (2 * (bc & 15))) & 3u;
+                    const int p = 4 * kk + (e >> 1);
+                    word |= code << ((e & 1) ? 16 + 2 * p : 2 * p);
+                }
+        }
+        frag[(tile * nch + chunk) * 512 + d] = word;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1488,10 +1508,12 @@ hipError_t launch_derive(uint32_t *packed, int64_t in, int64_t out, hipStream_t 
     const PackedLayout L = packed_layout(in, out);
     if (L.total == 0) return hipSuccess;
     const int64_t wpr = cdiv(out, 16);
-    hipLaunchKernelGGL((dev::derive_kernel<false>), dim3((unsigned)cdiv(L.fwd_words, 256)), dim3(256), 0, st,
-                       packed, in, out, wpr, cdiv(in, kFragChunk), packed + L.fwd_off, L.fwd_words);
-    hipLaunchKernelGGL((dev::derive_kernel<true>), dim3((unsigned)cdiv(L.dx_words, 256)), dim3(256), 0, st,
-                       packed, in, out, wpr, cdiv(out, kFragChunk), packed + L.dx_off, L.dx_words);
+    // forward operand: tiles over out, chunks over in; dX operand: the reverse
+    const int64_t nchf = cdiv(in, kFragChunk), nchd = cdiv(out, kFragChunk);
+    hipLaunchKernelGGL((dev::derive_kernel<false>), dim3((unsigned)cdiv(out, 256), (unsigned)cdiv(nchf, dev::D_G)),
+                       dim3(256), 0, st, packed, in, out, wpr, nchf, packed + L.fwd_off);
+    hipLaunchKernelGGL((dev::derive_kernel<true>), dim3((unsigned)cdiv(in, 256), (unsigned)cdiv(nchd, dev::D_G)),
+                       dim3(256), 0, st, packed, in, out, wpr, nchd, packed + L.dx_off);
     return hipGetLastError();
 }
 
