@@ -29,6 +29,8 @@ def entry_of(kernel: str) -> str | None:
     k = kernel
     if "materialize_kernel" in k or "derive_kernel" in k:
         return "materialize"
+    if "gemm_dw_kernel" in k:
+        return "bwd_dw"
     if "gemm" in k:
         if "<0>" in k or ", 0," in k:
             return "fwd"
