@@ -1235,19 +1235,25 @@ void gemm_rd_kernel(GemmArgs g) {
             constexpr bool OBF = decltype(obf_c)::value;
 #pragma unroll
             for (int fm = 0; fm < 4; fm++) {
+                // the four q pieces of each 128-byte row segment go out back to back
+                f32x4 scq[4];
+                bool mokq[4];
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
                     const int ml = fm * 32 + 8 * q;
-                    f32x4 sc = {1.0f, 1.0f, 1.0f, 1.0f};
-                    if constexpr (MODE == MODE_FWD) sc = *(const f32x4 *)(esc + ml);
-                    const bool mok = mw + ml < g.M;
-                    const int so = ml * esz;
+                    scq[q] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+                    if constexpr (MODE == MODE_FWD) scq[q] = *(const f32x4 *)(esc + ml);
+                    mokq[q] = mw + ml < g.M;
+                }
 #pragma unroll
-                    for (int fn = 0; fn < 4; fn++) {
+                for (int fn = 0; fn < 4; fn++) {
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const int so = (fm * 32 + 8 * q) * esz;
                         f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
                                    acc[fm][fn][4 * q + 3]};
-                        if constexpr (MODE == MODE_FWD) v = v * sc;
-                        const uint32_t off = mok ? vo[fn] : OOB;
+                        if constexpr (MODE == MODE_FWD) v = v * scq[q];
+                        const uint32_t off = mokq[q] ? vo[fn] : OOB;
                         if constexpr (OBF) {
                             const f32x2 a2 = {v.x, v.y}, b2 = {v.z, v.w};
                             const u32x2 pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(a2, bf16x2)),
@@ -1260,6 +1266,7 @@ void gemm_rd_kernel(GemmArgs g) {
                 }
             }
         };
+
         if (obf) rows(std::true_type{});
         else rows(std::false_type{});
     };
