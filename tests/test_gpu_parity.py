@@ -224,6 +224,48 @@ def test_parity_largest_sampled(o, proj):
     sampled_case(o, "largest", proj)
 
 
+def _frag_copy(tern, M_is_in):
+    """The fragment-ordered copy of include/tern.h, built from a tern matrix
+    [in, out] of {-1, 0, 1}: operand A[m][k] = tern[k][m] (forward copy,
+    M_is_in False) or tern[m][k] (dX copy).  Word (tile, chunk, wm, lane, fm)
+    holds the codes of row m = 256 tile + 128 wm + 32 fm + lane % 32 at
+    k = 32 chunk + 16 kk + 8 (lane // 32) + e at bit 2p (e even) or 16 + 2p
+    (e odd), p = 4 kk + e // 2; code 01 = +1, 11 = -1, 00 = 0."""
+    A = tern if M_is_in else tern.T
+    M, K = A.shape
+    tiles, nch = -(-M // 256), -(-K // 32)
+    Ap = np.zeros((tiles * 256, nch * 32), np.int64)
+    Ap[:M, :K] = A
+    code = np.where(Ap > 0, 1, np.where(Ap < 0, 3, 0)).astype(np.uint64)
+    c = code.reshape(tiles, 2, 4, 32, nch, 2, 2, 8)        # tile, wm, fm, l32, chunk, kk, h, e
+    c = c.transpose(0, 4, 1, 6, 3, 2, 5, 7)                # tile, chunk, wm, h, l32, fm, kk, e
+    kk = np.arange(2)[:, None]
+    e = np.arange(8)[None, :]
+    pos = np.where(e % 2 == 1, 16, 0) + 2 * (4 * kk + e // 2)
+    word = (c << pos.astype(np.uint64)).sum(axis=(-2, -1))  # codes occupy disjoint bits
+    return word.reshape(-1).astype(np.uint32)
+
+
+@pytest.mark.parametrize("n_in,n_out", [(8, 8), (136, 264), (520, 776), (264, 1032)])
+def test_fragment_copies(o, n_in, n_out):
+    """The handle's two fragment-ordered copies hold exactly the codes of the
+    canonical matrix, in the documented order (edges padded with 00)."""
+    log(f"fragment copies in={n_in} out={n_out}")
+    q = synth.int8_uniform(synth.stream_seed(6, n_in, n_out, 0), (n_in, n_out), -7, 7)
+    pk = tl.empty_packed(n_in, n_out)
+    tl.tern_materialize(to_dev(q), 2, pk)
+    torch.cuda.synchronize()
+    got = pk.cpu().numpy().view(np.uint32)
+    t = o.tern(q, 2)
+    canon = n_in * (-(-n_out // 16))
+    fwd_off = -(-canon // 64) * 64
+    fwd = _frag_copy(t, False)
+    dxc = _frag_copy(t, True)
+    assert got.size == fwd_off + fwd.size + dxc.size
+    assert np.array_equal(got[fwd_off:fwd_off + fwd.size], fwd), "forward copy differs"
+    assert np.array_equal(got[fwd_off + fwd.size:], dxc), "dX copy differs"
+
+
 # ---------------------------------------------------------------------------
 # properties
 # ---------------------------------------------------------------------------
