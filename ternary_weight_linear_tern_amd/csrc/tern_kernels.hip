@@ -54,6 +54,10 @@ constexpr uint32_t OOB = 0x80000000u;  // buffer offset that is always out of ra
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, 0x7FFFFFFF, 0x00020000);
 }
+// The same with a record count of n bytes (offsets >= n read as zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void *p, uint32_t n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)n, 0x00020000);
+}
 __device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
@@ -1061,6 +1065,13 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void *lds_wave_b
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)lds_wave_base, 4, voff, 0, 0, 0);
 }
 
+// 16 bytes per lane to LDS at lds + IMM + 16 lane from voff + soff + IMM; the
+// immediate moves both addresses and is covered by the range check.
+template <int IMM>
+__device__ __forceinline__ void dma16_imm(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)lds, 16, voff, soff, IMM, 0);
+}
+
 // Wait until at most N vector memory operations of this wave are outstanding
 // (and fence the compiler on both sides).
 template <int N>
@@ -1110,60 +1121,87 @@ void gemm_rd_kernel(GemmArgs g) {
     // slot of this lane's 16 bytes in every DMA row group, and its logical chunk
     const int cb = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
 
-    // ---- issue side: chunk ic of tile ij (coordinates itm, itn); iv false once
-    // the tiles are exhausted (then every load is out of range: no memory
-    // access, zeros into LDS, the same instruction count)
+    // ---- issue side: chunk ic of tile ij (coordinates itm, itn).  Each tile
+    // gets three buffer resources whose record counts end at the operand's
+    // last byte: this wave's activation rows (to the end of the tensor), its
+    // fragment words of the tile, and (dX) the scales.  A chunk only moves the
+    // scalar offsets.  The range check covers vector + scalar + immediate
+    // offsets per lane, so every byte past an edge reads as zero: the ragged
+    // K end of the tensor's last row, the even-padding chunk of the fragment
+    // words, and (record counts 0) every issue after the last tile.  Inside
+    // the tensor, bytes past K belong to the next row; they meet zero ternary
+    // codes and add nothing for finite inputs.  Four activation loads share
+    // one M0: the immediate offset 1024 i moves the LDS destination and the
+    // global address alike, and the lane offsets are stored less 1024 i
+    // (which needs K >= 32: 16 rows of 2 K bytes span 1024 bytes).
     int ij = 0, ic = 0, itm = 0, itn = 0, isp = 0;
     bool iv = p_item(0, total, g.tiles_m, g.tiles_n, itm, itn, isp);
-    const char *ib = nullptr;   // this wave's first activation row of tile ij
-    uint32_t boff[8];           // per DMA instruction: row * ld + cb, or OOB
+    const char *pa = nullptr;   // activation rows of tile ij (this wave's first row)
+    const uint32_t *pf = nullptr;   // this wave's fragment words of tile ij
+    uint32_t na = 0, nf = 0, ns = 0;   // record counts of the three resources
+    uint32_t boff[8];   // activation load i: lane's row * ld + 16-byte column - 1024 (i % 4), or OOB
+    const uint32_t soff_lane = lane < 32 ? (uint32_t)lane * 4u : OOB;   // dX scales: 32 per chunk
     auto set_itile = [&]() __attribute__((always_inline)) {
         const int n0 = itn * 256 + wn * 128;
-        ib = (const char *)g.act0 + (int64_t)n0 * ld;
+        // bytes from this wave's first row to the end of the tensor (integer
+        // arithmetic only: the int64 min / max overloads go through f64)
+        int64_t rem = (int64_t)(g.N - n0) * ld;
+        rem = (!iv || rem < 0) ? 0 : (rem > 0x7FFFFFF0 ? 0x7FFFFFF0 : rem);
+        pa = (const char *)g.act0 + (int64_t)n0 * ld;
+        na = __builtin_amdgcn_readfirstlane((uint32_t)rem);
+        pf = g.frag + ((int64_t)itm * nch * 512 + wm * 256);
+        nf = __builtin_amdgcn_readfirstlane(iv ? (uint32_t)(nch * 2048 - 1024) : 0u);
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int row = 16 * i + (lane >> 2);
-            boff[i] = n0 + row < g.N ? (uint32_t)(row * ld) + (uint32_t)cb : OOB;
+            boff[i] = (n0 + row < g.N ? (uint32_t)(row * ld) + (uint32_t)cb : OOB) - 1024u * (uint32_t)(i & 3);
+        }
+        if constexpr (MODE == MODE_DX) {
+            ns = __builtin_amdgcn_readfirstlane(iv ? (uint32_t)g.K * 4u : 0u);
+        } else if (iv) {
+            // this wave's 128 scales of the tile, for its epilogue
+            const int mb = itm * 256 + wm * 128;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scale + mb);
+            char *esc = wl + R_NST * R_STAGE + (ij & 3) * 512;
+#pragma unroll
+            for (int q = 0; q < 2; q++)
+                dma4(rs, esc + q * 256, mb + 64 * q + lane < g.M ? (uint32_t)(64 * q + lane) * 4u : OOB);
         }
     };
-    if (iv) set_itile();
+    set_itile();
 
     auto issue = [&](int s) __attribute__((always_inline)) {
         char *st = wl + s * R_STAGE;
-        const int64_t k0 = (int64_t)ic * R_KC;
-        const bool kin = iv && k0 * ES + cb < ld;
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(ib + k0 * ES);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(pa, na), rf = make_rsrc_n(pf, nf);
+        const int so = ic * R_KC * ES;
 #pragma unroll
-        for (int i = 0; i < 8; i++) dma16(rb, st + i * 1024, kin ? boff[i] : OOB);
-        // chunks past the copy's last one (the count is padded to even) read zeros
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.frag + ((int64_t)itm * nch + ic) * 512 + wm * 256);
-        dma16(ra, st + R_B, (iv && ic < nch) ? (uint32_t)lane * 16u : OOB);
-        if constexpr (MODE == MODE_DX) {
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scale + k0);
-            dma4(rs, st + R_B + R_A, (iv && lane < 32 && k0 + lane < g.K) ? (uint32_t)lane * 4u : OOB);
-        } else {
-            if (iv && ic == 0) {
-                // this wave's 128 scales of the tile, for its epilogue
-                const int mb = itm * 256 + wm * 128;
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scale + mb);
-                char *esc = wl + R_NST * R_STAGE + (ij & 3) * 512;
-#pragma unroll
-                for (int q = 0; q < 2; q++)
-                    dma4(rs, esc + q * 256, mb + 64 * q + lane < g.M ? (uint32_t)(64 * q + lane) * 4u : OOB);
-            }
+        for (int h4 = 0; h4 < 2; h4++) {
+            char *d = st + h4 * 4096;
+            dma16_imm<0>(ra, d, boff[4 * h4 + 0], so);
+            dma16_imm<1024>(ra, d, boff[4 * h4 + 1], so);
+            dma16_imm<2048>(ra, d, boff[4 * h4 + 2], so);
+            dma16_imm<3072>(ra, d, boff[4 * h4 + 3], so);
         }
-        if (iv && ++ic == nch2) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rf, (LDS_AS void *)(st + R_B), 16, (uint32_t)lane * 16u, ic * 2048,
+                                                 0, 0);
+        if constexpr (MODE == MODE_DX)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(g.scale, ns), (LDS_AS void *)(st + R_B + R_A), 4,
+                                                     soff_lane,
+                                                     ic * R_KC * 4, 0, 0);
+        if (++ic == nch2) {
             ic = 0;
-            ++ij;
-            iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
-            if (iv) set_itile();
+            if (iv) {
+                ++ij;
+                iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+                set_itile();
+            }
         }
     };
 
     // ---- compute side: tile cj
     int cj = 0, ctm = 0, ctn = 0, csp = 0;
     bool cv = p_item(0, total, g.tiles_m, g.tiles_n, ctm, ctn, csp);
-    int hist = 0;   // bit 0: the previous chunk ended a tile; bit 1: the one before
+    int hist = 0;   // bit 0: this chunk is one of a tile's first two after an epilogue
 
     f32x16 acc[4][4];
     u32x4 fa[2];        // fragment words (one dword per fm) of the current / next chunk
@@ -1289,9 +1327,10 @@ void gemm_rd_kernel(GemmArgs g) {
         for (int f = 0; f < 8; f++) {
             if (f == 4) {
                 // loads issued after the next chunk's: the two later chunk
-                // issues, plus 64 epilogue stores if a tile ended since
-                if (hist) wait_vm<63>();
-                else wait_vm<2 * OPS>();
+                // issues, plus 64 epilogue stores in a tile's first two
+                // chunks (where 63 waits for more than needed)
+                wait_vm<63>();
+                if (!hist) wait_vm<2 * OPS>();
                 read_ahead((sc + 1) & 3, std::integral_constant<int, SL1>{});
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1310,7 +1349,7 @@ void gemm_rd_kernel(GemmArgs g) {
         }
         __builtin_amdgcn_sched_barrier(0);
         sc = (sc + 1) & 3;
-        hist = (hist << 1) & 3;
+        hist >>= 1;
     };
 
     // prologue: three chunks in flight, then the first one's fragments
@@ -1333,7 +1372,7 @@ void gemm_rd_kernel(GemmArgs g) {
         zero_acc();
         ++cj;
         cv = p_item(cj, total, g.tiles_m, g.tiles_n, ctm, ctn, csp);
-        hist |= 1;
+        hist = 3;
     }
     // the last issues were out-of-range loads still writing zeros into this
     // wave's stages: drain them (and the stores) before the workgroup ends
@@ -1466,7 +1505,8 @@ template <bool BF, int MODE>
 hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)p.grid), block(dev::NT);
     if constexpr (BF) {
-        if (p.tile == TILE_256) {
+        // the forward / dX kernel's shared-M0 loads need K >= 32
+        if (p.tile == TILE_256 && (MODE == MODE_DW || a.K >= 32)) {
             // persistent: at most one workgroup per compute unit
             const int64_t cus = device_cus();
             const dim3 pgrid((unsigned)(p.grid < cus ? p.grid : cus));
