@@ -654,11 +654,12 @@ void gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // dW GEMM (bf16, 256 x 256 tiles, persistent, split-K): G[r][c] = sum over
 // tokens t of X[t][r] dY[t][c].  Both operands are token-major.  They stream
-// into a four-stage LDS ring in chunks of 32 tokens with direct-to-LDS buffer
-// loads issued three chunks ahead (across tile and split boundaries), and the
-// MFMA fragments come from ds_read_b64_tr_b16 transposing reads.  One barrier
-// per chunk; the MFMAs of a chunk's second K quarter run after the barrier,
-// while the next chunk's first fragments load.
+// into two LDS stages in chunks of 64 tokens with direct-to-LDS buffer loads
+// (across tile and split boundaries), and the MFMA fragments come from
+// ds_read_b64_tr_b16 transposing reads.  One barrier per chunk, before the
+// chunk's last K quarter: past it no wave reads the chunk's stage any more, so
+// the loads of the chunk after the next one go out right there, and the last
+// quarter's MFMAs run while the next chunk's first fragments load.
 // Epilogue, one split: gq = G * scale[c], and the tile's per-column sum of
 // G * tern over its 256 rows (fixed order) into the partial table; several
 // splits: the split's raw G, summed by dw_reduce_kernel.
@@ -669,7 +670,6 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int W_KC = 64;                 // tokens per chunk
 constexpr int W_NST = 2;                 // LDS stages
-constexpr int W_AHEAD = W_NST - 1;       // chunks issued ahead of the one computed
 constexpr int W_Q = W_KC / 16;           // MFMA K quarters per chunk
 constexpr int W_DR = W_KC / 8;           // DMA instructions per wave per operand and chunk
 constexpr int W_OP = W_KC * 512;         // one operand of a stage: W_KC tokens x 256 features
@@ -679,6 +679,13 @@ __shared__ float w_red[2 * 256];         // cross-wave sgrad partials of a tile
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void *lds_wave_base, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
+// 16 bytes per lane to LDS at lds + IMM + 16 lane from voff + soff + IMM; the
+// immediate moves both addresses and is covered by the range check.
+template <int IMM>
+__device__ __forceinline__ void dma16_imm(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)lds, 16, voff, soff, IMM, 0);
 }
 
 __device__ __forceinline__ void wait_vm0() {
@@ -710,25 +717,35 @@ __device__ __forceinline__ bool p_item(int j, int total, int tiles_m, int tiles_
 // (512 bytes).  Wave w, instruction i (< W_DR) writes rows 2 (W_DR w + i) and
 // + 1; lane l fills physical chunk l % 32 of row (l / 32) with the logical chunk
 // (l % 32) ^ (4 (row % 4)), which puts the four token rows of a transposing read
-// in four different 64-byte quarters of a 256-byte window.
+// in four different 64-byte quarters of a 256-byte window.  Four instructions
+// share one M0: the immediate offset 1024 (i % 4) moves the LDS destination and
+// the global address alike, so the lane offsets are stored less 1024 (i % 4)
+// (which needs 2 rows of a token-major operand to span 1024 bytes: M, N >= 256).
+// The resource's record count ends at the item's last token row, so rows past
+// it (ragged or padding chunks, or no item at all) read as zero.
 struct DmaTok {
-    uint32_t off[W_DR];   // per instruction: byte offset of the lane's chunk, or OOB
-    int row[W_DR];
+    uint32_t off[W_DR];   // per instruction: lane offset less 1024 (i % 4), or OOB less that
     __device__ __forceinline__ void init(int64_t ld_bytes, int cols_valid, int wave) {
         const int lane = threadIdx.x & 63;
 #pragma unroll
         for (int i = 0; i < W_DR; i++) {
-            row[i] = 2 * (W_DR * wave + i) + (lane >> 5);
-            const int c = (lane & 31) ^ (4 * (row[i] & 3));
-            off[i] = c * 8 < cols_valid ? (uint32_t)(row[i] * ld_bytes + c * 16) : OOB;
+            const int row = 2 * (W_DR * wave + i) + (lane >> 5);
+            const int c = (lane & 31) ^ (4 * (row & 3));
+            off[i] = (c * 8 < cols_valid ? (uint32_t)(row * ld_bytes + c * 16) : OOB) - 1024u * (uint32_t)(i & 3);
         }
     }
-    // base: token row 0 of this chunk; rows_left: tokens in range from there
-    __device__ __forceinline__ void issue(const char *base, int rows_left, char *lds_region, int wave) const {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+    // base: token row 0 of this chunk; nrec: bytes from there to the end of
+    // the item's rows (0: nothing in range)
+    __device__ __forceinline__ void issue(const char *base, uint32_t nrec, char *lds_region, int wave) const {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(base, nrec);
 #pragma unroll
-        for (int i = 0; i < W_DR; i++)
-            dma16(rs, lds_region + (W_DR * wave + i) * 1024, row[i] < rows_left ? off[i] : OOB);
+        for (int i4 = 0; i4 < W_DR; i4 += 4) {
+            char *d = lds_region + (W_DR * wave + i4) * 1024;
+            dma16_imm<0>(rs, d, off[i4 + 0], 0);
+            dma16_imm<1024>(rs, d, off[i4 + 1], 0);
+            dma16_imm<2048>(rs, d, off[i4 + 2], 0);
+            dma16_imm<3072>(rs, d, off[i4 + 3], 0);
+        }
     }
 };
 
@@ -804,31 +821,41 @@ void gemm_dw_kernel(GemmArgs g) {
     };
 
     // ---- issue side: chunk ic of item ij; iv false once the items run out
-    // (every load then is out of range: zeros into LDS, no memory access)
+    // (every record count is then 0: zeros into LDS, no memory access)
     int ij = 0, ic = 0, itm = 0, itn = 0, isp = 0, inch = 0;
-    int64_t ikbeg = 0, iklen = 0;
-    const char *ia = nullptr, *ib = nullptr;
+    const char *ia = nullptr, *ib = nullptr;   // token row of chunk ic in each operand
+    int64_t irem = 0;                          // token rows of the item from chunk ic on
     DmaTok da, db;
     bool iv = p_item(0, total, g.tiles_m, g.tiles_n, itm, itn, isp);
     auto set_itile = [&]() __attribute__((always_inline)) {
+        int64_t ikbeg = 0, iklen = 0;
         inch = item_chunks(isp, ikbeg, iklen);
+        irem = iv ? iklen : 0;
         ia = (const char *)g.act0 + ikbeg * lda + (int64_t)itm * 256 * ES;
         ib = (const char *)g.act1 + ikbeg * ldb + (int64_t)itn * 256 * ES;
         da.init(lda, g.M - itm * 256, wave);
         db.init(ldb, g.N - itn * 256, wave);
     };
-    if (iv) set_itile();
+    set_itile();
+    // record count of rows bytes (rows of ld bytes), saturated to the 31-bit range
+    auto nrec = [&](int64_t rows, int64_t ld) __attribute__((always_inline)) {
+        const int64_t b = rows * ld;
+        return __builtin_amdgcn_readfirstlane((uint32_t)(b <= 0 ? 0 : (b > 0x7FFFFFF0 ? 0x7FFFFFF0 : b)));
+    };
     auto issue = [&](int s) __attribute__((always_inline)) {
         char *st = w_lds + s * W_STAGE;
-        const int64_t k0 = (int64_t)ic * W_KC;
-        const int rows_left = iv ? (int)max<int64_t>(0, min<int64_t>(W_KC, iklen - k0)) : 0;
-        da.issue(ia + k0 * lda, rows_left, st, wave);
-        db.issue(ib + k0 * ldb, rows_left, st + W_OP, wave);
-        if (iv && ++ic == inch) {
+        da.issue(ia, nrec(irem, lda), st, wave);
+        db.issue(ib, nrec(irem, ldb), st + W_OP, wave);
+        ia += W_KC * lda;
+        ib += W_KC * ldb;
+        irem -= W_KC;
+        if (++ic == inch) {
             ic = 0;
-            ++ij;
-            iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
-            if (iv) set_itile();
+            if (iv) {
+                ++ij;
+                iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+                set_itile();
+            }
         }
     };
 
@@ -854,15 +881,14 @@ void gemm_dw_kernel(GemmArgs g) {
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
-    // one chunk (fragment slot SL): issue W_AHEAD chunks ahead; run K quarters
-    // 0 .. W_Q - 2, reading each next quarter's fragments during the current
-    // one's MFMAs; wait for the next chunk's loads in every wave (each wave's
-    // loads issued after them: its later chunk issues, 2 W_DR each), pass the
-    // barrier, read the next chunk's quarter 0 fragments, and run the last
-    // quarter's MFMAs (its fragments are already in registers).
+    // one chunk (fragment slot SL): run K quarters 0 .. W_Q - 2, reading each
+    // next quarter's fragments during the current one's MFMAs; wait for the
+    // next chunk's loads in every wave (nothing was issued after them), pass
+    // the barrier, refill this chunk's stage, read the next chunk's quarter 0
+    // fragments, and run the last quarter's MFMAs (its fragments are already
+    // in registers).
     auto chunk = [&](auto sl_c) __attribute__((always_inline)) {
         constexpr int SL = decltype(sl_c)::value, SL1 = SL ^ 1;
-        issue((sc + W_AHEAD) % W_NST);
         const char *st = w_lds + sc * W_STAGE;
         u32x4 qa[2][4], qb[2][4];
         __builtin_amdgcn_sched_barrier(0);
@@ -874,7 +900,10 @@ void gemm_dw_kernel(GemmArgs g) {
             else p_mma(acc, qa[q & 1], qb[q & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        w_barrier<(W_AHEAD - 1) * 2 * W_DR>();
+        w_barrier<0>();
+        // every wave has read all of this chunk's stage: refill it with the
+        // chunk after the next one
+        issue(sc);
         sc = (sc + 1) % W_NST;
         w_read_q(w_lds + sc * W_STAGE, f0a[SL1], f0b[SL1], wm, wn, lane, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -882,10 +911,10 @@ void gemm_dw_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: W_AHEAD chunks in flight; the first one's quarter 0 fragments
-#pragma unroll
-    for (int a = 0; a < W_AHEAD; a++) issue(a);
-    w_barrier<(W_AHEAD - 1) * 2 * W_DR>();
+    // prologue: two chunks in flight; the first one's quarter 0 fragments
+    issue(0);
+    issue(1);
+    w_barrier<2 * W_DR>();
     w_read_q(w_lds, f0a[0], f0b[0], wm, wn, lane, 0);
     zero_acc();
     while (cv) {
@@ -1063,13 +1092,6 @@ __shared__ __attribute__((aligned(16))) char r_lds[4 * R_WAVE];
 
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void *lds_wave_base, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)lds_wave_base, 4, voff, 0, 0, 0);
-}
-
-// 16 bytes per lane to LDS at lds + IMM + 16 lane from voff + soff + IMM; the
-// immediate moves both addresses and is covered by the range check.
-template <int IMM>
-__device__ __forceinline__ void dma16_imm(__amdgpu_buffer_rsrc_t rs, void *lds, uint32_t voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)lds, 16, voff, soff, IMM, 0);
 }
 
 // Wait until at most N vector memory operations of this wave are outstanding
@@ -1505,8 +1527,8 @@ template <bool BF, int MODE>
 hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)p.grid), block(dev::NT);
     if constexpr (BF) {
-        // the forward / dX kernel's shared-M0 loads need K >= 32
-        if (p.tile == TILE_256 && (MODE == MODE_DW || a.K >= 32)) {
+        // the shared-M0 loads need K >= 32 (forward / dX) and M, N >= 256 (dW)
+        if (p.tile == TILE_256 && (MODE == MODE_DW ? a.M >= 256 && a.N >= 256 : a.K >= 32)) {
             // persistent: at most one workgroup per compute unit
             const int64_t cus = device_cus();
             const dim3 pgrid((unsigned)(p.grid < cus ? p.grid : cus));
