@@ -734,18 +734,11 @@ struct DmaTok {
             off[i] = (c * 8 < cols_valid ? (uint32_t)(row * ld_bytes + c * 16) : OOB) - 1024u * (uint32_t)(i & 3);
         }
     }
-    // base: token row 0 of this chunk; nrec: bytes from there to the end of
-    // the item's rows (0: nothing in range)
-    __device__ __forceinline__ void issue(const char *base, uint32_t nrec, char *lds_region, int wave) const {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(base, nrec);
-#pragma unroll
-        for (int i4 = 0; i4 < W_DR; i4 += 4) {
-            char *d = lds_region + (W_DR * wave + i4) * 1024;
-            dma16_imm<0>(rs, d, off[i4 + 0], 0);
-            dma16_imm<1024>(rs, d, off[i4 + 1], 0);
-            dma16_imm<2048>(rs, d, off[i4 + 2], 0);
-            dma16_imm<3072>(rs, d, off[i4 + 3], 0);
-        }
+    // load I of this wave; rs: resource from token row 0 of the chunk whose
+    // record count ends at the item's last row (0: nothing in range)
+    template <int I>
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, char *lds_region, int wave) const {
+        dma16_imm<(I & 3) * 1024>(rs, lds_region + (W_DR * wave + (I & ~3)) * 1024, off[I], 0);
     }
 };
 
@@ -842,23 +835,6 @@ void gemm_dw_kernel(GemmArgs g) {
         const int64_t b = rows * ld;
         return __builtin_amdgcn_readfirstlane((uint32_t)(b <= 0 ? 0 : (b > 0x7FFFFFF0 ? 0x7FFFFFF0 : b)));
     };
-    auto issue = [&](int s) __attribute__((always_inline)) {
-        char *st = w_lds + s * W_STAGE;
-        da.issue(ia, nrec(irem, lda), st, wave);
-        db.issue(ib, nrec(irem, ldb), st + W_OP, wave);
-        ia += W_KC * lda;
-        ib += W_KC * ldb;
-        irem -= W_KC;
-        if (++ic == inch) {
-            ic = 0;
-            if (iv) {
-                ++ij;
-                iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
-                set_itile();
-            }
-        }
-    };
-
     // ---- compute side: item cj
     int cj = 0, ctm = 0, ctn = 0, csp = 0;
     int64_t ckbeg = 0, cklen = 0;
@@ -876,6 +852,52 @@ void gemm_dw_kernel(GemmArgs g) {
             for (int fn = 0; fn < 4; fn++)
 #pragma unroll
                 for (int i = 0; i < 16; i++) acc[fm][fn][i] = 0.0f;
+    };
+
+    // The refill of a stage is issued in two parts, each spread over 16 MFMAs
+    // (one load per two): part 0 (operand X) during the last K quarter of the
+    // chunk that freed the stage, part 1 (operand dY, then the step to the
+    // next chunk) during the first quarter of the next chunk.  p_mma_dma runs
+    // the 16 MFMAs of a quarter with the loads of one part between them.
+    auto p_mma_dma = [&](const u32x4 (&a)[4], const u32x4 (&b)[4], int s, auto part_c)
+                         __attribute__((always_inline)) {
+        constexpr int PART = decltype(part_c)::value;
+        char *reg = w_lds + s * W_STAGE + PART * W_OP;
+        const __amdgpu_buffer_rsrc_t rs =
+            PART == 0 ? make_rsrc_n(ia, nrec(irem, lda)) : make_rsrc_n(ib, nrec(irem, ldb));
+        const DmaTok &d = PART == 0 ? da : db;
+        auto two = [&](auto k_c) __attribute__((always_inline)) {
+            constexpr int K = decltype(k_c)::value;
+            constexpr int i0 = (2 * K) >> 2, j0 = (2 * K) & 3, i1 = (2 * K + 1) >> 2, j1 = (2 * K + 1) & 3;
+            acc[i0][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i0]),
+                                                                  __builtin_bit_cast(bf16x8, b[j0]), acc[i0][j0], 0, 0, 0);
+            acc[i1][j1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i1]),
+                                                                  __builtin_bit_cast(bf16x8, b[j1]), acc[i1][j1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            d.template issue<K>(rs, reg, wave);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        two(std::integral_constant<int, 0>{});
+        two(std::integral_constant<int, 1>{});
+        two(std::integral_constant<int, 2>{});
+        two(std::integral_constant<int, 3>{});
+        two(std::integral_constant<int, 4>{});
+        two(std::integral_constant<int, 5>{});
+        two(std::integral_constant<int, 6>{});
+        two(std::integral_constant<int, 7>{});
+        if constexpr (PART == 1) {
+            ia += W_KC * lda;
+            ib += W_KC * ldb;
+            irem -= W_KC;
+            if (++ic == inch) {
+                ic = 0;
+                if (iv) {
+                    ++ij;
+                    iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+                    set_itile();
+                }
+            }
+        }
     };
 
     using I0 = std::integral_constant<int, 0>;
@@ -896,25 +918,66 @@ void gemm_dw_kernel(GemmArgs g) {
         for (int q = 0; q < W_Q - 1; q++) {
             w_read_q(st, qa[(q + 1) & 1], qb[(q + 1) & 1], wm, wn, lane, q + 1);
             __builtin_amdgcn_sched_barrier(0);
-            if (q == 0) p_mma(acc, f0a[SL], f0b[SL]);
+            // quarter 0 finishes the refill of the other stage
+            if (q == 0) p_mma_dma(f0a[SL], f0b[SL], sc ^ 1, std::integral_constant<int, 1>{});
             else p_mma(acc, qa[q & 1], qb[q & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
         w_barrier<0>();
-        // every wave has read all of this chunk's stage: refill it with the
-        // chunk after the next one
-        issue(sc);
-        sc = (sc + 1) % W_NST;
+        // every wave has read all of this chunk's stage: its refill with the
+        // chunk after the next one starts during the last quarter
+        const int sfree = sc;
+        sc ^= 1;
         w_read_q(w_lds + sc * W_STAGE, f0a[SL1], f0b[SL1], wm, wn, lane, 0);
         __builtin_amdgcn_sched_barrier(0);
-        p_mma(acc, qa[(W_Q - 1) & 1], qb[(W_Q - 1) & 1]);
+        p_mma_dma(qa[(W_Q - 1) & 1], qb[(W_Q - 1) & 1], sfree, std::integral_constant<int, 0>{});
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: two chunks in flight; the first one's quarter 0 fragments
-    issue(0);
-    issue(1);
-    w_barrier<2 * W_DR>();
+    // prologue: chunk 0 and the first part of chunk 1 in flight (the first
+    // quarter finishes chunk 1); the first chunk's quarter 0 fragments
+    {
+        const __amdgpu_buffer_rsrc_t r0 = make_rsrc_n(ia, nrec(irem, lda));
+        const __amdgpu_buffer_rsrc_t r1 = make_rsrc_n(ib, nrec(irem, ldb));
+        da.template issue<0>(r0, w_lds, wave);
+        da.template issue<1>(r0, w_lds, wave);
+        da.template issue<2>(r0, w_lds, wave);
+        da.template issue<3>(r0, w_lds, wave);
+        da.template issue<4>(r0, w_lds, wave);
+        da.template issue<5>(r0, w_lds, wave);
+        da.template issue<6>(r0, w_lds, wave);
+        da.template issue<7>(r0, w_lds, wave);
+        db.template issue<0>(r1, w_lds + W_OP, wave);
+        db.template issue<1>(r1, w_lds + W_OP, wave);
+        db.template issue<2>(r1, w_lds + W_OP, wave);
+        db.template issue<3>(r1, w_lds + W_OP, wave);
+        db.template issue<4>(r1, w_lds + W_OP, wave);
+        db.template issue<5>(r1, w_lds + W_OP, wave);
+        db.template issue<6>(r1, w_lds + W_OP, wave);
+        db.template issue<7>(r1, w_lds + W_OP, wave);
+        ia += W_KC * lda;
+        ib += W_KC * ldb;
+        irem -= W_KC;
+        if (++ic == inch) {
+            ic = 0;
+            if (iv) {
+                ++ij;
+                iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+                set_itile();
+            }
+        }
+        const __amdgpu_buffer_rsrc_t r2 = make_rsrc_n(ia, nrec(irem, lda));
+        char *s1 = w_lds + W_STAGE;
+        da.template issue<0>(r2, s1, wave);
+        da.template issue<1>(r2, s1, wave);
+        da.template issue<2>(r2, s1, wave);
+        da.template issue<3>(r2, s1, wave);
+        da.template issue<4>(r2, s1, wave);
+        da.template issue<5>(r2, s1, wave);
+        da.template issue<6>(r2, s1, wave);
+        da.template issue<7>(r2, s1, wave);
+    }
+    w_barrier<W_DR>();
     w_read_q(w_lds, f0a[0], f0b[0], wm, wn, lane, 0);
     zero_acc();
     while (cv) {
@@ -1192,32 +1255,42 @@ void gemm_rd_kernel(GemmArgs g) {
     };
     set_itile();
 
-    auto issue = [&](int s) __attribute__((always_inline)) {
+    // Part p of the issue of chunk ic into stage s: parts 0-3 are two
+    // activation loads each (8 in all), part 4 the fragment words (and, dX,
+    // the scales) and the step to the next chunk.  The chunk loop spreads the
+    // parts over its first five fragments, so the texture unit sees two loads
+    // per four MFMAs per wave instead of a burst of ten.
+    auto issue_part = [&](int s, auto p_c) __attribute__((always_inline)) {
+        constexpr int P = decltype(p_c)::value;
         char *st = wl + s * R_STAGE;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(pa, na), rf = make_rsrc_n(pf, nf);
-        const int so = ic * R_KC * ES;
-#pragma unroll
-        for (int h4 = 0; h4 < 2; h4++) {
-            char *d = st + h4 * 4096;
-            dma16_imm<0>(ra, d, boff[4 * h4 + 0], so);
-            dma16_imm<1024>(ra, d, boff[4 * h4 + 1], so);
-            dma16_imm<2048>(ra, d, boff[4 * h4 + 2], so);
-            dma16_imm<3072>(ra, d, boff[4 * h4 + 3], so);
-        }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rf, (LDS_AS void *)(st + R_B), 16, (uint32_t)lane * 16u, ic * 2048,
-                                                 0, 0);
-        if constexpr (MODE == MODE_DX)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(g.scale, ns), (LDS_AS void *)(st + R_B + R_A), 4,
-                                                     soff_lane,
-                                                     ic * R_KC * 4, 0, 0);
-        if (++ic == nch2) {
-            ic = 0;
-            if (iv) {
-                ++ij;
-                iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
-                set_itile();
+        if constexpr (P < 4) {
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(pa, na);
+            const int so = ic * R_KC * ES;
+            char *d = st + (P >> 1) * 4096;
+            dma16_imm<(P & 1) * 2048>(ra, d, boff[2 * P], so);
+            dma16_imm<(P & 1) * 2048 + 1024>(ra, d, boff[2 * P + 1], so);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(pf, nf), (LDS_AS void *)(st + R_B), 16,
+                                                     (uint32_t)lane * 16u, ic * 2048, 0, 0);
+            if constexpr (MODE == MODE_DX)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(g.scale, ns), (LDS_AS void *)(st + R_B + R_A), 4,
+                                                         soff_lane, ic * R_KC * 4, 0, 0);
+            if (++ic == nch2) {
+                ic = 0;
+                if (iv) {
+                    ++ij;
+                    iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+                    set_itile();
+                }
             }
         }
+    };
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        issue_part(s, std::integral_constant<int, 0>{});
+        issue_part(s, std::integral_constant<int, 1>{});
+        issue_part(s, std::integral_constant<int, 2>{});
+        issue_part(s, std::integral_constant<int, 3>{});
+        issue_part(s, std::integral_constant<int, 4>{});
     };
 
     // ---- compute side: tile cj
@@ -1335,25 +1408,37 @@ void gemm_rd_kernel(GemmArgs g) {
     using I1 = std::integral_constant<int, 1>;
     int sc = 0;   // LDS stage of the current chunk
 
-    // one chunk (register slot SL): issue three chunks ahead, then the eight
-    // fragments (K quarter, 32 rows) of 4 MFMAs each.  The next fragment is
-    // decoded one dword per MFMA while the current one multiplies (the first
-    // fragment of the next chunk during the last one of this chunk); halfway,
-    // wait for the next chunk's loads and read its first fragments.
+    // one chunk (register slot SL): the eight fragments (K quarter, 32 rows) of
+    // 4 MFMAs each, with the issue of the chunk three ahead spread over the
+    // first five.  The next fragment is decoded one dword per MFMA while the
+    // current one multiplies (the first fragment of the next chunk during the
+    // last one of this chunk); halfway, wait for the next chunk's loads and
+    // read its first fragments.
     auto chunk = [&](auto sl_c) __attribute__((always_inline)) {
         constexpr int SL = decltype(sl_c)::value, SL1 = SL ^ 1;
-        issue((sc + 3) & 3);
+        const int sis = (sc + 3) & 3;
         r_read_b(wl + sc * R_STAGE, fb1, l32, h, 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int f = 0; f < 8; f++) {
+            if (f < 4) {
+                // f is a constant once the loop is unrolled
+                if (f == 0) issue_part(sis, std::integral_constant<int, 0>{});
+                if (f == 1) issue_part(sis, std::integral_constant<int, 1>{});
+                if (f == 2) issue_part(sis, std::integral_constant<int, 2>{});
+                if (f == 3) issue_part(sis, std::integral_constant<int, 3>{});
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if (f == 4) {
-                // loads issued after the next chunk's: the two later chunk
-                // issues, plus 64 epilogue stores in a tile's first two
-                // chunks (where 63 waits for more than needed)
+                // loads issued after the next chunk's: the chunk two ahead
+                // (OPS) and the 8 activation loads of the one three ahead, plus
+                // 64 epilogue stores in a tile's first two chunks (where 63
+                // waits for more than needed)
                 wait_vm<63>();
-                if (!hist) wait_vm<2 * OPS>();
+                if (!hist) wait_vm<OPS + 8>();
                 read_ahead((sc + 1) & 3, std::integral_constant<int, SL1>{});
+                __builtin_amdgcn_sched_barrier(0);
+                issue_part(sis, std::integral_constant<int, 4>{});
                 __builtin_amdgcn_sched_barrier(0);
             }
             const int fm = f & 3;
