@@ -209,6 +209,35 @@ def sampled_case(o, wname, proj):
         assert e <= tol, f"{wname}/{name}: {k} relL2 {e:.3e} > {tol:.1e}"
 
 
+# Shapes on which every product takes the 256 x 256 kernels with ragged edges:
+# M and N off the tile grid, K off the 32-wide chunk grid with an odd chunk
+# count (the padding chunk), and a token count off the 64-token dW chunk.
+@pytest.mark.parametrize("T,n_in,n_out", [(4000, 1032, 4104), (4000, 4104, 1032)])
+def test_parity_tile256_ragged_sampled(o, T, n_in, n_out):
+    log(f"parity 256-tile kernels, ragged T={T} in={n_in} out={n_out} (sampled)")
+    p = synth.make_inputs(T, n_in, n_out, act="bf16", config_id=303, proj_id=n_in)
+    d = DeviceProjection(p)
+    d.step()
+    torch.cuda.synchronize()
+    rows = np.union1d(synth.sample_indices(synth.stream_seed(78, T, n_in, 0), 40, T), [0, T - 1])
+    cols = np.union1d(synth.sample_indices(synth.stream_seed(78, T, n_out, 1), 14, n_out), [0, n_out - 1])
+    rt = torch.from_numpy(rows).cuda()
+    ct = torch.from_numpy(cols).cuda()
+    errs = dict(Y=rel_l2(d.Y[rt].cpu().numpy(), o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows)),
+                dX=rel_l2(d.dX[rt].cpu().numpy(), o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows)))
+    _, gq, sg = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
+    errs["gq"] = rel_l2(d.gq[:, ct].cpu().numpy(), gq)
+    errs["sgrad"] = rel_l2(d.sgrad[ct].cpu().numpy(), sg)
+    log(f"  relL2 {errs}")
+    for k, e in errs.items():
+        assert e <= tol_for("bf16"), f"{k} relL2 {e:.3e}"
+    # bf16 Y from the same kernel is the round-to-nearest-even of its fp32 Y
+    Yb = torch.empty((T, n_out), dtype=torch.bfloat16, device="cuda")
+    tl.tern_linear_fwd(d.X, d.packed, d.scale, Yb)
+    torch.cuda.synchronize()
+    assert torch.equal(Yb, d.Y.to(torch.bfloat16))
+
+
 @pytest.mark.parametrize("proj", range(6))
 def test_parity_mid_sampled(o, proj):
     sampled_case(o, "mid", proj)
