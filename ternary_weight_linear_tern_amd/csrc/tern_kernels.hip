@@ -854,54 +854,48 @@ void gemm_dw_kernel(GemmArgs g) {
                 for (int i = 0; i < 16; i++) acc[fm][fn][i] = 0.0f;
     };
 
-    // The refill of a stage is issued in two parts, each spread over 16 MFMAs
-    // (one load per two): part 0 (operand X) during the last K quarter of the
-    // chunk that freed the stage, part 1 (operand dY, then the step to the
-    // next chunk) during the first quarter of the next chunk.  p_mma_dma runs
-    // the 16 MFMAs of a quarter with the loads of one part between them.
-    auto p_mma_dma = [&](const u32x4 (&a)[4], const u32x4 (&b)[4], int s, auto part_c)
-                         __attribute__((always_inline)) {
-        constexpr int PART = decltype(part_c)::value;
-        char *reg = w_lds + s * W_STAGE + PART * W_OP;
-        const __amdgpu_buffer_rsrc_t rs =
-            PART == 0 ? make_rsrc_n(ia, nrec(irem, lda)) : make_rsrc_n(ib, nrec(irem, ldb));
-        const DmaTok &d = PART == 0 ? da : db;
-        auto two = [&](auto k_c) __attribute__((always_inline)) {
-            constexpr int K = decltype(k_c)::value;
-            constexpr int i0 = (2 * K) >> 2, j0 = (2 * K) & 3, i1 = (2 * K + 1) >> 2, j1 = (2 * K + 1) & 3;
-            acc[i0][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i0]),
-                                                                  __builtin_bit_cast(bf16x8, b[j0]), acc[i0][j0], 0, 0, 0);
-            acc[i1][j1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i1]),
-                                                                  __builtin_bit_cast(bf16x8, b[j1]), acc[i1][j1], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            d.template issue<K>(rs, reg, wave);
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        two(std::integral_constant<int, 0>{});
-        two(std::integral_constant<int, 1>{});
-        two(std::integral_constant<int, 2>{});
-        two(std::integral_constant<int, 3>{});
-        two(std::integral_constant<int, 4>{});
-        two(std::integral_constant<int, 5>{});
-        two(std::integral_constant<int, 6>{});
-        two(std::integral_constant<int, 7>{});
-        if constexpr (PART == 1) {
-            ia += W_KC * lda;
-            ib += W_KC * ldb;
-            irem -= W_KC;
-            if (++ic == inch) {
-                ic = 0;
-                if (iv) {
-                    ++ij;
-                    iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
-                    set_itile();
-                }
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // the issue side's step to the next chunk (and item)
+    auto next_chunk = [&]() __attribute__((always_inline)) {
+        ia += W_KC * lda;
+        ib += W_KC * ldb;
+        irem -= W_KC;
+        if (++ic == inch) {
+            ic = 0;
+            if (iv) {
+                ++ij;
+                iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+                set_itile();
             }
         }
     };
-
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
+    // The 16 MFMAs of the last K quarter with, after each, one of the 16
+    // loads (8 per operand) that refill stage s with the chunk after the next,
+    // then the step to that chunk.
+    auto p_mma_dma16 = [&](const u32x4 (&a)[4], const u32x4 (&b)[4], int s) __attribute__((always_inline)) {
+        char *st = w_lds + s * W_STAGE;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(ia, nrec(irem, lda)), rb = make_rsrc_n(ib, nrec(irem, ldb));
+        auto one = [&](auto k_c) __attribute__((always_inline)) {
+            constexpr int K = decltype(k_c)::value;
+            constexpr int i = K >> 2, j = K & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                                __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (K < 8) da.template issue<K & 7>(ra, st, wave);
+            else db.template issue<K & 7>(rb, st + W_OP, wave);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        one(std::integral_constant<int, 0>{}); one(std::integral_constant<int, 1>{});
+        one(std::integral_constant<int, 2>{}); one(std::integral_constant<int, 3>{});
+        one(std::integral_constant<int, 4>{}); one(std::integral_constant<int, 5>{});
+        one(std::integral_constant<int, 6>{}); one(std::integral_constant<int, 7>{});
+        one(std::integral_constant<int, 8>{}); one(std::integral_constant<int, 9>{});
+        one(std::integral_constant<int, 10>{}); one(std::integral_constant<int, 11>{});
+        one(std::integral_constant<int, 12>{}); one(std::integral_constant<int, 13>{});
+        one(std::integral_constant<int, 14>{}); one(std::integral_constant<int, 15>{});
+        next_chunk();
+    };
 
     // one chunk (fragment slot SL): run K quarters 0 .. W_Q - 2, reading each
     // next quarter's fragments during the current one's MFMAs; wait for the
@@ -918,66 +912,47 @@ void gemm_dw_kernel(GemmArgs g) {
         for (int q = 0; q < W_Q - 1; q++) {
             w_read_q(st, qa[(q + 1) & 1], qb[(q + 1) & 1], wm, wn, lane, q + 1);
             __builtin_amdgcn_sched_barrier(0);
-            // quarter 0 finishes the refill of the other stage
-            if (q == 0) p_mma_dma(f0a[SL], f0b[SL], sc ^ 1, std::integral_constant<int, 1>{});
+            if (q == 0) p_mma(acc, f0a[SL], f0b[SL]);
             else p_mma(acc, qa[q & 1], qb[q & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
         w_barrier<0>();
         // every wave has read all of this chunk's stage: its refill with the
-        // chunk after the next one starts during the last quarter
+        // chunk after the next one goes out during the last quarter, one load
+        // per MFMA
         const int sfree = sc;
         sc ^= 1;
         w_read_q(w_lds + sc * W_STAGE, f0a[SL1], f0b[SL1], wm, wn, lane, 0);
         __builtin_amdgcn_sched_barrier(0);
-        p_mma_dma(qa[(W_Q - 1) & 1], qb[(W_Q - 1) & 1], sfree, std::integral_constant<int, 0>{});
+        p_mma_dma16(qa[(W_Q - 1) & 1], qb[(W_Q - 1) & 1], sfree);
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: chunk 0 and the first part of chunk 1 in flight (the first
-    // quarter finishes chunk 1); the first chunk's quarter 0 fragments
-    {
-        const __amdgpu_buffer_rsrc_t r0 = make_rsrc_n(ia, nrec(irem, lda));
-        const __amdgpu_buffer_rsrc_t r1 = make_rsrc_n(ib, nrec(irem, ldb));
-        da.template issue<0>(r0, w_lds, wave);
-        da.template issue<1>(r0, w_lds, wave);
-        da.template issue<2>(r0, w_lds, wave);
-        da.template issue<3>(r0, w_lds, wave);
-        da.template issue<4>(r0, w_lds, wave);
-        da.template issue<5>(r0, w_lds, wave);
-        da.template issue<6>(r0, w_lds, wave);
-        da.template issue<7>(r0, w_lds, wave);
-        db.template issue<0>(r1, w_lds + W_OP, wave);
-        db.template issue<1>(r1, w_lds + W_OP, wave);
-        db.template issue<2>(r1, w_lds + W_OP, wave);
-        db.template issue<3>(r1, w_lds + W_OP, wave);
-        db.template issue<4>(r1, w_lds + W_OP, wave);
-        db.template issue<5>(r1, w_lds + W_OP, wave);
-        db.template issue<6>(r1, w_lds + W_OP, wave);
-        db.template issue<7>(r1, w_lds + W_OP, wave);
-        ia += W_KC * lda;
-        ib += W_KC * ldb;
-        irem -= W_KC;
-        if (++ic == inch) {
-            ic = 0;
-            if (iv) {
-                ++ij;
-                iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
-                set_itile();
-            }
-        }
-        const __amdgpu_buffer_rsrc_t r2 = make_rsrc_n(ia, nrec(irem, lda));
-        char *s1 = w_lds + W_STAGE;
-        da.template issue<0>(r2, s1, wave);
-        da.template issue<1>(r2, s1, wave);
-        da.template issue<2>(r2, s1, wave);
-        da.template issue<3>(r2, s1, wave);
-        da.template issue<4>(r2, s1, wave);
-        da.template issue<5>(r2, s1, wave);
-        da.template issue<6>(r2, s1, wave);
-        da.template issue<7>(r2, s1, wave);
-    }
-    w_barrier<W_DR>();
+    // prologue: chunks 0 and 1 in flight; the first one's quarter 0 fragments
+    auto issue_all = [&](int s) __attribute__((always_inline)) {
+        char *st = w_lds + s * W_STAGE;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(ia, nrec(irem, lda)), rb = make_rsrc_n(ib, nrec(irem, ldb));
+        da.template issue<0>(ra, st, wave);
+        da.template issue<1>(ra, st, wave);
+        da.template issue<2>(ra, st, wave);
+        da.template issue<3>(ra, st, wave);
+        da.template issue<4>(ra, st, wave);
+        da.template issue<5>(ra, st, wave);
+        da.template issue<6>(ra, st, wave);
+        da.template issue<7>(ra, st, wave);
+        db.template issue<0>(rb, st + W_OP, wave);
+        db.template issue<1>(rb, st + W_OP, wave);
+        db.template issue<2>(rb, st + W_OP, wave);
+        db.template issue<3>(rb, st + W_OP, wave);
+        db.template issue<4>(rb, st + W_OP, wave);
+        db.template issue<5>(rb, st + W_OP, wave);
+        db.template issue<6>(rb, st + W_OP, wave);
+        db.template issue<7>(rb, st + W_OP, wave);
+        next_chunk();
+    };
+    issue_all(0);
+    issue_all(1);
+    w_barrier<2 * W_DR>();
     w_read_q(w_lds, f0a[0], f0b[0], wm, wn, lane, 0);
     zero_acc();
     while (cv) {
