@@ -975,11 +975,12 @@ void gemm_dw_kernel(GemmArgs g) {
         // One split: gq = G * scale[c] and the sgrad partial.  Several splits:
         // the raw G partial (scale 1 makes the store exact), no sgrad partial.
         const bool split = g.splits > 1;
-        // tern codes of this lane's 64 rows x 4 columns, from the forward
+        // tern values of this lane's 64 rows x 4 columns, from the forward
         // fragment-ordered copy (its rows are the columns c, its K the rows r):
         // per 32-row fragment fm, the 16 bytes of each 8-row half hf hold the
-        // lane's four columns.  Pre-shifted by 4h, row 8 (i / 4) + 4h + i % 4
-        // of the fragment sits at a bit offset fixed by i.
+        // lane's four columns.  Pre-shifted by 16h, row 8 (i / 4) + 4h + i % 4
+        // of the fragment sits in nibble i % 4, at bits 1 and 3 (rows 0-15)
+        // or 0 and 2 (rows 16-31).
         const int nchf = (g.M + 31) >> 5;
         u32x4 tw[4][2];
 #pragma unroll
@@ -992,7 +993,7 @@ void gemm_dw_kernel(GemmArgs g) {
                                  ? *(const u32x4 *)(g.frag + ((int64_t)(ctn * nchf + sch) * 512 +
                                                               (wn * 64 + hf * 32 + l32) * 4))
                                  : z;
-                tw[fm][hf] >>= (uint32_t)(4 * h);
+                tw[fm][hf] >>= (uint32_t)(16 * h);
             }
         }
         float scv[4], ps[4];
@@ -1011,13 +1012,14 @@ void gemm_dw_kernel(GemmArgs g) {
                 const int so = (rg + (i & 3)) * g.N * 4;
                 // k = 16 kk + 8 hf + e within the fragment, e = 4h + i % 4
                 const int kk = i >> 3, hf = (i >> 2) & 1;
-                const int pos = ((i & 1) ? 16 : 0) + 8 * kk + 2 * ((i & 3) >> 1);
+                const int pos = 4 * (i & 3) + 1 - kk;   // nonzero bit; the sign bit is 2 above
 #pragma unroll
                 for (int fn = 0; fn < 4; fn++) {
                     const float gv = acc[fm][fn][i];
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gv * scv[fn]), ro, vo[fn], so,
                                                           0);
-                    ps[fn] += gv * code_to_f32((tw[fm][hf][fn] >> pos) & 3u);
+                    const uint32_t b = tw[fm][hf][fn] >> pos;
+                    ps[fn] += gv * code_to_f32((b & 1u) | ((b >> 1) & 2u));
                 }
             }
         if (!split) {
@@ -1049,11 +1051,14 @@ void gemm_dw_kernel(GemmArgs g) {
 // dX: m = r, k = c) in tiles of 256 rows and chunks of 32 K.  The 512 words of
 // (tile, chunk) are ordered (wm, lane, fm): wm = 128-row half, lane = lane of
 // the wave, fm = 32-row MFMA fragment, so one 16-byte load per lane brings a
-// wave all four of its fragments.  Word (wm, lane, fm) holds the 16 codes of
-// row m = 256 tile + 128 wm + 32 fm + lane % 32 at k = 32 chunk + 16 kk +
-// 8 (lane / 32) + e (kk < 2, e < 8), each at bit 2p (e even) or 16 + 2p (e
-// odd) with p = 4 kk + e / 2: one shift and one mask leave the two codes of an
-// MFMA operand dword at bits 0-1 and 16-17.  Codes beyond the matrix are 00.
+// wave all four of its fragments.  Word (wm, lane, fm) holds the 16 ternary
+// values of row m = 256 tile + 128 wm + 32 fm + lane % 32 at k = 32 chunk +
+// 16 kk + 8 (lane / 32) + e (kk < 2, e < 8) in nibble e: bits 1 (nonzero) and
+// 3 (negative) for kk = 0, bits 0 and 2 for kk = 1.  Masked with 0xAAAAAAAA
+// (kk = 0) or shifted left by one and masked (kk = 1), a word is eight fp4
+// (e2m1) values 0, +1.0 (0x2) or -1.0 (0xA), and byte j converts to the bf16
+// pair of MFMA operand dword j in one instruction.  Values beyond the matrix
+// are 0.
 // ---------------------------------------------------------------------------
 // One workgroup writes D_G chunks of one tile of a copy.  Both copies read a
 // block of the canonical words staged in LDS: for the dX operand, the tile's
@@ -1096,8 +1101,8 @@ __global__ __launch_bounds__(256) void derive_kernel(const uint32_t *__restrict_
                     if (sg * (32 * D_G) + kl >= K) continue;
                     const int br = DXOP ? ml : kl, bc = DXOP ? kl : ml;    // block row, block column
                     const uint32_t code = (blk[br][bc >> 4] >> (2 * (bc & 15))) & 3u;
-                    const int p = 4 * kk + (e >> 1);
-                    word |= code << ((e & 1) ? 16 + 2 * p : 2 * p);
+                    const uint32_t nz = code & 1u, neg = (code >> 1) & nz;
+                    word |= ((nz << 1) | (neg << 3)) >> kk << (4 * e);
                 }
         }
         frag[(tile * nch + chunk) * 512 + d] = word;
@@ -1151,16 +1156,29 @@ __device__ __forceinline__ void r_read_b(const char *st, u32x4 (&b)[4], int l32,
     for (int f = 0; f < 4; f++) b[f] = *(const u32x4 *)(st + (f * 32 + l32) * 64 + ps * 16);
 }
 
-// Two ternary codes at bits 0-1 and 16-17 of t (higher bits ignored) times a
-// pair of bf16 scales: p4 is the pair XOR 0x40004000.  Per 16-bit half: bits
-// 14-15 of (t << 14) are (nonzero, negative), which XORed into p4 restore the
-// scale (code 01) or flip its sign (code 11); the mask keeps nonzero codes.
-__device__ __forceinline__ uint32_t r_scaled_pair(uint32_t t, uint32_t p4) {
-    typedef short s16x2 __attribute__((ext_vector_type(2)));
-    const s16x2 tv = __builtin_bit_cast(s16x2, t);
-    const s16x2 sg = tv << (short)14;
-    const s16x2 nz = (s16x2)(tv << (short)15) >> (short)15;
-    return (p4 ^ __builtin_bit_cast(uint32_t, sg)) & __builtin_bit_cast(uint32_t, nz);
+// Byte J of x (two fp4 e2m1 values, low nibble first) -> two bf16 values in
+// one dword (the scale operand 1.0 leaves them unscaled).
+template <int J>
+__device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t x) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 1.0f, J));
+}
+__device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t x, int j) {
+    switch (j) {   // j is a constant wherever this is inlined
+    case 0: return fp4_pair_bf16<0>(x);
+    case 1: return fp4_pair_bf16<1>(x);
+    case 2: return fp4_pair_bf16<2>(x);
+    default: return fp4_pair_bf16<3>(x);
+    }
+}
+
+// A bf16 pair v of ternary values (0x0000, 0x3F80 = +1 or 0xBF80 = -1 per
+// half) times a pair of bf16 scales: q is the scale pair XOR 0x3F803F80.  v ^ q
+// is the scale where v = +1 and its negation where v = -1; the mask comes from
+// a byte permute with v as the selector (selector bytes 0x80, 0x3F and 0xBF
+// give 0xFF, selector 0 picks the zero byte of the second source), so zero
+// halves stay zero.
+__device__ __forceinline__ uint32_t r_scaled_pair(uint32_t v, uint32_t q) {
+    return (v ^ q) & __builtin_amdgcn_perm(0u, 0u, v);
 }
 
 template <int MODE>
@@ -1277,7 +1295,7 @@ void gemm_rd_kernel(GemmArgs g) {
     u32x4 fa[2];        // fragment words (one dword per fm) of the current / next chunk
     u32x4 fb0[2][4];    // activation fragments, K quarter 0, of the current / next chunk
     u32x4 fb1[4];       // K quarter 1 of the current chunk
-    uint32_t p4[2][8];  // dX: bf16 scale pairs ^ 0x40004000 of the current / next chunk
+    uint32_t p4[2][8];  // dX: bf16 scale pairs ^ 0x3F803F80 of the current / next chunk
 
     auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -1301,23 +1319,25 @@ void gemm_rd_kernel(GemmArgs g) {
                 const f32x4 lo = *(const f32x4 *)(sc + 16 * kk + 8 * h);
                 const f32x4 hi = *(const f32x4 *)(sc + 16 * kk + 8 * h + 4);
                 const f32x2 v0 = {lo.x, lo.y}, v1 = {lo.z, lo.w}, v2 = {hi.x, hi.y}, v3 = {hi.z, hi.w};
-                p4[SL][4 * kk + 0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2)) ^ 0x40004000u;
-                p4[SL][4 * kk + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2)) ^ 0x40004000u;
-                p4[SL][4 * kk + 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2)) ^ 0x40004000u;
-                p4[SL][4 * kk + 3] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v3, bf16x2)) ^ 0x40004000u;
+                p4[SL][4 * kk + 0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v0, bf16x2)) ^ 0x3F803F80u;
+                p4[SL][4 * kk + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v1, bf16x2)) ^ 0x3F803F80u;
+                p4[SL][4 * kk + 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2)) ^ 0x3F803F80u;
+                p4[SL][4 * kk + 3] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v3, bf16x2)) ^ 0x3F803F80u;
             }
         }
     };
 
     // dword j of decoded fragment f (K quarter f / 4, rows fm = f % 4) of
-    // fragment words w4
+    // fragment words w4: the quarter's fp4 values (bits 1 and 3 of each
+    // nibble) converted, times the dX scales
     auto dec = [&](const u32x4 &w4, const uint32_t (&pp)[8], int f, int j) __attribute__((always_inline)) {
         const int kk = f >> 2, fm = f & 3;
-        const uint32_t t = w4[fm] >> (2 * (4 * kk + j));
-        if constexpr (MODE == MODE_FWD) return tern_pair_bf16(t & 0x00030003u);
-        else return r_scaled_pair(t, pp[4 * kk + j]);
+        const uint32_t x = (kk ? w4[fm] << 1 : w4[fm]) & 0xAAAAAAAAu;
+        const uint32_t v = fp4_pair_bf16(x, j);
+        if constexpr (MODE == MODE_FWD) return v;
+        else return r_scaled_pair(v, pp[4 * kk + j]);
     };
-    constexpr int DEC_OPS = MODE == MODE_FWD ? 4 : 6;   // VALU per decoded dword
+    constexpr int DEC_OPS = MODE == MODE_FWD ? 2 : 5;   // VALU per decoded dword (with the masks)
     u32x4 acur;   // decoded fragment whose MFMAs come next (carried across chunks)
 
     // Epilogue of tile (ctm, ctn): 64 buffer stores per wave whatever the edges

@@ -257,21 +257,21 @@ def _frag_copy(tern, M_is_in):
     """The fragment-ordered copy of include/tern.h, built from a tern matrix
     [in, out] of {-1, 0, 1}: operand A[m][k] = tern[k][m] (forward copy,
     M_is_in False) or tern[m][k] (dX copy).  Word (tile, chunk, wm, lane, fm)
-    holds the codes of row m = 256 tile + 128 wm + 32 fm + lane % 32 at
-    k = 32 chunk + 16 kk + 8 (lane // 32) + e at bit 2p (e even) or 16 + 2p
-    (e odd), p = 4 kk + e // 2; code 01 = +1, 11 = -1, 00 = 0."""
+    holds the values of row m = 256 tile + 128 wm + 32 fm + lane % 32 at
+    k = 32 chunk + 16 kk + 8 (lane // 32) + e in nibble e: for kk = 0 the
+    fp4 (e2m1) encoding of the value (+1 = 0x2, -1 = 0xA, 0 = 0x0), for
+    kk = 1 the same shifted right by one bit."""
     A = tern if M_is_in else tern.T
     M, K = A.shape
     tiles, nch = -(-M // 256), -(-K // 32)
     Ap = np.zeros((tiles * 256, nch * 32), np.int64)
     Ap[:M, :K] = A
-    code = np.where(Ap > 0, 1, np.where(Ap < 0, 3, 0)).astype(np.uint64)
-    c = code.reshape(tiles, 2, 4, 32, nch, 2, 2, 8)        # tile, wm, fm, l32, chunk, kk, h, e
+    fp4 = np.where(Ap > 0, 0x2, np.where(Ap < 0, 0xA, 0)).astype(np.uint64)
+    c = fp4.reshape(tiles, 2, 4, 32, nch, 2, 2, 8)         # tile, wm, fm, l32, chunk, kk, h, e
     c = c.transpose(0, 4, 1, 6, 3, 2, 5, 7)                # tile, chunk, wm, h, l32, fm, kk, e
-    kk = np.arange(2)[:, None]
-    e = np.arange(8)[None, :]
-    pos = np.where(e % 2 == 1, 16, 0) + 2 * (4 * kk + e // 2)
-    word = (c << pos.astype(np.uint64)).sum(axis=(-2, -1))  # codes occupy disjoint bits
+    c = c >> np.arange(2, dtype=np.uint64)[:, None]        # kk = 1 one bit lower
+    pos = 4 * np.arange(8, dtype=np.uint64)[None, :]
+    word = (c << pos).sum(axis=(-2, -1))                   # values occupy disjoint bits
     return word.reshape(-1).astype(np.uint32)
 
 
