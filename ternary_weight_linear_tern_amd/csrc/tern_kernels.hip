@@ -871,8 +871,8 @@ void gemm_dw_kernel(GemmArgs g) {
         }
     };
     // The 16 MFMAs of the last K quarter with, after each, one of the 16
-    // loads (8 per operand) that refill stage s with the chunk after the next,
-    // then the step to that chunk.
+    // loads (8 per operand) that refill stage s with the chunk after the next
+    // and one of the next chunk's quarter-0 reads, then the step to that chunk.
     auto p_mma_dma16 = [&](const u32x4 (&a)[4], const u32x4 (&b)[4], int s) __attribute__((always_inline)) {
         char *st = w_lds + s * W_STAGE;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(ia, nrec(irem, lda)), rb = make_rsrc_n(ib, nrec(irem, ldb));
@@ -881,10 +881,8 @@ void gemm_dw_kernel(GemmArgs g) {
             constexpr int i = K >> 2, j = K & 3;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i]),
                                                                 __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
             if constexpr (K < 8) da.template issue<K & 7>(ra, st, wave);
             else db.template issue<K & 7>(rb, st + W_OP, wave);
-            __builtin_amdgcn_sched_barrier(0);
         };
         one(std::integral_constant<int, 0>{}); one(std::integral_constant<int, 1>{});
         one(std::integral_constant<int, 2>{}); one(std::integral_constant<int, 3>{});
@@ -894,6 +892,15 @@ void gemm_dw_kernel(GemmArgs g) {
         one(std::integral_constant<int, 10>{}); one(std::integral_constant<int, 11>{});
         one(std::integral_constant<int, 12>{}); one(std::integral_constant<int, 13>{});
         one(std::integral_constant<int, 14>{}); one(std::integral_constant<int, 15>{});
+        // each MFMA followed by one refill load and one of the next chunk's
+        // 16 quarter-0 transposing reads (issued just before this call)
+#pragma unroll
+        for (int k = 0; k < 16; k++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         next_chunk();
     };
 
@@ -911,9 +918,15 @@ void gemm_dw_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < W_Q - 1; q++) {
             w_read_q(st, qa[(q + 1) & 1], qb[(q + 1) & 1], wm, wn, lane, q + 1);
-            __builtin_amdgcn_sched_barrier(0);
             if (q == 0) p_mma(acc, f0a[SL], f0b[SL]);
             else p_mma(acc, qa[q & 1], qb[q & 1]);
+            // one MFMA, then one of the next quarter's 16 transposing reads:
+            // the reads issue in the MFMAs' shadow instead of as a burst
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         w_barrier<0>();
@@ -923,7 +936,6 @@ void gemm_dw_kernel(GemmArgs g) {
         const int sfree = sc;
         sc ^= 1;
         w_read_q(w_lds + sc * W_STAGE, f0a[SL1], f0b[SL1], wm, wn, lane, 0);
-        __builtin_amdgcn_sched_barrier(0);
         p_mma_dma16(qa[(W_Q - 1) & 1], qb[(W_Q - 1) & 1], sfree);
         __builtin_amdgcn_sched_barrier(0);
     };
