@@ -5,7 +5,11 @@ One step = for every projection of one layer of the workload: materialize
 (gq, sgrad), all through the C ABI on one stream, inputs already resident in
 HBM.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large] [--launch eager|graph]
+
+By default one step's library calls are recorded as a HIP graph (tern_graph_*)
+and its replays are timed (--launch eager times the calls themselves); the
+per-part times always come from eager calls, timed with events between them.
 """
 from __future__ import annotations
 
@@ -37,6 +41,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large", choices=["rwkv_small", "mid", "large", "largest"])
+    ap.add_argument("--launch", default="graph", choices=["eager", "graph"],
+                    help="graph (default): time replays of one recorded step; eager: time the calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="oracle sample: token rows per projection")
     ap.add_argument("--cpu-cols", type=int, default=768, help="oracle sample: output columns per projection")
@@ -89,7 +95,7 @@ def main():
 
     PARTS = ("materialize", "fwd", "bwd_dx", "bwd_dw")
 
-    def step(evs=None):
+    def step(evs=None, stream=stream):
         for j, d in enumerate(projs):
             if evs is not None:
                 evs[j][0].record(stream)
@@ -122,6 +128,30 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / a.steps
+
+    eager_ms_per_step = ms_per_step
+    if a.launch == "graph":
+        # one step recorded on a side stream, replayed as one launch per step
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        tl.tern_graph_begin(gs)
+        try:
+            step(stream=gs)
+        finally:
+            graph = tl.tern_graph_end(gs)
+        try:
+            for _ in range(a.warmup):
+                tl.tern_graph_launch(graph, gs)
+            torch.cuda.synchronize()
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record(gs)
+            for _ in range(a.steps):
+                tl.tern_graph_launch(graph, gs)
+            g1.record(gs)
+            torch.cuda.synchronize()
+            ms_per_step = g0.elapsed_time(g1) / a.steps
+        finally:
+            tl.tern_graph_destroy(graph)
 
     part_ms = {p: 0.0 for p in PARTS}
     for k in range(a.steps):
@@ -186,7 +216,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T,
                    "projections": [[n, i, o] for n, i, o in w.projs],
-                   "theta": w.theta, "q": w.q_law, "scale": w.scale_law, "act": w.act},
+                   "theta": w.theta, "q": w.q_law, "scale": w.scale_law, "act": w.act,
+                   "launch": "hipgraph" if a.launch == "graph" else "eager"},
+        "eager_ms_per_step": round(eager_ms_per_step, 4),
         "tokens_per_s": round(tokens_per_s, 1),
         "mfma_frac": round(tflops / peak, 4),
         "flops_per_step": flops_step,

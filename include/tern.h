@@ -158,6 +158,38 @@ int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype,
                        float *gq, float *sgrad, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/*
+ * Graphs of library calls.  The page's trainer launches every glue kernel and
+ * GEMM of a step separately and notes that it is launch-bound; a caller can
+ * instead record any sequence of the calls above (for example materialize,
+ * forward and backward of all six projections of a layer) once and replay it
+ * as one launch.
+ *
+ * tern_graph_begin -- start recording the work that this thread enqueues on
+ *   `stream`, which must be a created stream (not NULL, the legacy default
+ *   stream).  Until tern_graph_end, the entry points above validate their
+ *   arguments as usual but only record their kernels: nothing runs.  The
+ *   library records no memset, copy, allocation or synchronisation.
+ * tern_graph_end -- stop recording on `stream` and instantiate the graph;
+ *   *graph receives an opaque handle owned by the caller.  Buffers are
+ *   recorded by address: each replay reads and writes the same device
+ *   memory, with the contents it holds when the replay runs.  On failure
+ *   *graph is NULL.
+ * tern_graph_launch -- enqueue one replay on `stream` (any stream of the
+ *   device the graph was recorded on), ordered like a kernel launch.
+ * tern_graph_destroy -- release the handle (NULL is accepted); replays
+ *   already enqueued complete normally.
+ * The handle holds host-side graph objects, no device memory of its own.
+ * Errors: NULL (stream, graph or handle missing), HIP (the runtime refused the
+ *   capture, e.g. a stream that is already recording or a capture that a
+ *   synchronising call invalidated, or the instantiation or launch).
+ */
+typedef struct tern_graph_s *tern_graph_t;
+int tern_graph_begin(void *stream);
+int tern_graph_end(void *stream, tern_graph_t *graph);
+int tern_graph_launch(tern_graph_t graph, void *stream);
+int tern_graph_destroy(tern_graph_t graph);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *tern_status_str(int status);
 

@@ -40,6 +40,10 @@ SIGNATURES = {
     "tern_linear_bwd_dx": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp]),
     "tern_linear_bwd_dw": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
                                           _vp, _sz, _vp]),
+    "tern_graph_begin": (ctypes.c_int, [_vp]),
+    "tern_graph_end": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
+    "tern_graph_launch": (ctypes.c_int, [_vp, _vp]),
+    "tern_graph_destroy": (ctypes.c_int, [_vp]),
     "tern_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "tern_version": (ctypes.c_char_p, []),
 }
@@ -168,6 +172,28 @@ def tern_linear_bwd_dw(X, dY, tern_packed, scale, gq, sgrad, workspace, stream=N
                                   n_in, n_out, _ptr(gq), _ptr(sgrad), _ptr(workspace), ws_bytes,
                                   _stream(stream))
     _check("tern_linear_bwd_dw", rc)
+
+
+def tern_graph_begin(stream) -> None:
+    """Start recording the library calls enqueued on `stream` (a created
+    torch.cuda.Stream or raw handle, not the legacy default stream)."""
+    _check("tern_graph_begin", lib().tern_graph_begin(_stream(stream)))
+
+
+def tern_graph_end(stream) -> ctypes.c_void_p:
+    """Stop recording on `stream`; returns the instantiated graph's handle
+    (release it with tern_graph_destroy)."""
+    h = _vp()
+    _check("tern_graph_end", lib().tern_graph_end(_stream(stream), ctypes.byref(h)))
+    return h
+
+
+def tern_graph_launch(graph, stream=None) -> None:
+    _check("tern_graph_launch", lib().tern_graph_launch(graph, _stream(stream)))
+
+
+def tern_graph_destroy(graph) -> None:
+    _check("tern_graph_destroy", lib().tern_graph_destroy(graph))
 
 
 # ---------------------------------------------------------------------------

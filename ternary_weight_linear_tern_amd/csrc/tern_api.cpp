@@ -2,9 +2,12 @@
 //
 // Each entry point validates its arguments (HIP-free checks from tern_plan),
 // plans the launches and enqueues them on the caller's stream.  Nothing here
-// allocates, synchronises or keeps state.
+// allocates device memory, synchronises or keeps state; the graph calls at the
+// end hold host-side graph objects in a handle the caller owns.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <new>
 
 #include "../../include/tern.h"
 #include "tern_kernels.h"
@@ -249,6 +252,57 @@ int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype, const u
     if (rc) return rc;
     return hip_status(enqueue_dw(X, dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, gq, sgrad,
                                  workspace, L, (hipStream_t)stream));
+}
+
+// ---- graphs of library calls: stream capture, instantiation, replay
+
+struct tern_graph_s {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+int tern_graph_begin(void *stream) {
+    if (!stream) return TERN_ERR_NULL;
+    // thread-local mode: calls of other threads are not recorded and cannot
+    // invalidate this capture
+    return hip_status(hipStreamBeginCapture((hipStream_t)stream, hipStreamCaptureModeThreadLocal));
+}
+
+int tern_graph_end(void *stream, tern_graph_t *graph) {
+    if (!graph) return TERN_ERR_NULL;
+    *graph = nullptr;
+    if (!stream) return TERN_ERR_NULL;
+    hipGraph_t g = nullptr;
+    if (hipStreamEndCapture((hipStream_t)stream, &g) != hipSuccess || !g) {
+        if (g) (void)hipGraphDestroy(g);
+        return TERN_ERR_HIP;
+    }
+    hipGraphExec_t x = nullptr;
+    if (hipGraphInstantiate(&x, g, nullptr, nullptr, 0) != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        return TERN_ERR_HIP;
+    }
+    tern_graph_s *h = new (std::nothrow) tern_graph_s{g, x};
+    if (!h) {
+        (void)hipGraphExecDestroy(x);
+        (void)hipGraphDestroy(g);
+        return TERN_ERR_HIP;
+    }
+    *graph = h;
+    return TERN_OK;
+}
+
+int tern_graph_launch(tern_graph_t graph, void *stream) {
+    if (!graph) return TERN_ERR_NULL;
+    return hip_status(hipGraphLaunch(graph->exec, (hipStream_t)stream));
+}
+
+int tern_graph_destroy(tern_graph_t graph) {
+    if (!graph) return TERN_OK;
+    const hipError_t e1 = hipGraphExecDestroy(graph->exec);
+    const hipError_t e2 = hipGraphDestroy(graph->graph);
+    delete graph;
+    return e1 == hipSuccess && e2 == hipSuccess ? TERN_OK : TERN_ERR_HIP;
 }
 
 }  // extern "C"

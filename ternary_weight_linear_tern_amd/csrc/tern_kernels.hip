@@ -1497,13 +1497,19 @@ void gemm_rd_kernel(GemmArgs g) {
 // Small kernels
 // ---------------------------------------------------------------------------
 
-// Ternarise and pack: one thread per packed word (16 codes of one row).
+// Ternarise and pack: one thread per packed word (16 codes of one row); the
+// threads past the canonical words zero the padding up to the first copy.
 template <bool VEC>
 __global__ __launch_bounds__(256) void materialize_kernel(const int8_t *__restrict__ q, int64_t out,
                                                           int64_t wpr, int theta,
-                                                          uint32_t *__restrict__ packed, int64_t nwords) {
+                                                          uint32_t *__restrict__ packed, int64_t nwords,
+                                                          int64_t nfill) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= nwords) return;
+    if (i >= nfill) return;
+    if (i >= nwords) {   // alignment padding before the fragment-ordered copies
+        packed[i] = 0u;
+        return;
+    }
     const int64_t r = i / wpr, wc = i - r * wpr;
     const int8_t *row = q + r * out + wc * 16;
     uint32_t word = 0;
@@ -1657,11 +1663,14 @@ hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int thet
     const int64_t wpr = cdiv(out, 16);
     const int64_t nwords = in * wpr;
     if (nwords <= 0) return hipSuccess;
-    const dim3 grid((unsigned)cdiv(nwords, 256)), block(256);
+    const int64_t nfill = packed_layout(in, out).fwd_off;   // canonical words + padding
+    const dim3 grid((unsigned)cdiv(nfill, 256)), block(256);
     if (vec)
-        hipLaunchKernelGGL((dev::materialize_kernel<true>), grid, block, 0, st, q, out, wpr, theta, packed, nwords);
+        hipLaunchKernelGGL((dev::materialize_kernel<true>), grid, block, 0, st, q, out, wpr, theta, packed, nwords,
+                           nfill);
     else
-        hipLaunchKernelGGL((dev::materialize_kernel<false>), grid, block, 0, st, q, out, wpr, theta, packed, nwords);
+        hipLaunchKernelGGL((dev::materialize_kernel<false>), grid, block, 0, st, q, out, wpr, theta, packed, nwords,
+                           nfill);
     return hipGetLastError();
 }
 

@@ -157,3 +157,15 @@ def test_workspace_bytes(L):
             # always room for at least one row of sgrad partials, 256-byte granular
             assert w >= 4 * o and w % 256 == 0, (T, i, o, dt, w)
             assert tl.tern_linear_bwd_workspace_bytes(T, i, o, dt) == w  # pure function
+
+
+def test_graph_calls_reject_missing_handles(L):
+    """The graph calls refuse NULL streams and handles before any HIP call
+    (NULL is the legacy default stream, which cannot record)."""
+    h = ctypes.c_void_p(1234)
+    assert L.tern_graph_begin(None) == NULL
+    assert L.tern_graph_end(None, ctypes.byref(h)) == NULL
+    assert h.value is None, "a failed tern_graph_end must leave a NULL handle"
+    assert L.tern_graph_end(P(0x1000), None) == NULL
+    assert L.tern_graph_launch(None, P(0x1000)) == NULL
+    assert L.tern_graph_destroy(None) == OK

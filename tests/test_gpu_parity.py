@@ -295,6 +295,23 @@ def test_fragment_copies(o, n_in, n_out):
     assert np.array_equal(got[fwd_off + fwd.size:], dxc), "dX copy differs"
 
 
+@pytest.mark.parametrize("n_in,n_out", [(264, 520), (3, 24), (136, 1032)])
+def test_materialize_writes_every_word(n_in, n_out):
+    """Every word of the handle is written, the alignment padding between the
+    canonical matrix and the copies included: handles that start as all-zero
+    and all-one bits end up identical."""
+    log(f"materialize fills the handle in={n_in} out={n_out}")
+    q = to_dev(synth.int8_uniform(synth.stream_seed(7, n_in, n_out, 0), (n_in, n_out), -7, 7))
+    a = tl.empty_packed(n_in, n_out)
+    b = tl.empty_packed(n_in, n_out)
+    a.fill_(0)
+    b.fill_(-1)
+    tl.tern_materialize(q, 2, a)
+    tl.tern_materialize(q, 2, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "some handle words keep their previous contents"
+
+
 # ---------------------------------------------------------------------------
 # properties
 # ---------------------------------------------------------------------------
