@@ -78,9 +78,7 @@ int tern_materialize(const int8_t *q, int64_t in, int64_t out, int32_t theta, ui
     if (ranges_overlap(q, qb, tern_packed, pb)) return TERN_ERR_ALIAS;
     // the 16-byte vector path needs every row of q 16-byte aligned
     const bool vec = out % 16 == 0 && aligned16(q);
-    hipError_t e = launch_materialize(q, in, out, theta, vec, tern_packed, (hipStream_t)stream);
-    if (e == hipSuccess) e = launch_derive(tern_packed, in, out, (hipStream_t)stream);
-    return hip_status(e);
+    return hip_status(launch_materialize(q, in, out, theta, vec, tern_packed, (hipStream_t)stream));
 }
 
 int tern_linear_fwd(const void *X, int32_t act_dtype, const uint32_t *tern_packed, const float *scale,

@@ -27,10 +27,10 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStream_t st);
+// The whole packed handle (canonical words, padding, both fragment-ordered
+// copies; see PackedLayout) from q in one launch.
 hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int theta, bool vec,
                               uint32_t *packed, hipStream_t st);
-// Fragment-ordered copies of the canonical packed words (see PackedLayout).
-hipError_t launch_derive(uint32_t *packed, int64_t in, int64_t out, hipStream_t st);
 hipError_t launch_dw_reduce(const float *ws, int splits, const float *scale, const uint32_t *packed,
                             int64_t in, int64_t out, float *gq, float *part, hipStream_t st);
 hipError_t launch_sgrad_reduce(const float *part, int64_t nparts, int64_t out, float *sgrad,

@@ -1072,27 +1072,58 @@ void gemm_dw_kernel(GemmArgs g) {
 // pair of MFMA operand dword j in one instruction.  Values beyond the matrix
 // are 0.
 // ---------------------------------------------------------------------------
-// One workgroup writes D_G chunks of one tile of a copy.  Both copies read a
-// block of the canonical words staged in LDS: for the dX operand, the tile's
-// 256 rows m = r x the chunks' 2 D_G words of columns k = c; for the forward
-// operand, the chunks' 32 D_G rows k = r x the tile's 16 words of columns m = c.
+// 16 int8 of row r of q from column 16 wc (fewer at a ragged row end) ->
+// one canonical word: code of column 16 wc + j at bits 2j, 01 = +1 (q >= theta),
+// 11 = -1 (q <= -theta), 00 otherwise.  VEC: the 16 bytes are one aligned load.
+template <bool VEC>
+__device__ __forceinline__ uint32_t tern_word(const int8_t *__restrict__ q, int64_t out, int theta, int64_t r,
+                                              int64_t wc) {
+    const int8_t *row = q + r * out + wc * 16;
+    uint32_t word = 0;
+    if constexpr (VEC) {
+        const u32x4 v = *(const u32x4 *)row;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            const int b = (int)(int8_t)((v[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+            const uint32_t code = b >= theta ? 1u : (b <= -theta ? 3u : 0u);
+            word |= code << (2 * j);
+        }
+    } else {
+        const int64_t nc = out - wc * 16;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            if (j < nc) {
+                const int b = row[j];
+                const uint32_t code = b >= theta ? 1u : (b <= -theta ? 3u : 0u);
+                word |= code << (2 * j);
+            }
+        }
+    }
+    return word;
+}
+
+// One workgroup writes D_G chunks of one tile of a copy.  It first builds, in
+// LDS, the canonical words of the block of q it needs: for the dX operand, the
+// tile's 256 rows m = r x the chunks' 2 D_G words of columns k = c; for the
+// forward operand, the chunks' 32 D_G rows k = r x the tile's 16 words of
+// columns m = c.
 constexpr int D_G = 2;   // chunks per workgroup
-template <bool DXOP>
-__global__ __launch_bounds__(256) void derive_kernel(const uint32_t *__restrict__ canon, int64_t in,
-                                                     int64_t out, int64_t wpr, int64_t nch,
-                                                     uint32_t *__restrict__ frag) {
+constexpr int D_LDS = 256 * (2 * D_G + 1);   // words of the larger block (+1 word per row)
+template <bool VEC, bool DXOP>
+__device__ __forceinline__ void derive_block(const int8_t *__restrict__ q, int64_t in, int64_t out, int64_t wpr,
+                                             int theta, int64_t nch, int64_t tile, int64_t sg,
+                                             uint32_t *__restrict__ frag, uint32_t *blk) {
     // block rows x words (+1 word per row against bank conflicts)
-    constexpr int BR = DXOP ? 256 : 32 * D_G, BW = DXOP ? 2 * D_G : 16;
-    __shared__ uint32_t blk[BR][BW + 1];
+    constexpr int BR = DXOP ? 256 : 32 * D_G, BW = DXOP ? 2 * D_G : 16, LD = BW + 1;
+    static_assert(BR * LD <= D_LDS, "block does not fit");
     const int t = threadIdx.x;
-    const int64_t tile = blockIdx.x, sg = blockIdx.y;
-    const int64_t r0 = DXOP ? tile * 256 : sg * (32 * D_G);   // first canonical row
-    const int64_t w0 = DXOP ? sg * (2 * D_G) : tile * 16;     // first canonical word column
+    const int64_t r0 = DXOP ? tile * 256 : sg * (32 * D_G);   // first row of q
+    const int64_t w0 = DXOP ? sg * (2 * D_G) : tile * 16;     // first word column
 #pragma unroll
     for (int idx = t; idx < BR * BW; idx += 256) {
         const int row = idx / BW, w = idx % BW;
         const int64_t r = r0 + row, wc = w0 + w;
-        blk[row][w] = (r < in && wc < wpr) ? canon[r * wpr + wc] : 0u;
+        blk[row * LD + w] = (r < in && wc < wpr) ? tern_word<VEC>(q, out, theta, r, wc) : 0u;
     }
     __syncthreads();
     const int64_t M = DXOP ? in : out, K = DXOP ? out : in;
@@ -1112,7 +1143,7 @@ __global__ __launch_bounds__(256) void derive_kernel(const uint32_t *__restrict_
                     const int kl = sl * 32 + kk * 16 + (lane >> 5) * 8 + e;   // k within the group
                     if (sg * (32 * D_G) + kl >= K) continue;
                     const int br = DXOP ? ml : kl, bc = DXOP ? kl : ml;    // block row, block column
-                    const uint32_t code = (blk[br][bc >> 4] >> (2 * (bc & 15))) & 3u;
+                    const uint32_t code = (blk[br * LD + (bc >> 4)] >> (2 * (bc & 15))) & 3u;
                     const uint32_t nz = code & 1u, neg = (code >> 1) & nz;
                     word |= ((nz << 1) | (neg << 3)) >> kk << (4 * e);
                 }
@@ -1497,42 +1528,40 @@ void gemm_rd_kernel(GemmArgs g) {
 // Small kernels
 // ---------------------------------------------------------------------------
 
-// Ternarise and pack: one thread per packed word (16 codes of one row); the
-// threads past the canonical words zero the padding up to the first copy.
+// Ternarise and pack, one launch for the whole handle.  Blocks [0, nb_canon):
+// one thread per canonical word (16 codes of one row), and past the canonical
+// words the zero padding up to the first copy.  The next nb_fwd blocks write
+// the forward operand's copy, the rest the dX operand's copy; each of those
+// ternarises the block of q it needs itself, so no block waits for another.
+struct MatGrid {
+    int64_t nwords, nfill;      // canonical words; words up to the forward copy
+    int64_t nchf, nchd;         // 32-K chunks of the forward / dX copy
+    int64_t fwd_off, dx_off;    // word offsets of the copies
+    int nb_canon, ngf, nb_fwd, ngd;   // blocks: canonical part; chunk groups and blocks of the copies
+};
 template <bool VEC>
-__global__ __launch_bounds__(256) void materialize_kernel(const int8_t *__restrict__ q, int64_t out,
-                                                          int64_t wpr, int theta,
-                                                          uint32_t *__restrict__ packed, int64_t nwords,
-                                                          int64_t nfill) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= nfill) return;
-    if (i >= nwords) {   // alignment padding before the fragment-ordered copies
-        packed[i] = 0u;
+__global__ __launch_bounds__(256) void materialize_kernel(const int8_t *__restrict__ q, int64_t in, int64_t out,
+                                                          int64_t wpr, int theta, uint32_t *__restrict__ packed,
+                                                          MatGrid mg) {
+    __shared__ uint32_t blk[D_LDS];
+    int b = blockIdx.x;
+    if (b < mg.nb_canon) {
+        const int64_t i = (int64_t)b * 256 + threadIdx.x;
+        if (i < mg.nwords) {
+            const int64_t r = i / wpr;
+            packed[i] = tern_word<VEC>(q, out, theta, r, i - r * wpr);
+        } else if (i < mg.nfill) {
+            packed[i] = 0u;   // alignment padding before the fragment-ordered copies
+        }
         return;
     }
-    const int64_t r = i / wpr, wc = i - r * wpr;
-    const int8_t *row = q + r * out + wc * 16;
-    uint32_t word = 0;
-    if constexpr (VEC) {
-        const u32x4 v = *(const u32x4 *)row;
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-            const int b = (int)(int8_t)((v[j >> 2] >> (8 * (j & 3))) & 0xFFu);
-            const uint32_t code = b >= theta ? 1u : (b <= -theta ? 3u : 0u);
-            word |= code << (2 * j);
-        }
-    } else {
-        const int64_t nc = out - wc * 16;
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-            if (j < nc) {
-                const int b = row[j];
-                const uint32_t code = b >= theta ? 1u : (b <= -theta ? 3u : 0u);
-                word |= code << (2 * j);
-            }
-        }
+    b -= mg.nb_canon;
+    if (b < mg.nb_fwd) {
+        derive_block<VEC, false>(q, in, out, wpr, theta, mg.nchf, b / mg.ngf, b % mg.ngf, packed + mg.fwd_off, blk);
+        return;
     }
-    packed[i] = word;
+    b -= mg.nb_fwd;
+    derive_block<VEC, true>(q, in, out, wpr, theta, mg.nchd, b / mg.ngd, b % mg.ngd, packed + mg.dx_off, blk);
 }
 
 // Split-K finish of dW: G = sum over splits (ascending), gq = G * scale, and
@@ -1660,30 +1689,30 @@ hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStrea
 
 hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int theta, bool vec,
                               uint32_t *packed, hipStream_t st) {
-    const int64_t wpr = cdiv(out, 16);
-    const int64_t nwords = in * wpr;
-    if (nwords <= 0) return hipSuccess;
-    const int64_t nfill = packed_layout(in, out).fwd_off;   // canonical words + padding
-    const dim3 grid((unsigned)cdiv(nfill, 256)), block(256);
-    if (vec)
-        hipLaunchKernelGGL((dev::materialize_kernel<true>), grid, block, 0, st, q, out, wpr, theta, packed, nwords,
-                           nfill);
-    else
-        hipLaunchKernelGGL((dev::materialize_kernel<false>), grid, block, 0, st, q, out, wpr, theta, packed, nwords,
-                           nfill);
-    return hipGetLastError();
-}
-
-hipError_t launch_derive(uint32_t *packed, int64_t in, int64_t out, hipStream_t st) {
     const PackedLayout L = packed_layout(in, out);
     if (L.total == 0) return hipSuccess;
     const int64_t wpr = cdiv(out, 16);
+    dev::MatGrid mg;
+    mg.nwords = in * wpr;
+    mg.nfill = L.fwd_off;
     // forward operand: tiles over out, chunks over in; dX operand: the reverse
-    const int64_t nchf = cdiv(in, kFragChunk), nchd = cdiv(out, kFragChunk);
-    hipLaunchKernelGGL((dev::derive_kernel<false>), dim3((unsigned)cdiv(out, 256), (unsigned)cdiv(nchf, dev::D_G)),
-                       dim3(256), 0, st, packed, in, out, wpr, nchf, packed + L.fwd_off);
-    hipLaunchKernelGGL((dev::derive_kernel<true>), dim3((unsigned)cdiv(in, 256), (unsigned)cdiv(nchd, dev::D_G)),
-                       dim3(256), 0, st, packed, in, out, wpr, nchd, packed + L.dx_off);
+    mg.nchf = cdiv(in, kFragChunk);
+    mg.nchd = cdiv(out, kFragChunk);
+    mg.fwd_off = L.fwd_off;
+    mg.dx_off = L.dx_off;
+    const int64_t nb_canon = cdiv(mg.nfill, 256), ngf = cdiv(mg.nchf, dev::D_G), ngd = cdiv(mg.nchd, dev::D_G);
+    const int64_t nb_fwd = cdiv(out, 256) * ngf, nb_dx = cdiv(in, 256) * ngd;
+    const int64_t blocks = nb_canon + nb_fwd + nb_dx;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    mg.nb_canon = (int)nb_canon;
+    mg.ngf = (int)ngf;
+    mg.nb_fwd = (int)nb_fwd;
+    mg.ngd = (int)ngd;
+    const dim3 grid((unsigned)blocks), block(256);
+    if (vec)
+        hipLaunchKernelGGL((dev::materialize_kernel<true>), grid, block, 0, st, q, in, out, wpr, theta, packed, mg);
+    else
+        hipLaunchKernelGGL((dev::materialize_kernel<false>), grid, block, 0, st, q, in, out, wpr, theta, packed, mg);
     return hipGetLastError();
 }
 
