@@ -8,8 +8,9 @@ HBM.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large] [--launch eager|graph]
 
 By default one step's library calls are recorded as a HIP graph (tern_graph_*)
-and its replays are timed (--launch eager times the calls themselves); the
-per-part times always come from eager calls, timed with events between them.
+whose dW launches form a branch of their own (--streams), and its replays are
+timed (--launch eager times the calls themselves); the per-part times always
+come from eager calls, timed with events between them.
 """
 from __future__ import annotations
 
@@ -43,6 +44,10 @@ def parse():
     ap.add_argument("--workload", default="large", choices=["rwkv_small", "mid", "large", "largest"])
     ap.add_argument("--launch", default="graph", choices=["eager", "graph"],
                     help="graph (default): time replays of one recorded step; eager: time the calls")
+    ap.add_argument("--streams", type=int, default=2, choices=[1, 2, 3],
+                    help="graph branches of the recorded step: 1 = one chain; 2 = dW of every projection on "
+                         "its own branch; 3 = dX and dW each on their own branch (each branch waits only for "
+                         "its projection's materialize)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="oracle sample: token rows per projection")
     ap.add_argument("--cpu-cols", type=int, default=768, help="oracle sample: output columns per projection")
@@ -129,14 +134,40 @@ def main():
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / a.steps
 
+    def record_dag(streams):
+        """The step as a DAG: every projection's forward, dX and dW depend only
+        on its materialize.  Branch streams join the recording through events
+        recorded on the first stream and rejoin it at the end."""
+        s0 = streams[0]
+        sdx, sdw = streams[1 if len(streams) == 3 else 0], streams[-1]
+
+        def fork(src, dst):
+            e = torch.cuda.Event()
+            e.record(src)
+            dst.wait_event(e)
+
+        for sx in streams[1:]:
+            fork(s0, sx)
+        for d in projs:
+            tl.tern_materialize(d["q"], d["theta"], d["packed"], s0)
+            for sx in streams[1:]:
+                fork(s0, sx)
+            tl.tern_linear_fwd(d["X"], d["packed"], d["scale"], d["Y"], s0)
+            tl.tern_linear_bwd_dx(d["dY"], d["packed"], d["scale"], d["dX"], stream=sdx)
+            tl.tern_linear_bwd_dw(d["X"], d["dY"], d["packed"], d["scale"], d["gq"], d["sgrad"], d["ws"], sdw)
+        for sx in streams[1:]:
+            fork(sx, s0)
+
     eager_ms_per_step = ms_per_step
     if a.launch == "graph":
-        # one step recorded on a side stream, replayed as one launch per step
+        # one step recorded on a side stream (plus branch streams), replayed as
+        # one launch per step
         gs = torch.cuda.Stream()
         gs.wait_stream(stream)
+        branches = [torch.cuda.Stream() for _ in range(a.streams - 1)]
         tl.tern_graph_begin(gs)
         try:
-            step(stream=gs)
+            record_dag([gs] + branches)
         finally:
             graph = tl.tern_graph_end(gs)
         try:
@@ -217,7 +248,7 @@ def main():
         "config": {"workload": w.name, "T": w.T,
                    "projections": [[n, i, o] for n, i, o in w.projs],
                    "theta": w.theta, "q": w.q_law, "scale": w.scale_law, "act": w.act,
-                   "launch": "hipgraph" if a.launch == "graph" else "eager"},
+                   "launch": f"hipgraph, {a.streams} branch(es)" if a.launch == "graph" else "eager"},
         "eager_ms_per_step": round(eager_ms_per_step, 4),
         "tokens_per_s": round(tokens_per_s, 1),
         "mfma_frac": round(tflops / peak, 4),
