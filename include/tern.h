@@ -159,6 +159,42 @@ int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype,
                        void *stream);
 
 /*
+ * Accumulating variants of the backward.  dX += adds one projection's input
+ * gradient to a buffer that already holds others (an input feeding several
+ * projections).  gq, sgrad += alpha * ... sums weight-side gradients over
+ * micro-batches: the page's trainer averages the gradients of B > 1 sequences,
+ * which alpha = 1/B expresses.
+ *
+ * tern_linear_bwd_dx_acc -- dX [T, in] (fp32, read and written) +=
+ *   dY . W_eff^T, with the same arithmetic as tern_linear_bwd_dx; the sum is
+ *   added to the old value in fp32.  Same argument rules; no workspace.  With
+ *   T, in or out 0 nothing is added.
+ *   Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, HIP.
+ *
+ * tern_linear_bwd_acc_workspace_bytes -- device workspace (bytes) that
+ *   tern_linear_bwd_dw_acc needs (at least that of tern_linear_bwd: G always
+ *   goes through the workspace here).  0 for invalid sizes.
+ *
+ * tern_linear_bwd_dw_acc -- with G = X^T . dY as in tern_linear_bwd:
+ *   gq[r, c] += alpha * (G[r, c] * scale[c])   (fp32, read and written),
+ *   sgrad[c] += alpha * sum_r G[r, c] * tern[r, c]   (the sum in the same
+ *   fixed order, added to the old value in f64, then rounded to fp32).
+ *   workspace: at least tern_linear_bwd_acc_workspace_bytes(...) bytes.
+ *   alpha: any float (1 adds, 1/B averages B micro-batches).  With T = 0
+ *   nothing is added.
+ *   Errors: NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, ALIAS, HIP.
+ */
+int tern_linear_bwd_dx_acc(const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
+                           const float *scale, int64_t T, int64_t in, int64_t out,
+                           float *dX, void *stream);
+size_t tern_linear_bwd_acc_workspace_bytes(int64_t T, int64_t in, int64_t out, int32_t act_dtype);
+int tern_linear_bwd_dw_acc(const void *X, const void *dY, int32_t act_dtype,
+                           const uint32_t *tern_packed, const float *scale,
+                           int64_t T, int64_t in, int64_t out, float alpha,
+                           float *gq, float *sgrad, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
  * Graphs of library calls.  The page's trainer launches every glue kernel and
  * GEMM of a step separately and notes that it is launch-bound; a caller can
  * instead record any sequence of the calls above (for example materialize,

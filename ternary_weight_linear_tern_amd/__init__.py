@@ -40,6 +40,10 @@ SIGNATURES = {
     "tern_linear_bwd_dx": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp]),
     "tern_linear_bwd_dw": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
                                           _vp, _sz, _vp]),
+    "tern_linear_bwd_dx_acc": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "tern_linear_bwd_acc_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "tern_linear_bwd_dw_acc": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, ctypes.c_float,
+                                              _vp, _vp, _vp, _sz, _vp]),
     "tern_graph_begin": (ctypes.c_int, [_vp]),
     "tern_graph_end": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
     "tern_graph_launch": (ctypes.c_int, [_vp, _vp]),
@@ -174,6 +178,35 @@ def tern_linear_bwd_dw(X, dY, tern_packed, scale, gq, sgrad, workspace, stream=N
     _check("tern_linear_bwd_dw", rc)
 
 
+def tern_linear_bwd_dx_acc(dY, tern_packed, scale, dX, n_in: int | None = None, stream=None) -> None:
+    """dX (fp32) += dY . (scale * tern)^T."""
+    T, n_out = dY.shape
+    n_in = dX.shape[1] if n_in is None else n_in
+    if dX.dtype != torch.float32:
+        raise TypeError("dX must be float32")
+    rc = lib().tern_linear_bwd_dx_acc(_ptr(dY), _act_code(dY), _ptr(tern_packed), _ptr(scale), T, n_in, n_out,
+                                      _ptr(dX), _stream(stream))
+    _check("tern_linear_bwd_dx_acc", rc)
+
+
+def tern_linear_bwd_acc_workspace_bytes(T: int, n_in: int, n_out: int, act_dtype) -> int:
+    code = act_dtype if isinstance(act_dtype, int) else (
+        TERN_BF16 if act_dtype == torch.bfloat16 else TERN_F32)
+    return int(lib().tern_linear_bwd_acc_workspace_bytes(T, n_in, n_out, code))
+
+
+def tern_linear_bwd_dw_acc(X, dY, tern_packed, scale, gq, sgrad, workspace, alpha: float = 1.0,
+                           stream=None) -> None:
+    """gq += alpha * G * scale, sgrad += alpha * sum_r G * tern (G = X^T . dY)."""
+    T, n_in = X.shape
+    n_out = scale.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().tern_linear_bwd_dw_acc(_ptr(X), _ptr(dY), _act_code(X), _ptr(tern_packed), _ptr(scale), T,
+                                      n_in, n_out, float(alpha), _ptr(gq), _ptr(sgrad), _ptr(workspace),
+                                      ws_bytes, _stream(stream))
+    _check("tern_linear_bwd_dw_acc", rc)
+
+
 def tern_graph_begin(stream) -> None:
     """Start recording the library calls enqueued on `stream` (a created
     torch.cuda.Stream or raw handle, not the legacy default stream)."""
@@ -213,6 +246,8 @@ def packed_canonical(tern_packed: torch.Tensor, n_in: int, n_out: int) -> torch.
     return tern_packed.reshape(-1)[: n_in * wpr].view(n_in, wpr)
 
 
-def empty_workspace(T: int, n_in: int, n_out: int, act_dtype, device="cuda") -> torch.Tensor:
-    nbytes = tern_linear_bwd_workspace_bytes(T, n_in, n_out, act_dtype)
+def empty_workspace(T: int, n_in: int, n_out: int, act_dtype, device="cuda", acc: bool = False) -> torch.Tensor:
+    """Workspace of tern_linear_bwd / tern_linear_bwd_dw (acc: of tern_linear_bwd_dw_acc)."""
+    q = tern_linear_bwd_acc_workspace_bytes if acc else tern_linear_bwd_workspace_bytes
+    nbytes = q(T, n_in, n_out, act_dtype)
     return torch.empty((max(nbytes, 16) // 16, 16), dtype=torch.uint8, device=device)

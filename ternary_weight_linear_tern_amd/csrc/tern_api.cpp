@@ -127,11 +127,12 @@ size_t tern_linear_bwd_workspace_bytes(int64_t T, int64_t in, int64_t out, int32
 namespace {
 
 // Shared argument checks of the backward entry points.  Sizes of absent parts
-// (want_dx / want_dw false) are not checked.
+// (want_dx / want_dw false) are not checked; acc sizes the workspace for the
+// accumulating dW variant.
 int check_bwd(const void *X, const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
               const float *scale, int64_t T, int64_t in, int64_t out, void *dX, int32_t dx_dtype,
               float *gq, float *sgrad, void *workspace, size_t workspace_bytes, bool want_dx,
-              bool want_dw, BwdLayout &L) {
+              bool want_dw, bool acc, BwdLayout &L) {
     int rc = validate_shape(T, in, out);
     if (rc) return rc;
     if (!act_ok(act_dtype) || (want_dx && dx_dtype != TERN_F32)) return TERN_ERR_DTYPE;
@@ -142,7 +143,7 @@ int check_bwd(const void *X, const void *dY, int32_t act_dtype, const uint32_t *
     const size_t sb = (size_t)out * 4;
     const size_t dxb = want_dx ? (size_t)T * in * 4 : 0;
     const size_t gqb = want_dw ? (size_t)in * out * 4 : 0, sgb = want_dw ? (size_t)out * 4 : 0;
-    L = plan_bwd(T, in, out, bf);
+    L = plan_bwd(T, in, out, bf, acc);
     const size_t wsb = want_dw ? L.total : 0;
     if ((xb && !X) || (dyb && !dY) || (pb && !tern_packed) || (sb && !scale) || (dxb && !dX) ||
         (gqb && !gq) || (sgb && !sgrad))
@@ -171,12 +172,14 @@ GemmArgs args_for(const GemmPlan &p, const uint32_t *tern_packed, const float *s
     return a;
 }
 
+// acc: dX += dY . W_eff^T instead of dX = ...
 hipError_t enqueue_dx(const void *dY, bool bf, const uint32_t *tern_packed, const float *scale, int64_t T,
-                      int64_t in, int64_t out, void *dX, const BwdLayout &L, hipStream_t st) {
+                      int64_t in, int64_t out, void *dX, const BwdLayout &L, hipStream_t st, bool acc = false) {
     const size_t dxb = (size_t)T * in * 4;
     if (dxb == 0) return hipSuccess;
-    if (out == 0) return launch_zero(dX, dxb, st);  // empty sum
+    if (out == 0) return acc ? hipSuccess : launch_zero(dX, dxb, st);  // empty sum
     GemmArgs a = args_for(L.dx, tern_packed, scale, T, in, out);
+    a.acc = acc;
     a.frag = tern_packed + packed_layout(in, out).dx_off;
     a.nch = (int)((out + kFragChunk - 1) / kFragChunk);
     a.act0 = dY;
@@ -184,9 +187,12 @@ hipError_t enqueue_dx(const void *dY, bool bf, const uint32_t *tern_packed, cons
     return launch_gemm(L.dx, bf, a, st);
 }
 
+// acc: gq += alpha * G * scale and sgrad += alpha * sum_r G * tern; G then
+// always goes through the workspace (L planned with acc).
 hipError_t enqueue_dw(const void *X, const void *dY, bool bf, const uint32_t *tern_packed, const float *scale,
                       int64_t T, int64_t in, int64_t out, float *gq, float *sgrad, void *workspace,
-                      const BwdLayout &L, hipStream_t st) {
+                      const BwdLayout &L, hipStream_t st, bool acc = false, float alpha = 1.0f) {
+    if (acc && (T == 0 || in == 0 || out == 0)) return hipSuccess;   // nothing to add
     if (T == 0 || in == 0 || out == 0) {
         // G is an empty sum (T == 0) or empty: gq = 0 and sgrad = 0 where they exist
         hipError_t e = hipSuccess;
@@ -200,18 +206,19 @@ hipError_t enqueue_dw(const void *X, const void *dY, bool bf, const uint32_t *te
     a.act0 = X;
     a.act1 = dY;
     a.part = part;
+    a.acc = acc;
     hipError_t e;
-    if (L.dw.splits > 1) {
+    if (L.dw.splits > 1 || acc) {
         float *ws = (float *)((char *)workspace + L.ws_off);
         a.out_ptr = ws;
         e = launch_gemm(L.dw, bf, a, st);
         if (e == hipSuccess)
-            e = launch_dw_reduce(ws, (int)L.dw.splits, scale, tern_packed, in, out, gq, part, st);
+            e = launch_dw_reduce(ws, (int)L.dw.splits, scale, tern_packed, in, out, gq, part, acc, alpha, st);
     } else {
         a.out_ptr = gq;
         e = launch_gemm(L.dw, bf, a, st);
     }
-    if (e == hipSuccess) e = launch_sgrad_reduce(part, L.part_rows, out, sgrad, st);
+    if (e == hipSuccess) e = launch_sgrad_reduce(part, L.part_rows, out, sgrad, acc, alpha, st);
     return e;
 }
 
@@ -222,7 +229,7 @@ int tern_linear_bwd(const void *X, const void *dY, int32_t act_dtype, const uint
                     float *gq, float *sgrad, void *workspace, size_t workspace_bytes, void *stream) {
     BwdLayout L;
     int rc = check_bwd(X, dY, act_dtype, tern_packed, scale, T, in, out, dX, dx_dtype, gq, sgrad,
-                       workspace, workspace_bytes, true, true, L);
+                       workspace, workspace_bytes, true, true, false, L);
     if (rc) return rc;
     const bool bf = act_dtype == TERN_BF16;
     hipStream_t st = (hipStream_t)stream;
@@ -235,7 +242,7 @@ int tern_linear_bwd_dx(const void *dY, int32_t act_dtype, const uint32_t *tern_p
                        int64_t T, int64_t in, int64_t out, void *dX, int32_t dx_dtype, void *stream) {
     BwdLayout L;
     int rc = check_bwd(nullptr, dY, act_dtype, tern_packed, scale, T, in, out, dX, dx_dtype, nullptr,
-                       nullptr, nullptr, 0, true, false, L);
+                       nullptr, nullptr, 0, true, false, false, L);
     if (rc) return rc;
     return hip_status(enqueue_dx(dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, dX, L,
                                  (hipStream_t)stream));
@@ -246,10 +253,38 @@ int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype, const u
                        void *workspace, size_t workspace_bytes, void *stream) {
     BwdLayout L;
     int rc = check_bwd(X, dY, act_dtype, tern_packed, scale, T, in, out, nullptr, TERN_F32, gq, sgrad,
-                       workspace, workspace_bytes, false, true, L);
+                       workspace, workspace_bytes, false, true, false, L);
     if (rc) return rc;
     return hip_status(enqueue_dw(X, dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, gq, sgrad,
                                  workspace, L, (hipStream_t)stream));
+}
+
+// ---- accumulating variants
+
+size_t tern_linear_bwd_acc_workspace_bytes(int64_t T, int64_t in, int64_t out, int32_t act_dtype) {
+    if (validate_shape(T, in, out) != TERN_OK || !act_ok(act_dtype)) return 0;
+    return plan_bwd(T, in, out, act_dtype == TERN_BF16, true).total;
+}
+
+int tern_linear_bwd_dx_acc(const void *dY, int32_t act_dtype, const uint32_t *tern_packed, const float *scale,
+                           int64_t T, int64_t in, int64_t out, float *dX, void *stream) {
+    BwdLayout L;
+    int rc = check_bwd(nullptr, dY, act_dtype, tern_packed, scale, T, in, out, dX, TERN_F32, nullptr, nullptr,
+                       nullptr, 0, true, false, false, L);
+    if (rc) return rc;
+    return hip_status(enqueue_dx(dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, dX, L,
+                                 (hipStream_t)stream, true));
+}
+
+int tern_linear_bwd_dw_acc(const void *X, const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
+                           const float *scale, int64_t T, int64_t in, int64_t out, float alpha, float *gq,
+                           float *sgrad, void *workspace, size_t workspace_bytes, void *stream) {
+    BwdLayout L;
+    int rc = check_bwd(X, dY, act_dtype, tern_packed, scale, T, in, out, nullptr, TERN_F32, gq, sgrad, workspace,
+                       workspace_bytes, false, true, true, L);
+    if (rc) return rc;
+    return hip_status(enqueue_dw(X, dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, gq, sgrad,
+                                 workspace, L, (hipStream_t)stream, true, alpha));
 }
 
 // ---- graphs of library calls: stream capture, instantiation, replay

@@ -24,6 +24,7 @@ struct GemmArgs {
     int in, out, wpr, T;
     int y_bf16;
     int nch;                 // FWD / DX: chunks of 32 K per tile in the fragment copy
+    int acc;                 // DX: add to the existing dX; DW: raw G into out_ptr even with one split
 };
 
 hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStream_t st);
@@ -31,9 +32,12 @@ hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStrea
 // copies; see PackedLayout) from q in one launch.
 hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int theta, bool vec,
                               uint32_t *packed, hipStream_t st);
+// acc: gq += alpha * G * scale instead of gq = G * scale
 hipError_t launch_dw_reduce(const float *ws, int splits, const float *scale, const uint32_t *packed,
-                            int64_t in, int64_t out, float *gq, float *part, hipStream_t st);
-hipError_t launch_sgrad_reduce(const float *part, int64_t nparts, int64_t out, float *sgrad,
+                            int64_t in, int64_t out, float *gq, float *part, bool acc, float alpha,
+                            hipStream_t st);
+// acc: sgrad += alpha * (sum of the partials) instead of sgrad = the sum
+hipError_t launch_sgrad_reduce(const float *part, int64_t nparts, int64_t out, float *sgrad, bool acc, float alpha,
                                hipStream_t st);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 

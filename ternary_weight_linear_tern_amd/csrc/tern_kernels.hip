@@ -580,6 +580,7 @@ void gemm_kernel(GemmArgs g) {
                                acc[fm][fn][4 * q + 3]};
                     if constexpr (MODE == MODE_FWD) v = v * sc;
                     const int64_t o = (int64_t)n * ldo + m;
+                    if (MODE == MODE_DX && g.acc) v += *(const f32x4 *)((const float *)g.out_ptr + o);
                     if (MODE == MODE_FWD && g.y_bf16) {
                         f32x2 a = {v.x, v.y}, b = {v.z, v.w};
                         u32x2 pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2)),
@@ -594,7 +595,7 @@ void gemm_kernel(GemmArgs g) {
     } else {
         // MODE_DW: C[m][n] = G[r][c] (m = r < in, n = c < out)
         float *dst = (float *)g.out_ptr;
-        if (g.splits > 1) {
+        if (g.splits > 1 || g.acc) {   // raw G of this split (sp = 0 with one split)
             dst += (int64_t)sp * g.M * g.N;
 #pragma unroll
             for (int fm = 0; fm < G::FM; fm++)
@@ -984,9 +985,10 @@ void gemm_dw_kernel(GemmArgs g) {
 #pragma unroll
         for (int fn = 0; fn < 4; fn++)
             vo[fn] = nw + fn * 32 + l32 < g.N ? (uint32_t)((4 * h * g.N + fn * 32 + l32) * 4) : OOB;
-        // One split: gq = G * scale[c] and the sgrad partial.  Several splits:
-        // the raw G partial (scale 1 makes the store exact), no sgrad partial.
-        const bool split = g.splits > 1;
+        // One split: gq = G * scale[c] and the sgrad partial.  Several splits,
+        // or accumulation: the raw G partial (scale 1 makes the store exact),
+        // no sgrad partial; dw_reduce_kernel finishes gq and the partials.
+        const bool split = g.splits > 1 || g.acc;
         // tern values of this lane's 64 rows x 4 columns, from the forward
         // fragment-ordered copy (its rows are the columns c, its K the rows r):
         // per 32-row fragment fm, the 16 bytes of each 8-row half hf hold the
@@ -1224,10 +1226,11 @@ __device__ __forceinline__ uint32_t r_scaled_pair(uint32_t v, uint32_t q) {
     return (v ^ q) & __builtin_amdgcn_perm(0u, 0u, v);
 }
 
-template <int MODE>
+template <int MODE, bool ACC = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_rd_kernel(GemmArgs g) {
     static_assert(MODE == MODE_FWD || MODE == MODE_DX, "forward and dX only");
+    static_assert(!ACC || MODE == MODE_DX, "accumulation is a dX variant");
     constexpr int ES = 2;
     // vector memory operations per chunk issue: 8 activation + 1 fragment (+ 1 scale)
     constexpr int OPS = MODE == MODE_DX ? 10 : 9;
@@ -1385,7 +1388,11 @@ void gemm_rd_kernel(GemmArgs g) {
 
     // Epilogue of tile (ctm, ctn): 64 buffer stores per wave whatever the edges
     // (out-of-range stores get an out-of-range offset), so the vmcnt arithmetic
-    // of the main loop holds.  Lane offsets cover the 4 columns n of the lane;
+    // of the main loop holds.  ACC (dX += ...): the 4 old values of each
+    // row segment are loaded first (out-of-range offsets read zero; the
+    // compiler waits for them before the add).  The main loop's waits bound the
+    // number of operations still outstanding, so the 64 extra loads only make
+    // them wait for more than needed.  Lane offsets cover the 4 columns n of the lane;
     // the row block m goes in the scalar offset.  M is a multiple of 8 and the
     // 8-row groups are wave-uniform, so the m test is scalar.
     auto epilogue = [&]() __attribute__((always_inline)) {
@@ -1418,12 +1425,21 @@ void gemm_rd_kernel(GemmArgs g) {
                 }
 #pragma unroll
                 for (int fn = 0; fn < 4; fn++) {
+                    f32x4 old[4];
+                    if constexpr (ACC) {
+#pragma unroll
+                        for (int q = 0; q < 4; q++)
+                            old[q] = __builtin_bit_cast(
+                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, mokq[q] ? vo[fn] : OOB,
+                                                                             (fm * 32 + 8 * q) * esz, 0));
+                    }
 #pragma unroll
                     for (int q = 0; q < 4; q++) {
                         const int so = (fm * 32 + 8 * q) * esz;
                         f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
                                    acc[fm][fn][4 * q + 3]};
                         if constexpr (MODE == MODE_FWD) v = v * scq[q];
+                        if constexpr (ACC) v += old[q];
                         const uint32_t off = mokq[q] ? vo[fn] : OOB;
                         if constexpr (OBF) {
                             const f32x2 a2 = {v.x, v.y}, b2 = {v.z, v.w};
@@ -1434,6 +1450,8 @@ void gemm_rd_kernel(GemmArgs g) {
                             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off, so, 0);
                         }
                     }
+                    // keep each group's loads after the previous group's stores
+                    if constexpr (ACC) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
@@ -1564,15 +1582,16 @@ __global__ __launch_bounds__(256) void materialize_kernel(const int8_t *__restri
     derive_block<VEC, true>(q, in, out, wpr, theta, mg.nchd, b / mg.ngd, b % mg.ngd, packed + mg.dx_off, blk);
 }
 
-// Split-K finish of dW: G = sum over splits (ascending), gq = G * scale, and
-// the sgrad partial of a block of kReduceRows rows (ascending r).  Each thread
+// Split-K finish of dW: G = sum over splits (ascending), gq = G * scale (acc:
+// gq + alpha * G * scale), and the sgrad partial of a block of kReduceRows rows
+// (ascending r).  Each thread
 // owns 4 consecutive columns (16-byte loads and stores); a block covers 1024
 // columns of kReduceRows rows.
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ ws, int splits,
                                                         const float *__restrict__ scale,
                                                         const uint32_t *__restrict__ packed, int in,
                                                         int out, int64_t wpr, float *__restrict__ gq,
-                                                        float *__restrict__ part) {
+                                                        float *__restrict__ part, int acc, float alpha) {
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= out) return;
     const int r0 = blockIdx.y * kReduceRows;
@@ -1584,7 +1603,9 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
         const int64_t o = (int64_t)r * out + c;
         f32x4 gv = *(const f32x4 *)(ws + o);
         for (int k = 1; k < splits; k++) gv += *(const f32x4 *)(ws + k * plane + o);
-        *(f32x4 *)(gq + o) = gv * s;
+        f32x4 t = gv * s;
+        if (acc) t = *(const f32x4 *)(gq + o) + alpha * t;
+        *(f32x4 *)(gq + o) = t;
         // the 4 codes of columns c .. c + 3 (c % 4 == 0, so one word holds them)
         const uint32_t word = packed[(int64_t)r * wpr + (c >> 4)] >> (2 * (c & 15));
         p.x += gv.x * code_to_f32(word & 3u);
@@ -1597,10 +1618,12 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
 
 // sgrad[c] = sum of the row-block partials in ascending order, in f64, as a
 // fixed two-level sum: 8 consecutive groups of blocks are each summed in
-// ascending order, then the 8 group sums in ascending order.  A block of 256
-// threads serves 32 columns.
+// ascending order, then the 8 group sums in ascending order (acc: added, times
+// alpha, to the existing sgrad in f64).  A block of 256 threads serves 32
+// columns.
 __global__ __launch_bounds__(256) void sgrad_reduce_kernel(const float *__restrict__ part, int nparts,
-                                                           int out, float *__restrict__ sgrad) {
+                                                           int out, float *__restrict__ sgrad, int acc,
+                                                           float alpha) {
     __shared__ double red[8][32];
     const int cl = threadIdx.x & 31, grp = threadIdx.x >> 5;
     const int c = blockIdx.x * 32 + cl;
@@ -1617,6 +1640,7 @@ __global__ __launch_bounds__(256) void sgrad_reduce_kernel(const float *__restri
         double s = red[0][cl];
 #pragma unroll
         for (int g2 = 1; g2 < 8; g2++) s += red[g2][cl];
+        if (acc) s = (double)sgrad[c] + (double)alpha * s;
         sgrad[c] = (float)s;
     }
 }
@@ -1661,6 +1685,8 @@ hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
             const dim3 pgrid((unsigned)(p.grid < cus ? p.grid : cus));
             if constexpr (MODE == MODE_DW)
                 hipLaunchKernelGGL(dev::gemm_dw_kernel, pgrid, block, 0, st, a);
+            else if (MODE == MODE_DX && a.acc)
+                hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE_DX, true>), pgrid, block, 0, st, a);
             else
                 hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE>), pgrid, block, 0, st, a);
             return hipGetLastError();
@@ -1717,17 +1743,20 @@ hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int thet
 }
 
 hipError_t launch_dw_reduce(const float *ws, int splits, const float *scale, const uint32_t *packed,
-                            int64_t in, int64_t out, float *gq, float *part, hipStream_t st) {
+                            int64_t in, int64_t out, float *gq, float *part, bool acc, float alpha,
+                            hipStream_t st) {
     const dim3 grid((unsigned)cdiv(out, 1024), (unsigned)cdiv(in, kReduceRows)), block(256);
     hipLaunchKernelGGL(dev::dw_reduce_kernel, grid, block, 0, st, ws, splits, scale, packed, (int)in,
-                       (int)out, cdiv(out, 16), gq, part);
+                       (int)out, cdiv(out, 16), gq, part, (int)acc, alpha);
     return hipGetLastError();
 }
 
-hipError_t launch_sgrad_reduce(const float *part, int64_t nparts, int64_t out, float *sgrad, hipStream_t st) {
+hipError_t launch_sgrad_reduce(const float *part, int64_t nparts, int64_t out, float *sgrad, bool acc, float alpha,
+                               hipStream_t st) {
     if (out <= 0) return hipSuccess;
     const dim3 grid((unsigned)cdiv(out, 32)), block(256);
-    hipLaunchKernelGGL(dev::sgrad_reduce_kernel, grid, block, 0, st, part, (int)nparts, (int)out, sgrad);
+    hipLaunchKernelGGL(dev::sgrad_reduce_kernel, grid, block, 0, st, part, (int)nparts, (int)out, sgrad,
+                       (int)acc, alpha);
     return hipGetLastError();
 }
 

@@ -100,18 +100,19 @@ GemmPlan plan_gemm(int mode, int64_t T, int64_t in, int64_t out, bool bf16) {
     return p;
 }
 
-BwdLayout plan_bwd(int64_t T, int64_t in, int64_t out, bool bf16) {
+BwdLayout plan_bwd(int64_t T, int64_t in, int64_t out, bool bf16, bool acc) {
     BwdLayout L;
     L.dx = plan_gemm(MODE_DX, T, in, out, bf16);
     L.dw = plan_gemm(MODE_DW, T, in, out, bf16);
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     if (T > 0 && in > 0 && out > 0) {
         const int64_t bm = tile_bm(L.dw.tile);
-        L.part_rows = L.dw.splits > 1 ? cdiv(in, kReduceRows) : cdiv(in, bm);
+        const bool raw = L.dw.splits > 1 || acc;   // G through the workspace and the reduce kernel
+        L.part_rows = raw ? cdiv(in, kReduceRows) : cdiv(in, bm);
         L.part_off = 0;
         L.part_bytes = al(size_t(L.part_rows) * size_t(out) * 4);
         L.ws_off = L.part_bytes;
-        L.ws_bytes = L.dw.splits > 1 ? al(size_t(L.dw.splits) * size_t(in) * size_t(out) * 4) : 0;
+        L.ws_bytes = raw ? al(size_t(L.dw.splits) * size_t(in) * size_t(out) * 4) : 0;
     }
     L.total = L.part_bytes + L.ws_bytes;
     return L;

@@ -48,7 +48,9 @@ struct BwdLayout {
     size_t total = 0;
 };
 
-BwdLayout plan_bwd(int64_t T, int64_t in, int64_t out, bool bf16);
+// acc: the accumulating dW variant, whose G always goes through the split
+// workspace (raw G, then the reduce kernel adds to gq).
+BwdLayout plan_bwd(int64_t T, int64_t in, int64_t out, bool bf16, bool acc = false);
 
 // Row-block height of the split-K reduction (and thus of its sgrad partials).
 constexpr int kReduceRows = 16;

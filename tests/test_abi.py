@@ -169,3 +169,40 @@ def test_graph_calls_reject_missing_handles(L):
     assert L.tern_graph_end(P(0x1000), None) == NULL
     assert L.tern_graph_launch(None, P(0x1000)) == NULL
     assert L.tern_graph_destroy(None) == OK
+
+
+def test_acc_variants_reject(L):
+    """The accumulating entry points apply the backward's checks; dW needs the
+    larger accumulating workspace."""
+    s = P(0)
+    X, dY, pk, sc = P(0x1000000), P(0x2000000), P(0x3000000), P(0x4000000)
+    dX, gq, sg = P(0x5000000), P(0x6000000), P(0x7000000)
+    T, n_in, n_out = 4096, 2048, 2048
+    dx = L.tern_linear_bwd_dx_acc
+    assert dx(dY, 3, pk, sc, T, n_in, n_out, dX, s) == DTYPE
+    assert dx(dY, BF16, pk, sc, T, 100, n_out, dX, s) == SHAPE
+    assert dx(None, BF16, pk, sc, T, n_in, n_out, dX, s) == NULL
+    assert dx(dY, BF16, pk, sc, T, n_in, n_out, None, s) == NULL
+    assert dx(dY, BF16, pk, sc, T, n_in, n_out, P(0x5000004), s) == ALIGN
+    assert dx(dY, BF16, pk, sc, T, n_in, n_out, P(0x2000000 + 4096), s) == ALIAS   # dX over dY
+    dw = L.tern_linear_bwd_dw_acc
+    need = tl.tern_linear_bwd_acc_workspace_bytes(T, n_in, n_out, BF16)
+    plain = tl.tern_linear_bwd_workspace_bytes(T, n_in, n_out, BF16)
+    assert need >= plain + 4 * n_in * n_out   # room for G itself
+    ws, gq2 = P(0x10000000), P(0x30000000)
+    a = ctypes.c_float(0.5)
+    assert dw(X, dY, BF16, pk, sc, T, n_in, n_out, a, gq2, sg, ws, need - 1, s) == WORKSPACE
+    assert dw(X, dY, BF16, pk, sc, T, n_in, n_out, a, gq2, sg, None, need, s) == WORKSPACE
+    assert dw(X, dY, BF16, pk, sc, T, n_in, 12, a, gq2, sg, ws, need, s) == SHAPE
+    assert dw(None, dY, BF16, pk, sc, T, n_in, n_out, a, gq2, sg, ws, need, s) == NULL
+    assert dw(X, dY, BF16, pk, sc, T, n_in, n_out, a, None, sg, ws, need, s) == NULL
+    assert dw(X, dY, BF16, pk, sc, T, n_in, n_out, a, P(0x2000000 + 4096), sg, ws, need, s) == ALIAS  # gq over dY
+
+
+def test_acc_workspace_bytes(L):
+    assert tl.tern_linear_bwd_acc_workspace_bytes(8, 12, 8, BF16) == 0
+    assert tl.tern_linear_bwd_acc_workspace_bytes(8, 8, 8, 9) == 0
+    for (T, i, o) in [(64, 64, 64), (2048, 512, 2048), (16384, 8192, 2048), (1000, 200, 72)]:
+        for dt in (F32, BF16):
+            w = tl.tern_linear_bwd_acc_workspace_bytes(T, i, o, dt)
+            assert w >= tl.tern_linear_bwd_workspace_bytes(T, i, o, dt) and w >= 4 * i * o and w % 256 == 0
