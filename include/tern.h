@@ -195,6 +195,45 @@ int tern_linear_bwd_dw_acc(const void *X, const void *dY, int32_t act_dtype,
                            void *stream);
 
 /*
+ * SR4 health panel (page "train_gpu.cu": the sr4_panel struct and
+ * sr4_panel_compute, which the trainer runs on the host after a step).  Here
+ * the counts are taken on the device into a caller-owned accumulator, one
+ * ternary matrix per tern_panel_add call:
+ *   total        elements counted;
+ *   neg, zero, pos  elements whose ternary value (threshold rule with theta)
+ *                is -1, 0, +1;
+ *   rail         elements with |q| == q_clamp (the page's SR4_Q_CLAMP, 7);
+ *   dead         elements with |q| < theta (equal to zero by definition);
+ *   churn        elements whose ternary value differs from the one in
+ *                prev_packed (the previous step's handle), over churn_total
+ *                elements compared (calls with prev_packed NULL add none);
+ *   scale_count, scale_sum, scale_min, scale_max  over the scale columns.
+ * The page's fractions are the counts over total (churn over total when every
+ * matrix was compared, else 0) and scale_sum / scale_count.  Integer counts
+ * are exact; the scale sum is a fixed-order f64 sum per call, so repeated runs
+ * give identical panels.
+ *
+ * tern_panel_reset -- zero the accumulator (min +inf, max -inf).
+ * tern_panel_add -- add one matrix: q int8 [in, out], scale fp32 [out],
+ *   prev_packed a handle of tern_materialize for the same in, out (its
+ *   canonical part is read) or NULL.  theta in [1, 127], q_clamp in
+ *   [0, 128].  panel is device memory, 8-byte aligned, written in stream
+ *   order (calls on one stream accumulate).
+ * Errors: NULL, SHAPE, THETA (theta or q_clamp out of range), ALIGN, ALIAS,
+ *   HIP.
+ */
+typedef struct tern_panel {
+    uint64_t total, neg, zero, pos, rail, dead;
+    uint64_t churn, churn_total;
+    uint64_t scale_count;
+    double scale_sum, scale_min, scale_max;
+} tern_panel_t;
+int tern_panel_reset(tern_panel_t *panel, void *stream);
+int tern_panel_add(const int8_t *q, int64_t in, int64_t out, int32_t theta, int32_t q_clamp,
+                   const uint32_t *prev_packed, const float *scale, tern_panel_t *panel,
+                   void *stream);
+
+/*
  * Graphs of library calls.  The page's trainer launches every glue kernel and
  * GEMM of a step separately and notes that it is launch-bound; a caller can
  * instead record any sequence of the calls above (for example materialize,

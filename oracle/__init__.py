@@ -66,6 +66,8 @@ class Oracle:
         L.oracle_linear_wgrad.argtypes = [vp, vp, i32, vp, i32, vp, i64, i64, i64, vp, i64,
                                           vp, vp, vp]
         L.oracle_linear_wgrad.restype = ctypes.c_int
+        L.oracle_panel_add.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.oracle_panel_add.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         self.L = L
@@ -115,6 +117,34 @@ class Oracle:
         if self.L.oracle_unpack(self._p(packed), n_in, n_out, self._p(out)) != 0:
             raise ValueError("oracle_unpack: reserved or nonzero padding code")
         return out
+
+    def panel(self, mats, theta: int, q_clamp: int = 7) -> dict:
+        """SR4 health panel over the matrices `mats`, a list of (q, prev_tern or
+        None, scale).  Returns the counts and the page's fractions: churn only
+        when every matrix has a previous classification."""
+        counts = np.zeros(7, dtype=np.int64)
+        sstat = np.array([0.0, 0.0, np.inf, -np.inf])
+        snap_valid = True
+        for q, prev, scale in mats:
+            q = np.ascontiguousarray(q, dtype=np.int8)
+            n_in, n_out = q.shape
+            prev = None if prev is None else np.ascontiguousarray(prev, dtype=np.int8)
+            snap_valid = snap_valid and prev is not None
+            scale = np.ascontiguousarray(scale, dtype=np.float32)
+            if self.L.oracle_panel_add(self._p(q), n_in, n_out, int(theta), int(q_clamp), self._p(prev),
+                                       self._p(scale), self._p(counts), self._p(sstat)) != 0:
+                raise ValueError(f"oracle_panel_add: theta {theta} rejected")
+        names = ("total", "neg", "zero", "pos", "rail", "dead", "churn")
+        r = {k: int(v) for k, v in zip(names, counts)}
+        dt = float(r["total"]) if r["total"] else 1.0
+        r.update(pct_neg=r["neg"] / dt, pct_zero=r["zero"] / dt, pct_pos=r["pos"] / dt,
+                 rail_pct=r["rail"] / dt, dead_pct=r["dead"] / dt,
+                 churn_frac=(r["churn"] / dt) if snap_valid else 0.0,
+                 scale_count=int(sstat[0]), scale_sum=float(sstat[1]),
+                 scale_mean=float(sstat[1] / sstat[0]) if sstat[0] else 0.0,
+                 scale_min=float(sstat[2]) if sstat[0] else 0.0,
+                 scale_max=float(sstat[3]) if sstat[0] else 0.0)
+        return r
 
     def widen(self, a: np.ndarray) -> np.ndarray:
         a, dt = self._act(a)

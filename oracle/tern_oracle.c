@@ -255,3 +255,32 @@ int oracle_linear_wgrad(const void *X, const void *dY, int32_t dtype, const int8
     free(tern);
     return 0;
 }
+
+/* ---- SR4 health panel (page "train_gpu.cu", sr4_panel_compute) ---- */
+
+int oracle_panel_add(const int8_t *q, int64_t in, int64_t out, int32_t theta, int32_t q_clamp,
+                     const int8_t *prev_tern, const float *scale, int64_t counts[7],
+                     double sstat[4]) {
+    if (theta < 1) return -1;
+    const int64_t n = in * out;
+    for (int64_t k = 0; k < n; k++) {
+        const int v = q[k];
+        const int t = v >= theta ? 1 : (v <= -theta ? -1 : 0);
+        const int a = v < 0 ? -v : v;
+        counts[0] += 1;
+        if (t < 0) counts[1] += 1;
+        else if (t > 0) counts[3] += 1;
+        else counts[2] += 1;
+        if (a == q_clamp) counts[4] += 1;
+        if (a < theta) counts[5] += 1;
+        if (prev_tern && prev_tern[k] != t) counts[6] += 1;
+    }
+    for (int64_t c = 0; c < out; c++) {
+        const double s = (double)scale[c];
+        sstat[0] += 1.0;
+        sstat[1] += s;
+        if (s < sstat[2]) sstat[2] = s;
+        if (s > sstat[3]) sstat[3] = s;
+    }
+    return 0;
+}

@@ -88,6 +88,20 @@ int oracle_linear_wgrad(const void *X, const void *dY, int32_t dtype, const int8
                         int64_t out, const int64_t *cols, int64_t ncols,
                         double *G, double *gq, double *sgrad);
 
+/* SR4 health panel of one ternary matrix, added to running totals (page
+ * "train_gpu.cu", sr4_panel and sr4_panel_compute).  For every element of q
+ * [in, out]: its class under the threshold rule (negative, zero, positive),
+ * rail (|q| == q_clamp), dead (|q| < theta), and, when prev_tern is not NULL,
+ * churn (the class differs from prev_tern, the previous classification).  For
+ * every column of scale [out]: its sum (double, ascending), minimum, maximum.
+ *   counts[7] += {total, neg, zero, pos, rail, dead, churn}
+ *   sstat[0] += out (columns), sstat[1] += sum, sstat[2] = min, sstat[3] = max
+ *   (sstat[2], sstat[3] start at +/-HUGE_VAL for an empty panel).
+ * Returns 0, or -1 if theta < 1. */
+int oracle_panel_add(const int8_t *q, int64_t in, int64_t out, int32_t theta, int32_t q_clamp,
+                     const int8_t *prev_tern, const float *scale, int64_t counts[7],
+                     double sstat[4]);
+
 /* Threads the OpenMP build uses (1 without OpenMP). */
 int oracle_num_threads(void);
 

@@ -44,6 +44,8 @@ SIGNATURES = {
     "tern_linear_bwd_acc_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "tern_linear_bwd_dw_acc": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, ctypes.c_float,
                                               _vp, _vp, _vp, _sz, _vp]),
+    "tern_panel_reset": (ctypes.c_int, [_vp, _vp]),
+    "tern_panel_add": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "tern_graph_begin": (ctypes.c_int, [_vp]),
     "tern_graph_end": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
     "tern_graph_launch": (ctypes.c_int, [_vp, _vp]),
@@ -205,6 +207,45 @@ def tern_linear_bwd_dw_acc(X, dY, tern_packed, scale, gq, sgrad, workspace, alph
                                       n_in, n_out, float(alpha), _ptr(gq), _ptr(sgrad), _ptr(workspace),
                                       ws_bytes, _stream(stream))
     _check("tern_linear_bwd_dw_acc", rc)
+
+
+PANEL_COUNTS = ("total", "neg", "zero", "pos", "rail", "dead", "churn", "churn_total", "scale_count")
+PANEL_STATS = ("scale_sum", "scale_min", "scale_max")
+
+
+def empty_panel(device="cuda") -> torch.Tensor:
+    """Device storage of one tern_panel_t (9 uint64 counts, then 3 doubles)."""
+    return torch.empty((len(PANEL_COUNTS) + len(PANEL_STATS),), dtype=torch.float64, device=device)
+
+
+def tern_panel_reset(panel: torch.Tensor, stream=None) -> None:
+    _check("tern_panel_reset", lib().tern_panel_reset(_ptr(panel), _stream(stream)))
+
+
+def tern_panel_add(q: torch.Tensor, theta: int, scale: torch.Tensor, panel: torch.Tensor, prev_packed=None,
+                   q_clamp: int = 7, stream=None) -> None:
+    """Add one ternary matrix (q int8 [in, out], scale [out]) to the panel;
+    prev_packed: the previous step's handle for churn, or None."""
+    n_in, n_out = q.shape
+    rc = lib().tern_panel_add(_ptr(q), n_in, n_out, int(theta), int(q_clamp), _ptr(prev_packed), _ptr(scale),
+                              _ptr(panel), _stream(stream))
+    _check("tern_panel_add", rc)
+
+
+def panel_values(panel: torch.Tensor) -> dict:
+    """The accumulator's fields, and the page's fractions of them (churn only
+    when every element was compared with a previous handle)."""
+    h = panel.cpu()
+    n = len(PANEL_COUNTS)
+    counts = h[:n].view(torch.int64).tolist()
+    r = dict(zip(PANEL_COUNTS, counts))
+    r.update(zip(PANEL_STATS, h[n:].tolist()))
+    dt = float(r["total"]) if r["total"] else 1.0
+    valid = r["total"] > 0 and r["churn_total"] == r["total"]
+    r.update(pct_neg=r["neg"] / dt, pct_zero=r["zero"] / dt, pct_pos=r["pos"] / dt, rail_pct=r["rail"] / dt,
+             dead_pct=r["dead"] / dt, churn_frac=r["churn"] / dt if valid else 0.0,
+             scale_mean=r["scale_sum"] / r["scale_count"] if r["scale_count"] else 0.0)
+    return r
 
 
 def tern_graph_begin(stream) -> None:

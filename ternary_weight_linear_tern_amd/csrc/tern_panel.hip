@@ -1,0 +1,186 @@
+// tern_panel.hip -- the SR4 health panel on gfx950 (C ABI in include/tern.h).
+//
+// The page "train_gpu.cu" (sr4_panel, sr4_panel_compute) copies q and scale
+// to the host after a step and counts there: the ternary class of every
+// element under the threshold rule, rail (|q| at the clamp), dead (|q| below
+// theta), churn against the previous classification, and the scale's mean,
+// minimum and maximum.  Here one kernel counts a matrix on the device, one
+// thread per 16 elements of a row (the span of one packed word), so the
+// classes and the churn against the previous handle's canonical word are
+// popcounts of 2-bit codes; block sums go to the accumulator with integer
+// atomics, which are exact in any order.  A one-block kernel adds the scale
+// statistics in a fixed order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tern.h"
+#include "tern_plan.h"
+
+namespace tern {
+namespace pdev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ void panel_reset_kernel(tern_panel_t *p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        p->total = p->neg = p->zero = p->pos = p->rail = p->dead = 0;
+        p->churn = p->churn_total = p->scale_count = 0;
+        p->scale_sum = 0.0;
+        p->scale_min = __builtin_inf();
+        p->scale_max = -__builtin_inf();
+    }
+}
+
+// Sum of v over the block (256 threads, 4 waves), valid in thread 0.
+__device__ __forceinline__ uint64_t block_sum(uint64_t v, uint64_t *red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void panel_count_kernel(const int8_t *__restrict__ q, int64_t out, int64_t wpr,
+                                                          int64_t nwords, int theta, int clamp,
+                                                          const uint32_t *__restrict__ prev,
+                                                          tern_panel_t *__restrict__ p) {
+    __shared__ uint64_t red[4];
+    uint32_t tot = 0, neg = 0, pos = 0, rail = 0, dead = 0, churn = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nwords; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / wpr, wc = i - r * wpr;
+        const int8_t *row = q + r * out + wc * 16;
+        const int nc = out - wc * 16 < 16 ? (int)(out - wc * 16) : 16;
+        int8_t b[16];
+        if constexpr (VEC) {
+            const u32x4 v = *(const u32x4 *)row;
+#pragma unroll
+            for (int j = 0; j < 16; j++) b[j] = (int8_t)((v[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; j++) b[j] = j < nc ? row[j] : (int8_t)0;
+        }
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            if (j < nc) {
+                const int v = b[j], a = v < 0 ? -v : v;
+                const uint32_t code = v >= theta ? 1u : (v <= -theta ? 3u : 0u);
+                word |= code << (2 * j);
+                rail += a == clamp;
+                dead += a < theta;
+            }
+        }
+        tot += (uint32_t)nc;
+        // code 01 = +1, 11 = -1 (bit 0: nonzero, bit 1: negative)
+        pos += (uint32_t)__builtin_popcount(word & ~(word >> 1) & 0x55555555u);
+        neg += (uint32_t)__builtin_popcount(word & (word >> 1) & 0x55555555u);
+        if (prev) {
+            const uint32_t d = word ^ prev[i];   // padding codes are 00 in both
+            churn += (uint32_t)__builtin_popcount((d | (d >> 1)) & 0x55555555u);
+        }
+    }
+    const uint64_t s_tot = block_sum(tot, red);
+    const uint64_t s_neg = block_sum(neg, red);
+    const uint64_t s_pos = block_sum(pos, red);
+    const uint64_t s_rail = block_sum(rail, red);
+    const uint64_t s_dead = block_sum(dead, red);
+    const uint64_t s_churn = block_sum(churn, red);
+    if (threadIdx.x == 0 && s_tot) {
+        atomicAdd((unsigned long long *)&p->total, (unsigned long long)s_tot);
+        atomicAdd((unsigned long long *)&p->neg, (unsigned long long)s_neg);
+        atomicAdd((unsigned long long *)&p->zero, (unsigned long long)(s_tot - s_neg - s_pos));
+        atomicAdd((unsigned long long *)&p->pos, (unsigned long long)s_pos);
+        atomicAdd((unsigned long long *)&p->rail, (unsigned long long)s_rail);
+        atomicAdd((unsigned long long *)&p->dead, (unsigned long long)s_dead);
+        if (prev) {
+            atomicAdd((unsigned long long *)&p->churn, (unsigned long long)s_churn);
+            atomicAdd((unsigned long long *)&p->churn_total, (unsigned long long)s_tot);
+        }
+    }
+}
+
+// One block: thread t sums columns t, t + 256, ... in f64 (ascending), then a
+// fixed tree over the threads; thread 0 adds the result to the accumulator.
+__global__ __launch_bounds__(256) void panel_scale_kernel(const float *__restrict__ scale, int64_t out,
+                                                          tern_panel_t *__restrict__ p) {
+    __shared__ double ssum[256];
+    __shared__ float smin[256], smax[256];
+    const int t = threadIdx.x;
+    double s = 0.0;
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    for (int64_t c = t; c < out; c += 256) {
+        const float v = scale[c];
+        s += (double)v;
+        mn = v < mn ? v : mn;
+        mx = v > mx ? v : mx;
+    }
+    ssum[t] = s;
+    smin[t] = mn;
+    smax[t] = mx;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (t < h) {
+            ssum[t] += ssum[t + h];
+            smin[t] = smin[t + h] < smin[t] ? smin[t + h] : smin[t];
+            smax[t] = smax[t + h] > smax[t] ? smax[t + h] : smax[t];
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        p->scale_count += (uint64_t)out;
+        p->scale_sum += ssum[0];
+        if ((double)smin[0] < p->scale_min) p->scale_min = (double)smin[0];
+        if ((double)smax[0] > p->scale_max) p->scale_max = (double)smax[0];
+    }
+}
+
+}  // namespace pdev
+}  // namespace tern
+
+using namespace tern;
+
+extern "C" {
+
+int tern_panel_reset(tern_panel_t *panel, void *stream) {
+    if (!panel) return TERN_ERR_NULL;
+    if (((uintptr_t)panel & 7u) != 0) return TERN_ERR_ALIGN;
+    hipLaunchKernelGGL(pdev::panel_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, panel);
+    return hipGetLastError() == hipSuccess ? TERN_OK : TERN_ERR_HIP;
+}
+
+int tern_panel_add(const int8_t *q, int64_t in, int64_t out, int32_t theta, int32_t q_clamp,
+                   const uint32_t *prev_packed, const float *scale, tern_panel_t *panel, void *stream) {
+    if (in < 0 || out < 0 || in > kMaxInOut || out > kMaxInOut) return TERN_ERR_SHAPE;
+    if (theta < 1 || theta > 127 || q_clamp < 0 || q_clamp > 128) return TERN_ERR_THETA;
+    const size_t qb = (size_t)in * (size_t)out, sb = (size_t)out * 4, pb = sizeof(tern_panel_t);
+    const size_t hb = prev_packed ? (size_t)in * (size_t)((out + 15) / 16) * 4 : 0;
+    if (!panel || (qb && !q) || (sb && !scale)) return TERN_ERR_NULL;
+    if (((uintptr_t)panel & 7u) != 0 || ((uintptr_t)scale & 3u) != 0 || ((uintptr_t)prev_packed & 3u) != 0)
+        return TERN_ERR_ALIGN;
+    if (ranges_overlap(panel, pb, q, qb) || ranges_overlap(panel, pb, scale, sb) ||
+        ranges_overlap(panel, pb, prev_packed, hb))
+        return TERN_ERR_ALIAS;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t wpr = (out + 15) / 16, nwords = in * wpr;
+    if (nwords > 0) {
+        int64_t blocks = (nwords + 255) / 256;
+        if (blocks > 2048) blocks = 2048;
+        const bool vec = out % 16 == 0 && ((uintptr_t)q & 15u) == 0;
+        if (vec)
+            hipLaunchKernelGGL(pdev::panel_count_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, q, out,
+                               wpr, nwords, (int)theta, (int)q_clamp, prev_packed, panel);
+        else
+            hipLaunchKernelGGL(pdev::panel_count_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, q, out,
+                               wpr, nwords, (int)theta, (int)q_clamp, prev_packed, panel);
+        if (hipGetLastError() != hipSuccess) return TERN_ERR_HIP;
+    }
+    if (out > 0) {
+        hipLaunchKernelGGL(pdev::panel_scale_kernel, dim3(1), dim3(256), 0, st, scale, out, panel);
+        if (hipGetLastError() != hipSuccess) return TERN_ERR_HIP;
+    }
+    return TERN_OK;
+}
+
+}  // extern "C"

@@ -301,7 +301,70 @@ def pin_widen(o):
     assert list(got) == want, list(got)
 
 
+def pin_panel_golden(o):
+    """The SR4 health panel of a hand-counted 2 x 8 example
+    (tests/golden/panel_example.txt)."""
+    g = _golden_kv("panel_example.txt")
+    q = np.array([[int(v) for v in g["q0"][0]], [int(v) for v in g["q1"][0]]], dtype=np.int8)
+    scale = np.array([float(v) for v in g["scale"][0]], dtype=np.float32)
+    r = o.panel([(q, np.zeros_like(q), scale)], int(g["theta"][0][0]), int(g["clamp"][0][0]))
+    for k in ("total", "neg", "zero", "pos", "rail", "dead", "churn"):
+        assert r[k] == int(g[k][0][0]), (k, r[k])
+    for k in ("scale_sum", "scale_mean", "scale_min", "scale_max"):
+        assert r[k] == float(g[k][0][0]), (k, r[k])
+    assert r["churn_frac"] == 10 / 16 and r["rail_pct"] == 4 / 16
+
+
+def _panel_brute(mats, theta, clamp):
+    """Counts written out independently in pure Python."""
+    c = dict(total=0, neg=0, zero=0, pos=0, rail=0, dead=0, churn=0)
+    svals = []
+    for q, prev, scale in mats:
+        for k, v in enumerate(q.reshape(-1).tolist()):
+            t = 1 if v >= theta else (-1 if v <= -theta else 0)
+            c["total"] += 1
+            c["neg" if t < 0 else ("pos" if t > 0 else "zero")] += 1
+            c["rail"] += abs(v) == clamp
+            c["dead"] += abs(v) < theta
+            if prev is not None:
+                c["churn"] += int(prev.reshape(-1)[k]) != t
+        svals += [float(x) for x in scale]
+    return c, svals
+
+
+def pin_panel_brute_and_invariants(o):
+    """Panel counts equal pure-Python counting over several matrices, and the
+    definitions' invariants hold: zero == dead (a zero ternary value is exactly
+    |q| < theta), neg + zero + pos == total, churn 0 against the matrix's own
+    classification and neg + pos against its negation."""
+    rng = np.random.default_rng(5)
+    for theta, clamp in ((2, 7), (1, 7), (3, 5)):
+        mats = []
+        for shape in ((3, 16), (5, 24), (1, 8)):
+            q = rng.integers(-9, 10, size=shape).astype(np.int8)
+            q.reshape(-1)[0] = clamp
+            q.reshape(-1)[-1] = -128
+            prev = rng.integers(-1, 2, size=shape).astype(np.int8)
+            scale = rng.uniform(0.01, 0.1, size=shape[1]).astype(np.float32)
+            mats.append((q, prev, scale))
+        r = o.panel(mats, theta, clamp)
+        want, svals = _panel_brute(mats, theta, clamp)
+        for k, v in want.items():
+            assert r[k] == v, (theta, clamp, k, r[k], v)
+        assert r["scale_count"] == len(svals)
+        assert r["scale_min"] == min(svals) and r["scale_max"] == max(svals)
+        assert abs(r["scale_sum"] - sum(svals)) <= 1e-12 * len(svals)
+        assert r["zero"] == r["dead"] and r["neg"] + r["zero"] + r["pos"] == r["total"]
+        own = [(q, o.tern(q, theta), s) for q, _, s in mats]
+        assert o.panel(own, theta, clamp)["churn"] == 0
+        neg = [(q, -o.tern(q, theta), s) for q, _, s in mats]
+        rn = o.panel(neg, theta, clamp)
+        assert rn["churn"] == rn["neg"] + rn["pos"]
+        # without a previous classification for every matrix there is no churn
+        assert o.panel([mats[0], (mats[1][0], None, mats[1][2])], theta, clamp)["churn_frac"] == 0.0
+
+
 ALL_PINS = [pin_tern_golden, pin_tern_properties, pin_pack_golden, pin_pack_roundtrip,
             pin_worked_example, pin_brute_force, pin_sign_matrix_gemm,
             pin_bilinear_identities, pin_finite_differences, pin_dead_zone,
-            pin_sampling_consistent, pin_widen]
+            pin_sampling_consistent, pin_widen, pin_panel_golden, pin_panel_brute_and_invariants]

@@ -206,3 +206,20 @@ def test_acc_workspace_bytes(L):
         for dt in (F32, BF16):
             w = tl.tern_linear_bwd_acc_workspace_bytes(T, i, o, dt)
             assert w >= tl.tern_linear_bwd_workspace_bytes(T, i, o, dt) and w >= 4 * i * o and w % 256 == 0
+
+
+def test_panel_rejects(L):
+    s = P(0)
+    assert L.tern_panel_reset(None, s) == NULL
+    assert L.tern_panel_reset(P(0x1004), s) == ALIGN
+    q, sc, pan = P(0x1000000), P(0x2000000), P(0x3000000)
+    add = L.tern_panel_add
+    assert add(q, -1, 64, 2, 7, None, sc, pan, s) == SHAPE
+    assert add(q, 64, 64, 0, 7, None, sc, pan, s) == THETA
+    assert add(q, 64, 64, 2, 129, None, sc, pan, s) == THETA
+    assert add(None, 64, 64, 2, 7, None, sc, pan, s) == NULL
+    assert add(q, 64, 64, 2, 7, None, None, pan, s) == NULL
+    assert add(q, 64, 64, 2, 7, None, sc, None, s) == NULL
+    assert add(q, 64, 64, 2, 7, None, sc, P(0x3000004), s) == ALIGN
+    assert add(q, 64, 64, 2, 7, P(0x4000002), sc, pan, s) == ALIGN
+    assert add(q, 64, 64, 2, 7, None, sc, P(0x1000000 + 64), s) == ALIAS   # panel inside q

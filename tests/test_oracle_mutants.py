@@ -39,6 +39,13 @@ MUTANTS = [
     ("bf16_widen_shift", "uint32_t u = (uint32_t)((const uint16_t *)src)[i] << 16;",
      "uint32_t u = (uint32_t)((const uint16_t *)src)[i] << 15;"),
     ("pack_bit_order", "word |= code << (2 * j);", "word |= code << (30 - 2 * j);"),
+    ("panel_dead_inclusive", "if (a < theta) counts[5] += 1;", "if (a <= theta) counts[5] += 1;"),
+    ("panel_rail_uses_theta", "if (a == q_clamp) counts[4] += 1;", "if (a == theta) counts[4] += 1;"),
+    ("panel_churn_ignores_sign", "if (prev_tern && prev_tern[k] != t) counts[6] += 1;",
+     "if (prev_tern && (prev_tern[k] != 0) != (t != 0)) counts[6] += 1;"),
+    ("panel_zero_counted_as_pos", "else if (t > 0) counts[3] += 1;", "else if (t >= 0) counts[3] += 1;"),
+    ("panel_scale_min_skips_first", "for (int64_t c = 0; c < out; c++) {\n        const double s",
+     "for (int64_t c = 1; c < out; c++) {\n        const double s"),
 ]
 
 
