@@ -195,6 +195,30 @@ int tern_linear_bwd_dw_acc(const void *X, const void *dY, int32_t act_dtype,
                            void *stream);
 
 /*
+ * Projections that read one input.  nvg_train.rs (lin_fwd_shared) runs up to
+ * four linears that read the same x off one staging pass of x, and the
+ * trainer's attention projections read one input.  Here such a group is one
+ * projection over the concatenated columns, W_group = [W_1 | W_2 | ...] of
+ * [in, out_1 + ... + out_n]: one materialize, one forward (Y_group [T, sum out]
+ * holds each Y_i as a column slice), one backward whose dX is the sum of the
+ * projections' input gradients, and gq / sgrad as column slices.  Each
+ * output column keeps its own summation order, so a Y_i slice equals the Y of
+ * projection i alone bit for bit.
+ *
+ * tern_group_gather -- q_group[r, off_i + c] = q[i][r, c] and
+ *   scale_group[off_i + c] = scale[i][c], with off_i = out[0] + ... +
+ *   out[i-1].  q, scale, out: host arrays of n entries (1 <= n <= 8) holding
+ *   device pointers to row-major int8 [in, out[i]] and fp32 [out[i]].
+ *   q_group: device int8 [in, sum out]; scale_group: device fp32 [sum out].
+ *   Then tern_materialize(q_group, in, sum out, ...) builds the group's
+ *   handle.  Errors: NULL, SHAPE (n outside [1, 8], a negative size or a
+ *   total above the limits), ALIAS (an output overlapping an input or the
+ *   other output), HIP.
+ */
+int tern_group_gather(const int8_t *const *q, const float *const *scale, const int64_t *out,
+                      int32_t n, int64_t in, int8_t *q_group, float *scale_group, void *stream);
+
+/*
  * SR4 health panel (page "train_gpu.cu": the sr4_panel struct and
  * sr4_panel_compute, which the trainer runs on the host after a step).  Here
  * the counts are taken on the device into a caller-owned accumulator, one

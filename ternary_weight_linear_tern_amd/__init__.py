@@ -44,6 +44,7 @@ SIGNATURES = {
     "tern_linear_bwd_acc_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "tern_linear_bwd_dw_acc": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, ctypes.c_float,
                                               _vp, _vp, _vp, _sz, _vp]),
+    "tern_group_gather": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp]),
     "tern_panel_reset": (ctypes.c_int, [_vp, _vp]),
     "tern_panel_add": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "tern_graph_begin": (ctypes.c_int, [_vp]),
@@ -207,6 +208,18 @@ def tern_linear_bwd_dw_acc(X, dY, tern_packed, scale, gq, sgrad, workspace, alph
                                       n_in, n_out, float(alpha), _ptr(gq), _ptr(sgrad), _ptr(workspace),
                                       ws_bytes, _stream(stream))
     _check("tern_linear_bwd_dw_acc", rc)
+
+
+def tern_group_gather(qs, scales, q_group: torch.Tensor, scale_group: torch.Tensor, stream=None) -> None:
+    """q_group [in, sum out] and scale_group [sum out] from the members' q
+    [in, out_i] and scale [out_i] (projections that read one input)."""
+    n = len(qs)
+    n_in = qs[0].shape[0] if n else 0
+    qa = (_vp * max(n, 1))(*[_ptr(t) for t in qs])
+    sa = (_vp * max(n, 1))(*[_ptr(t) for t in scales])
+    oa = (_i64 * max(n, 1))(*[int(t.shape[1]) for t in qs])
+    rc = lib().tern_group_gather(qa, sa, oa, n, n_in, _ptr(q_group), _ptr(scale_group), _stream(stream))
+    _check("tern_group_gather", rc)
 
 
 PANEL_COUNTS = ("total", "neg", "zero", "pos", "rail", "dead", "churn", "churn_total", "scale_count")

@@ -223,3 +223,21 @@ def test_panel_rejects(L):
     assert add(q, 64, 64, 2, 7, None, sc, P(0x3000004), s) == ALIGN
     assert add(q, 64, 64, 2, 7, P(0x4000002), sc, pan, s) == ALIGN
     assert add(q, 64, 64, 2, 7, None, sc, P(0x1000000 + 64), s) == ALIAS   # panel inside q
+
+
+def test_group_gather_rejects(L):
+    s = P(0)
+    g = L.tern_group_gather
+    q = (ctypes.c_void_p * 2)(0x1000000, 0x2000000)
+    sc = (ctypes.c_void_p * 2)(0x3000000, 0x3100000)
+    outs = (ctypes.c_int64 * 2)(64, 128)
+    qg, sg = P(0x4000000), P(0x5000000)
+    assert g(q, sc, outs, 0, 64, qg, sg, s) == SHAPE
+    assert g(q, sc, outs, 9, 64, qg, sg, s) == SHAPE
+    assert g(q, sc, outs, 2, -1, qg, sg, s) == SHAPE
+    assert g(q, sc, (ctypes.c_int64 * 2)(64, -8), 2, 64, qg, sg, s) == SHAPE
+    assert g(None, sc, outs, 2, 64, qg, sg, s) == NULL
+    assert g(q, sc, outs, 2, 64, None, sg, s) == NULL
+    assert g((ctypes.c_void_p * 2)(0x1000000, None), sc, outs, 2, 64, qg, sg, s) == NULL
+    assert g(q, sc, outs, 2, 64, P(0x1000000 + 100), sg, s) == ALIAS      # q_group over member 0's q
+    assert g(q, sc, outs, 2, 64, qg, P(0x4000000 + 64), s) == ALIAS       # scale_group inside q_group
