@@ -1584,7 +1584,9 @@ __global__ __launch_bounds__(256) void materialize_kernel(const int8_t *__restri
 
 // Split-K finish of dW: G = sum over splits (ascending), gq = G * scale (acc:
 // gq + alpha * G * scale), and the sgrad partial of a block of kReduceRows rows
-// (ascending r).  Each thread
+// (ascending r).  The row and split loops are unrolled so that several rows'
+// loads are in flight per thread (one block per compute unit at the usual
+// sizes, so the loads' latency would otherwise set the pace).  Each thread
 // owns 4 consecutive columns (16-byte loads and stores); a block covers 1024
 // columns of kReduceRows rows.
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ ws, int splits,
@@ -1599,9 +1601,11 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
     const f32x4 s = *(const f32x4 *)(scale + c);
     const int64_t plane = (int64_t)in * out;
     f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
     for (int r = r0; r < r1; r++) {
         const int64_t o = (int64_t)r * out + c;
         f32x4 gv = *(const f32x4 *)(ws + o);
+#pragma unroll 4
         for (int k = 1; k < splits; k++) gv += *(const f32x4 *)(ws + k * plane + o);
         f32x4 t = gv * s;
         if (acc) t = *(const f32x4 *)(gq + o) + alpha * t;

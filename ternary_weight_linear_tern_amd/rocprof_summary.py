@@ -14,6 +14,7 @@ while the kernel source is unchanged.
 from __future__ import annotations
 
 import csv
+import re
 import hashlib
 import json
 import os
@@ -32,12 +33,11 @@ def entry_of(kernel: str) -> str | None:
     if "gemm_dw_kernel" in k:
         return "bwd_dw"
     if "gemm" in k:
-        if "<0>" in k or ", 0," in k:
-            return "fwd"
-        if "<1>" in k or ", 1," in k:
-            return "bwd_dx"
-        if "<2>" in k or ", 2," in k:
-            return "bwd_dw"
+        # gemm_rd_kernel<MODE, ACC> and gemm_kernel<BF, MODE, BM>: the mode is
+        # the first template argument of the former, the second of the latter
+        m = re.search(r"gemm_rd_kernel<(\d)", k) or re.search(r"gemm_kernel<\w+, (\d)", k)
+        mode = m.group(1) if m else None
+        return {"0": "fwd", "1": "bwd_dx", "2": "bwd_dw"}.get(mode)
     if "dw_reduce" in k or "sgrad_reduce" in k:
         return "bwd_dw"
     return None
