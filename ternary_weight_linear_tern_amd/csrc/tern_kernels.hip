@@ -1386,6 +1386,8 @@ void gemm_rd_kernel(GemmArgs g) {
     constexpr int DEC_OPS = MODE == MODE_FWD ? 2 : 5;   // VALU per decoded dword (with the masks)
     u32x4 acur;   // decoded fragment whose MFMAs come next (carried across chunks)
 
+    int sc = 0;   // LDS stage of the current chunk
+
     // Epilogue of tile (ctm, ctn): 64 buffer stores per wave whatever the edges
     // (out-of-range stores get an out-of-range offset), so the vmcnt arithmetic
     // of the main loop holds.  ACC (dX += ...): the 4 old values of each
@@ -1456,13 +1458,63 @@ void gemm_rd_kernel(GemmArgs g) {
             }
         };
 
+        // fp32 without accumulation: each 32-row x 64-column piece of the
+        // wave's block passes through the LDS stage the last chunk consumed
+        // (free until the next chunk's first issue), transposed so that every
+        // store writes 4 rows x 256 contiguous bytes (whole 128-byte lines)
+        // instead of 32 rows x 32 bytes.  Lane (l32, h) holds row l32 of the
+        // piece in 16-byte slots 8 (fm % 2) + 2 q + h; slot s of row t sits at
+        // s ^ (t % 16), which makes both the writes and the reads free of bank
+        // conflicts.  Still 64 stores per wave, in the same resource; they
+        // carry the non-temporal hint (whole lines, read by a later kernel,
+        // so they need not displace the operand panels in L2).
+        auto rows_t = [&]() __attribute__((always_inline)) {
+            char *eb = wl + ((sc + 3) & 3) * R_STAGE;
+#pragma unroll
+            for (int fn = 0; fn < 4; fn++) {
+#pragma unroll
+                for (int fp = 0; fp < 2; fp++) {
+#pragma unroll
+                    for (int f2 = 0; f2 < 2; f2++) {
+                        const int fm = 2 * fp + f2;
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                                       acc[fm][fn][4 * q + 3]};
+                            if constexpr (MODE == MODE_FWD) v = v * *(const f32x4 *)(esc + fm * 32 + 8 * q);
+                            const int slot = (8 * f2 + 2 * q + h) ^ (l32 & 15);
+                            *(f32x4 *)(eb + l32 * 256 + slot * 16) = v;
+                        }
+                    }
+                    // the piece is in LDS before any lane reads another's row
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int k = 0; k < 8; k++) {
+                        const int t = 4 * k + (lane >> 4), pc = lane & 15;
+                        const f32x4 v = *(const f32x4 *)(eb + t * 256 + ((pc ^ (t & 15)) * 16));
+                        const int row = fn * 32 + t, col = fp * 64 + pc * 4;
+                        const uint32_t off =
+                            nw + row < g.N && mw + col < g.M ? (uint32_t)((row * ldo + col) * 4) : OOB;
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off, 0, 2);
+                    }
+                    // every read has returned before the next piece (or the
+                    // next chunk's loads) overwrites the stage
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_waitcnt(0xC07F);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+
         if (obf) rows(std::true_type{});
-        else rows(std::false_type{});
+        else if constexpr (ACC) rows(std::false_type{});
+        else rows_t();
     };
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    int sc = 0;   // LDS stage of the current chunk
 
     // one chunk (register slot SL): the eight fragments (K quarter, 32 rows) of
     // 4 MFMAs each, with the issue of the chunk three ahead spread over the
