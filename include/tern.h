@@ -57,6 +57,7 @@ extern "C" {
 #define TERN_ERR_WORKSPACE -6  /* workspace missing or smaller than required */
 #define TERN_ERR_ALIAS     -7  /* an output overlaps an input or another output */
 #define TERN_ERR_HIP       -8  /* the HIP runtime refused a launch */
+#define TERN_ERR_VALUE     -9  /* a scalar argument outside its range (optimizer step, learning rate) */
 
 /* Number of uint32 words of a packed ternary handle for an [in, out] matrix
  * (0 if in or out is 0, -1 for negative sizes).  The caller allocates this
@@ -193,6 +194,26 @@ int tern_linear_bwd_dw_acc(const void *X, const void *dY, int32_t act_dtype,
                            int64_t T, int64_t in, int64_t out, float alpha,
                            float *gq, float *sgrad, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/*
+ * tern_scale_adamw -- the step of the per-column scale that follows its
+ * gradient (page "train_gpu.cu": the trainer multiplies sgrad by
+ * scale_lr / lr, then runs its AdamW launcher on the scale with the step's
+ * bias corrections bc1 = 1 - b1^step, bc2 = 1 - b2^step; its hyper-parameters
+ * are b1 0.9, b2 0.999, eps 1e-8, weight decay 0).  The update kernel's body
+ * is not on the page; this is textbook AdamW with decoupled weight decay, in
+ * fp32, per column c < out:
+ *   g = sgrad[c] * (scale_lr / lr)
+ *   m[c] = b1 m[c] + (1 - b1) g;   v[c] = b2 v[c] + (1 - b2) g^2
+ *   scale[c] -= lr ((m[c] / bc1) / (sqrt(v[c] / bc2) + eps) + wd scale[c])
+ * sgrad [out] is read; scale, m, v [out] (fp32, device, 4-byte aligned) are
+ * updated in place; m = v = 0 before the first step (step = 1).
+ * Errors: NULL, SHAPE (out < 0 or too large), VALUE (step < 1, lr or
+ *   scale_lr not positive and finite), ALIGN, ALIAS, HIP.
+ */
+int tern_scale_adamw(const float *sgrad, float *scale, float *m, float *v, int64_t out,
+                     int32_t step, float lr, float scale_lr, float b1, float b2, float eps,
+                     float wd, void *stream);
 
 /*
  * Projections that read one input.  nvg_train.rs (lin_fwd_shared) runs up to

@@ -68,6 +68,9 @@ class Oracle:
         L.oracle_linear_wgrad.restype = ctypes.c_int
         L.oracle_panel_add.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, vp]
         L.oracle_panel_add.restype = ctypes.c_int
+        f64 = ctypes.c_double
+        L.oracle_scale_adamw.argtypes = [vp, vp, vp, vp, i64, i32, f64, f64, f64, f64, f64, f64]
+        L.oracle_scale_adamw.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
         self.L = L
@@ -145,6 +148,19 @@ class Oracle:
                  scale_min=float(sstat[2]) if sstat[0] else 0.0,
                  scale_max=float(sstat[3]) if sstat[0] else 0.0)
         return r
+
+    def scale_adamw(self, sgrad, scale, m, v, t, lr, scale_lr, b1=0.9, b2=0.999, eps=1e-8, wd=0.0):
+        """One AdamW step of the per-column scale; returns new (scale, m, v)
+        as float64 arrays (the inputs are not modified)."""
+        g = np.ascontiguousarray(sgrad, dtype=np.float64)
+        sc = np.array(scale, dtype=np.float64)
+        mm = np.array(m, dtype=np.float64)
+        vv = np.array(v, dtype=np.float64)
+        if self.L.oracle_scale_adamw(self._p(g), self._p(sc), self._p(mm), self._p(vv), g.size, int(t),
+                                     float(lr), float(scale_lr), float(b1), float(b2), float(eps),
+                                     float(wd)) != 0:
+            raise ValueError(f"oracle_scale_adamw: step {t} rejected")
+        return sc, mm, vv
 
     def widen(self, a: np.ndarray) -> np.ndarray:
         a, dt = self._act(a)

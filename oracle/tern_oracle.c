@@ -23,6 +23,7 @@
  */
 #include "tern_oracle.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -281,6 +282,23 @@ int oracle_panel_add(const int8_t *q, int64_t in, int64_t out, int32_t theta, in
         sstat[1] += s;
         if (s < sstat[2]) sstat[2] = s;
         if (s > sstat[3]) sstat[3] = s;
+    }
+    return 0;
+}
+
+/* ---- scale step: AdamW on the per-column scale (textbook form, see header) ---- */
+
+int oracle_scale_adamw(const double *sgrad, double *scale, double *m, double *v, int64_t out,
+                       int32_t t, double lr, double scale_lr, double b1, double b2, double eps,
+                       double wd) {
+    if (t < 1) return -1;
+    const double bc1 = 1.0 - pow(b1, (double)t), bc2 = 1.0 - pow(b2, (double)t);
+    for (int64_t c = 0; c < out; c++) {
+        const double g = sgrad[c] * scale_lr / lr;
+        m[c] = b1 * m[c] + (1.0 - b1) * g;
+        v[c] = b2 * v[c] + (1.0 - b2) * g * g;
+        const double mhat = m[c] / bc1, vhat = v[c] / bc2;
+        scale[c] -= lr * (mhat / (sqrt(vhat) + eps) + wd * scale[c]);
     }
     return 0;
 }

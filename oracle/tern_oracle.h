@@ -102,6 +102,19 @@ int oracle_panel_add(const int8_t *q, int64_t in, int64_t out, int32_t theta, in
                      const int8_t *prev_tern, const float *scale, int64_t counts[7],
                      double sstat[4]);
 
+/* The scale step that follows the scale gradient (page "train_gpu.cu": the
+ * trainer multiplies sgrad by scale_lr / lr and calls its AdamW launcher on
+ * the per-column scale, which forms bc1 = 1 - b1^t and bc2 = 1 - b2^t; the
+ * update kernel's body is not on the page).  Textbook AdamW with decoupled
+ * weight decay, in double, element by element:
+ *   g = sgrad[c] * scale_lr / lr
+ *   m[c] = b1 m[c] + (1 - b1) g;   v[c] = b2 v[c] + (1 - b2) g^2
+ *   scale[c] -= lr ((m[c] / bc1) / (sqrt(v[c] / bc2) + eps) + wd scale[c])
+ * scale, m, v (double) are updated in place.  Returns 0, or -1 if t < 1. */
+int oracle_scale_adamw(const double *sgrad, double *scale, double *m, double *v, int64_t out,
+                       int32_t t, double lr, double scale_lr, double b1, double b2, double eps,
+                       double wd);
+
 /* Threads the OpenMP build uses (1 without OpenMP). */
 int oracle_num_threads(void);
 

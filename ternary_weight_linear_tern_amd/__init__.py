@@ -25,7 +25,7 @@ TERN_BF16 = 1
 STATUS = {
     0: "TERN_OK", -1: "TERN_ERR_NULL", -2: "TERN_ERR_SHAPE", -3: "TERN_ERR_THETA",
     -4: "TERN_ERR_DTYPE", -5: "TERN_ERR_ALIGN", -6: "TERN_ERR_WORKSPACE", -7: "TERN_ERR_ALIAS",
-    -8: "TERN_ERR_HIP",
+    -8: "TERN_ERR_HIP", -9: "TERN_ERR_VALUE",
 }
 
 # Every symbol include/tern.h declares: name -> (restype, argtypes)
@@ -45,6 +45,7 @@ SIGNATURES = {
     "tern_linear_bwd_dw_acc": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, ctypes.c_float,
                                               _vp, _vp, _vp, _sz, _vp]),
     "tern_group_gather": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp]),
+    "tern_scale_adamw": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32] + [ctypes.c_float] * 6 + [_vp]),
     "tern_panel_reset": (ctypes.c_int, [_vp, _vp]),
     "tern_panel_add": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "tern_graph_begin": (ctypes.c_int, [_vp]),
@@ -220,6 +221,17 @@ def tern_group_gather(qs, scales, q_group: torch.Tensor, scale_group: torch.Tens
     oa = (_i64 * max(n, 1))(*[int(t.shape[1]) for t in qs])
     rc = lib().tern_group_gather(qa, sa, oa, n, n_in, _ptr(q_group), _ptr(scale_group), _stream(stream))
     _check("tern_group_gather", rc)
+
+
+def tern_scale_adamw(sgrad, scale, m, v, step: int, lr: float, scale_lr: float | None = None, b1: float = 0.9,
+                     b2: float = 0.999, eps: float = 1e-8, wd: float = 0.0, stream=None) -> None:
+    """AdamW step of the per-column scale from its gradient (in place on
+    scale, m, v; scale_lr defaults to lr)."""
+    sl = lr if scale_lr is None else scale_lr
+    rc = lib().tern_scale_adamw(_ptr(sgrad), _ptr(scale), _ptr(m), _ptr(v), int(scale.shape[0]), int(step),
+                                float(lr), float(sl), float(b1), float(b2), float(eps), float(wd),
+                                _stream(stream))
+    _check("tern_scale_adamw", rc)
 
 
 PANEL_COUNTS = ("total", "neg", "zero", "pos", "rail", "dead", "churn", "churn_total", "scale_count")

@@ -57,6 +57,7 @@ const char *tern_status_str(int status) {
         case TERN_ERR_WORKSPACE: return "workspace missing or too small";
         case TERN_ERR_ALIAS: return "output overlaps an input or another output";
         case TERN_ERR_HIP: return "HIP launch failed";
+        case TERN_ERR_VALUE: return "scalar argument out of range (optimizer step or learning rate)";
         default: return "unknown status";
     }
 }

@@ -364,7 +364,44 @@ def pin_panel_brute_and_invariants(o):
         assert o.panel([mats[0], (mats[1][0], None, mats[1][2])], theta, clamp)["churn_frac"] == 0.0
 
 
+def pin_adamw_closed_forms(o):
+    """AdamW on the scale, pinned by closed forms of the textbook update:
+    * a constant gradient from zero moments gives m = g (1 - b1^t) exactly, so
+      the bias-corrected moments are g and g^2 and every step moves the scale
+      by lr g / (|g| + eps) (a zero gradient does not move it);
+    * with zero gradient and weight decay, scale_t = scale_0 (1 - lr wd)^t;
+    * the page's factor scale_lr / lr multiplies the gradient: after one step
+      from zero, m = (1 - b1) g scale_lr / lr;
+    * without eps the step does not depend on that factor (Adam's invariance
+      to a constant gradient scale)."""
+    rng = np.random.default_rng(7)
+    g = np.concatenate([rng.normal(0.0, 3e-2, 12), [0.0, 1e-9, -4.0]])
+    n = g.size
+    s0 = rng.uniform(0.01, 0.1, n)
+    lr, b1, b2, eps = 2e-3, 0.9, 0.999, 1e-8
+    s, m, v = s0.copy(), np.zeros(n), np.zeros(n)
+    for t in range(1, 21):
+        s, m, v = o.scale_adamw(g, s, m, v, t, lr, lr, b1, b2, eps, 0.0)
+        assert np.allclose(m, g * (1.0 - b1 ** t), rtol=1e-12, atol=0.0), t
+        assert np.allclose(v, g * g * (1.0 - b2 ** t), rtol=1e-12, atol=0.0), t
+        want = s0 - t * lr * g / (np.abs(g) + eps)
+        assert np.allclose(s, want, rtol=1e-12, atol=1e-15), t
+    wd = 0.1
+    s, m, v = s0.copy(), np.zeros(n), np.zeros(n)
+    for t in range(1, 6):
+        s, m, v = o.scale_adamw(np.zeros(n), s, m, v, t, lr, lr, b1, b2, eps, wd)
+    assert np.allclose(s, s0 * (1.0 - lr * wd) ** 5, rtol=1e-13, atol=0.0)
+    _, m1, _ = o.scale_adamw(g, s0, np.zeros(n), np.zeros(n), 1, lr, 10.0 * lr, b1, b2, eps, 0.0)
+    assert np.allclose(m1, (1.0 - b1) * g * 10.0, rtol=1e-13, atol=0.0)
+    m0 = rng.normal(0.0, 1e-2, n)
+    v0 = rng.uniform(1e-5, 1e-3, n)
+    a, _, _ = o.scale_adamw(g, s0, m0 * 10.0, v0 * 100.0, 3, lr, 10.0 * lr, b1, b2, 0.0, 0.0)
+    b, _, _ = o.scale_adamw(g, s0, m0, v0, 3, lr, lr, b1, b2, 0.0, 0.0)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-16)
+
+
 ALL_PINS = [pin_tern_golden, pin_tern_properties, pin_pack_golden, pin_pack_roundtrip,
             pin_worked_example, pin_brute_force, pin_sign_matrix_gemm,
             pin_bilinear_identities, pin_finite_differences, pin_dead_zone,
-            pin_sampling_consistent, pin_widen, pin_panel_golden, pin_panel_brute_and_invariants]
+            pin_sampling_consistent, pin_widen, pin_panel_golden, pin_panel_brute_and_invariants,
+            pin_adamw_closed_forms]

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = tl.tern_status_str(code)
         assert s and s != "unknown status"
     assert tl.tern_status_str(-99) == "unknown status"
@@ -241,3 +241,20 @@ def test_group_gather_rejects(L):
     assert g((ctypes.c_void_p * 2)(0x1000000, None), sc, outs, 2, 64, qg, sg, s) == NULL
     assert g(q, sc, outs, 2, 64, P(0x1000000 + 100), sg, s) == ALIAS      # q_group over member 0's q
     assert g(q, sc, outs, 2, 64, qg, P(0x4000000 + 64), s) == ALIAS       # scale_group inside q_group
+
+
+def test_scale_adamw_rejects(L):
+    s = P(0)
+    f = L.tern_scale_adamw
+    sg, sc, m, v = P(0x1000000), P(0x2000000), P(0x3000000), P(0x4000000)
+    hp = [ctypes.c_float(x) for x in (1e-3, 1e-3, 0.9, 0.999, 1e-8, 0.0)]
+    VALUE = -9
+    assert f(sg, sc, m, v, -1, 1, *hp, s) == SHAPE
+    assert f(sg, sc, m, v, 64, 0, *hp, s) == VALUE
+    assert f(sg, sc, m, v, 64, 1, ctypes.c_float(0.0), *hp[1:], s) == VALUE
+    assert f(sg, sc, m, v, 64, 1, hp[0], ctypes.c_float(float("inf")), *hp[2:], s) == VALUE
+    assert f(None, sc, m, v, 64, 1, *hp, s) == NULL
+    assert f(sg, sc, None, v, 64, 1, *hp, s) == NULL
+    assert f(sg, P(0x2000002), m, v, 64, 1, *hp, s) == ALIGN
+    assert f(sg, sc, P(0x2000000 + 128), v, 64, 1, *hp, s) == ALIAS   # m overlaps scale
+    assert f(sg, sc, m, v, 0, 1, *hp, s) == OK                       # nothing to update

@@ -39,6 +39,12 @@ MUTANTS = [
     ("bf16_widen_shift", "uint32_t u = (uint32_t)((const uint16_t *)src)[i] << 16;",
      "uint32_t u = (uint32_t)((const uint16_t *)src)[i] << 15;"),
     ("pack_bit_order", "word |= code << (2 * j);", "word |= code << (30 - 2 * j);"),
+    ("adamw_bias_correction_step", "bc1 = 1.0 - pow(b1, (double)t)", "bc1 = 1.0 - pow(b1, (double)t + 1.0)"),
+    ("adamw_eps_inside_sqrt", "(sqrt(vhat) + eps)", "sqrt(vhat + eps)"),
+    ("adamw_no_one_minus_b1", "m[c] = b1 * m[c] + (1.0 - b1) * g;", "m[c] = b1 * m[c] + g;"),
+    ("adamw_coupled_decay", "const double g = sgrad[c] * scale_lr / lr;",
+     "const double g = sgrad[c] * scale_lr / lr + wd * scale[c];"),
+    ("adamw_dropped_lr_ratio", "const double g = sgrad[c] * scale_lr / lr;", "const double g = sgrad[c];"),
     ("panel_dead_inclusive", "if (a < theta) counts[5] += 1;", "if (a <= theta) counts[5] += 1;"),
     ("panel_rail_uses_theta", "if (a == q_clamp) counts[4] += 1;", "if (a == theta) counts[4] += 1;"),
     ("panel_churn_ignores_sign", "if (prev_tern && prev_tern[k] != t) counts[6] += 1;",
