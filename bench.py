@@ -44,10 +44,12 @@ def parse():
     ap.add_argument("--workload", default="large", choices=["rwkv_small", "mid", "large", "largest"])
     ap.add_argument("--launch", default="graph", choices=["eager", "graph"],
                     help="graph (default): time replays of one recorded step; eager: time the calls")
-    ap.add_argument("--streams", type=int, default=2, choices=[1, 2, 3],
+    ap.add_argument("--streams", default="auto", choices=["auto", "1", "2", "3"],
                     help="graph branches of the recorded step: 1 = one chain; 2 = dW of every projection on "
                          "its own branch; 3 = dX and dW each on their own branch (each branch waits only for "
-                         "its projection's materialize)")
+                         "its projection's materialize); auto = 3 when some projection's forward or dX has "
+                         "fewer 256 x 256 tiles than the GPU has compute units (so that two products share "
+                         "the chip), else 2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="oracle sample: token rows per projection")
     ap.add_argument("--cpu-cols", type=int, default=768, help="oracle sample: output columns per projection")
@@ -159,12 +161,19 @@ def main():
             fork(sx, s0)
 
     eager_ms_per_step = ms_per_step
+    if a.streams == "auto":
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        tiles = lambda m, n: -(-m // 256) * -(-n // 256)
+        small = any(min(tiles(d["n_out"], w.T), tiles(d["n_in"], w.T)) < cus for d in projs)
+        n_streams = 3 if small else 2
+    else:
+        n_streams = int(a.streams)
     if a.launch == "graph":
         # one step recorded on a side stream (plus branch streams), replayed as
         # one launch per step
         gs = torch.cuda.Stream()
         gs.wait_stream(stream)
-        branches = [torch.cuda.Stream() for _ in range(a.streams - 1)]
+        branches = [torch.cuda.Stream() for _ in range(n_streams - 1)]
         tl.tern_graph_begin(gs)
         try:
             record_dag([gs] + branches)
@@ -248,7 +257,7 @@ def main():
         "config": {"workload": w.name, "T": w.T,
                    "projections": [[n, i, o] for n, i, o in w.projs],
                    "theta": w.theta, "q": w.q_law, "scale": w.scale_law, "act": w.act,
-                   "launch": f"hipgraph, {a.streams} branch(es)" if a.launch == "graph" else "eager"},
+                   "launch": f"hipgraph, {n_streams} branch(es)" if a.launch == "graph" else "eager"},
         "eager_ms_per_step": round(eager_ms_per_step, 4),
         "tokens_per_s": round(tokens_per_s, 1),
         "mfma_frac": round(tflops / peak, 4),
