@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 output for the profiles/ folder.
 
     python -m ternary_weight_linear_tern_amd.rocprof_summary stats  <kernel_stats.csv> [title]
+    python -m ternary_weight_linear_tern_amd.rocprof_summary counters <counter_collection.csv> [title]
     python -m ternary_weight_linear_tern_amd.rocprof_summary traffic <fetch_counter_collection.csv> \\
         <write_counter_collection.csv> <workload> <dispatch_steps> [kernel_src]
 
@@ -98,10 +99,53 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, steps: int, kernel_sr
     return out, "\n".join(lines)
 
 
+XCDS = 8          # GRBM_GUI_ACTIVE is reported summed over the 8 XCD instances
+SIMDS = 256 * 4   # MI355X: 256 compute units x 4 SIMDs
+
+
+def counters(path: str, title: str = "") -> str:
+    """Per kernel, medians over its dispatches: duration, shader clock
+    (GRBM_GUI_ACTIVE per XCD over the dispatch's time), MFMA busy
+    (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles, rocprofv3's MfmaUtil), bf16
+    matrix TFLOP/s from SQ_INSTS_VALU_MFMA_MOPS_BF16 (512 flops per op) and the
+    share of wave cycles waiting on LDS.  The counter window of a dispatch
+    outlasts kernels of a few tens of microseconds, so their clock (and MFMA
+    busy) figures are not meaningful; they are marked."""
+    import statistics
+    per = defaultdict(lambda: defaultdict(float))
+    secs = {}
+    for r in csv.DictReader(open(path)):
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        secs[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    rows = defaultdict(list)
+    for key, c in per.items():
+        sec = secs[key]
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        rows[key[1]].append(dict(
+            sec=sec, clk=gui / sec / 1e9 if sec else 0.0,
+            busy=100.0 * c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * SIMDS) if gui else 0.0,
+            tf=c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512.0 / sec / 1e12 if sec else 0.0,
+            wl=100.0 * c.get("SQ_WAIT_INST_LDS", 0.0) / c["SQ_WAVE_CYCLES"] if c.get("SQ_WAVE_CYCLES") else 0.0))
+    out = [f"# {title}" if title else "# kernel counters", "",
+           "| kernel | dispatches | median us | clock GHz | MFMA busy % | bf16 MFMA TFLOP/s | LDS wait % of wave cycles |",
+           "|---|---|---|---|---|---|---|"]
+    for name, rs in sorted(rows.items(), key=lambda kv: -sum(r["sec"] for r in kv[1])):
+        med = {k: statistics.median(r[k] for r in rs) for k in rs[0]}
+        short = med["sec"] < 50e-6
+        clk = "(short)" if short else f"{med['clk']:.2f}"
+        busy = "(short)" if short else f"{med['busy']:.1f}"
+        out.append(f"| {name[:80]} | {len(rs)} | {1e6 * med['sec']:.1f} | {clk} | {busy} | {med['tf']:.0f} | "
+                   f"{med['wl']:.1f} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     cmd = sys.argv[1]
     if cmd == "stats":
         print(stats(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
+    elif cmd == "counters":
+        print(counters(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
     elif cmd == "traffic":
         src = sys.argv[6] if len(sys.argv) > 6 else os.path.join(PKG, "csrc", "tern_kernels.hip")
         data, text = traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), src)
