@@ -2,6 +2,7 @@
 
     python -m ternary_weight_linear_tern_amd.rocprof_summary stats  <kernel_stats.csv> [title]
     python -m ternary_weight_linear_tern_amd.rocprof_summary counters <counter_collection.csv> [title]
+    python -m ternary_weight_linear_tern_amd.rocprof_summary ratios <counter_collection.csv> [title]
     python -m ternary_weight_linear_tern_amd.rocprof_summary traffic <fetch_counter_collection.csv> \\
         <write_counter_collection.csv> <workload> <dispatch_steps> [kernel_src]
 
@@ -140,10 +141,42 @@ def counters(path: str, title: str = "") -> str:
     return "\n".join(out)
 
 
+def ratios(path: str, title: str = "") -> str:
+    """Per kernel, the median over its dispatches of every counter in the
+    file divided by SQ_WAVE_CYCLES (wave-cycle shares), and of the icache
+    miss rate when SQC_ICACHE_HITS / SQC_ICACHE_MISSES are present."""
+    import statistics
+    per = defaultdict(lambda: defaultdict(float))
+    for r in csv.DictReader(open(path)):
+        per[(r["Dispatch_Id"], r["Kernel_Name"])][r["Counter_Name"]] += float(r["Counter_Value"])
+    rows = defaultdict(list)
+    for (_, name), c in per.items():
+        d = {}
+        w = c.get("SQ_WAVE_CYCLES")
+        for k, v in c.items():
+            if w and k.startswith("SQ_") and k != "SQ_WAVE_CYCLES":
+                d[k + " / SQ_WAVE_CYCLES"] = v / w
+        if "SQC_ICACHE_HITS" in c:
+            tot = c["SQC_ICACHE_HITS"] + c.get("SQC_ICACHE_MISSES", 0.0)
+            d["icache miss rate"] = c.get("SQC_ICACHE_MISSES", 0.0) / tot if tot else 0.0
+        rows[name].append(d)
+    keys = sorted({k for rs in rows.values() for d in rs for k in d})
+    out = [f"# {title}" if title else "# counter ratios", "", "| kernel | " + " | ".join(keys) + " |",
+           "|---|" + "---|" * len(keys)]
+    for name, rs in sorted(rows.items()):
+        if not any(rs):
+            continue
+        vals = [f"{statistics.median(d.get(k, 0.0) for d in rs):.4f}" for k in keys]
+        out.append(f"| {name[:60]} | " + " | ".join(vals) + " |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     cmd = sys.argv[1]
     if cmd == "stats":
         print(stats(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
+    elif cmd == "ratios":
+        print(ratios(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
     elif cmd == "counters":
         print(counters(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
     elif cmd == "traffic":
