@@ -225,6 +225,10 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom_kernels,
                 "flops_per_step": gemm_flops[dom], "ms_per_step": round(part_ms[dom], 4)}
+    if traffic is not None:
+        # the same kernel against the HBM roof: its counted bytes over its time
+        gbs = traffic / (part_ms[dom] * 1e-3) / 1e9
+        roofline.update(hbm_gbs=round(gbs, 1), hbm_peak_gbs=PEAK_HBM_GBS, hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
 
     if a.copy_calibration:
         # one elementwise kernel per copy: reads and writes COPY_BYTES once
