@@ -63,7 +63,7 @@ def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr, flush=True)
+              "(the library has no multi-GPU path; sharding is described, not built)", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import numpy as np
