@@ -44,12 +44,13 @@ def parse():
     ap.add_argument("--workload", default="large", choices=["rwkv_small", "mid", "large", "largest"])
     ap.add_argument("--launch", default="graph", choices=["eager", "graph"],
                     help="graph (default): time replays of one recorded step; eager: time the calls")
-    ap.add_argument("--streams", default="auto", choices=["auto", "1", "2", "3"],
+    ap.add_argument("--streams", default="auto", choices=["auto", "1", "2", "3", "p3"],
                     help="graph branches of the recorded step: 1 = one chain; 2 = dW of every projection on "
                          "its own branch; 3 = dX and dW each on their own branch (each branch waits only for "
-                         "its projection's materialize); auto = 3 when some projection's forward or dX has "
-                         "fewer 256 x 256 tiles than the GPU has compute units (so that two products share "
-                         "the chip), else 2")
+                         "its projection's materialize); p3 = whole projections (materialize, forward, dX, "
+                         "dW) dealt over three branches; auto = p3 when some projection's forward or dX has "
+                         "fewer 256 x 256 tiles than the GPU has compute units (small products, whose "
+                         "latencies then overlap), else 2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="oracle sample: token rows per projection")
     ap.add_argument("--cpu-cols", type=int, default=768, help="oracle sample: output columns per projection")
@@ -160,14 +161,37 @@ def main():
         for sx in streams[1:]:
             fork(sx, s0)
 
+    def record_projections(streams):
+        """The step as independent chains: projection j's materialize, forward,
+        dX and dW in order on branch j % len(streams)."""
+        s0 = streams[0]
+
+        def fork(src, dst):
+            e = torch.cuda.Event()
+            e.record(src)
+            dst.wait_event(e)
+
+        for sx in streams[1:]:
+            fork(s0, sx)
+        for j, d in enumerate(projs):
+            st = streams[j % len(streams)]
+            tl.tern_materialize(d["q"], d["theta"], d["packed"], st)
+            tl.tern_linear_fwd(d["X"], d["packed"], d["scale"], d["Y"], st)
+            tl.tern_linear_bwd_dx(d["dY"], d["packed"], d["scale"], d["dX"], stream=st)
+            tl.tern_linear_bwd_dw(d["X"], d["dY"], d["packed"], d["scale"], d["gq"], d["sgrad"], d["ws"], st)
+        for sx in streams[1:]:
+            fork(sx, s0)
+
     eager_ms_per_step = ms_per_step
     if a.streams == "auto":
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         tiles = lambda m, n: -(-m // 256) * -(-n // 256)
         small = any(min(tiles(d["n_out"], w.T), tiles(d["n_in"], w.T)) < cus for d in projs)
-        n_streams = 3 if small else 2
+        mode = "p3" if small else "2"
     else:
-        n_streams = int(a.streams)
+        mode = a.streams
+    by_projection = mode.startswith("p")
+    n_streams = int(mode[1:] if by_projection else mode)
     if a.launch == "graph":
         # one step recorded on a side stream (plus branch streams), replayed as
         # one launch per step
@@ -176,7 +200,7 @@ def main():
         branches = [torch.cuda.Stream() for _ in range(n_streams - 1)]
         tl.tern_graph_begin(gs)
         try:
-            record_dag([gs] + branches)
+            (record_projections if by_projection else record_dag)([gs] + branches)
         finally:
             graph = tl.tern_graph_end(gs)
         try:
@@ -261,7 +285,8 @@ def main():
         "config": {"workload": w.name, "T": w.T,
                    "projections": [[n, i, o] for n, i, o in w.projs],
                    "theta": w.theta, "q": w.q_law, "scale": w.scale_law, "act": w.act,
-                   "launch": f"hipgraph, {n_streams} branch(es)" if a.launch == "graph" else "eager"},
+                   "launch": (f"hipgraph, {n_streams} branch(es)" + (" by projection" if by_projection else ""))
+                   if a.launch == "graph" else "eager"},
         "eager_ms_per_step": round(eager_ms_per_step, 4),
         "tokens_per_s": round(tokens_per_s, 1),
         "mfma_frac": round(tflops / peak, 4),

@@ -149,10 +149,12 @@ def test_graph_invalid_call_records_nothing():
         tl.tern_graph_destroy(g)
 
 
-def test_graph_branches_match_eager():
-    """A recording on three streams (forward on the first, dX and dW on
-    branches that fork after each materialize and rejoin at the end) replays
-    to the eager results bit for bit."""
+@pytest.mark.parametrize("layout", ["products", "projections"])
+def test_graph_branches_match_eager(layout):
+    """A recording on three streams replays to the eager results bit for bit:
+    products (forward on the first stream, dX and dW on branches that fork
+    after each materialize) or projections (each projection's whole chain on
+    one of the streams); the branches rejoin the first stream at the end."""
     ps = [synth.make_inputs(T, i, o, act="bf16", config_id=730 + n) for n, (T, i, o) in enumerate(SHAPES)]
     projs = [DeviceProjection(p) for p in ps]
     for d in projs:
@@ -169,24 +171,31 @@ def test_graph_branches_match_eager():
     try:
         fork(s0, s1)
         fork(s0, s2)
-        for d in projs:
-            tl.tern_materialize(d.q, d.p.theta, d.packed, s0)
-            fork(s0, s1)
-            fork(s0, s2)
-            tl.tern_linear_fwd(d.X, d.packed, d.scale, d.Y, s0)
-            tl.tern_linear_bwd_dx(d.dY, d.packed, d.scale, d.dX, stream=s1)
-            tl.tern_linear_bwd_dw(d.X, d.dY, d.packed, d.scale, d.gq, d.sgrad, d.ws, s2)
+        for j, d in enumerate(projs):
+            if layout == "products":
+                tl.tern_materialize(d.q, d.p.theta, d.packed, s0)
+                fork(s0, s1)
+                fork(s0, s2)
+                tl.tern_linear_fwd(d.X, d.packed, d.scale, d.Y, s0)
+                tl.tern_linear_bwd_dx(d.dY, d.packed, d.scale, d.dX, stream=s1)
+                tl.tern_linear_bwd_dw(d.X, d.dY, d.packed, d.scale, d.gq, d.sgrad, d.ws, s2)
+            else:
+                st = (s0, s1, s2)[j % 3]
+                tl.tern_materialize(d.q, d.p.theta, d.packed, st)
+                tl.tern_linear_fwd(d.X, d.packed, d.scale, d.Y, st)
+                tl.tern_linear_bwd_dx(d.dY, d.packed, d.scale, d.dX, stream=st)
+                tl.tern_linear_bwd_dw(d.X, d.dY, d.packed, d.scale, d.gq, d.sgrad, d.ws, st)
         fork(s1, s0)
         fork(s2, s0)
     finally:
         g = tl.tern_graph_end(s0)
     try:
         for rep in range(3):
-            log(f"graph branches: replay {rep}")
+            log(f"graph branches ({layout}): replay {rep}")
             _poison(projs, s0)
             s0.synchronize()
             tl.tern_graph_launch(g, s0)
             s0.synchronize()
-            _same(_outputs(projs), eager, f"branched replay {rep}")
+            _same(_outputs(projs), eager, f"branched ({layout}) replay {rep}")
     finally:
         tl.tern_graph_destroy(g)
