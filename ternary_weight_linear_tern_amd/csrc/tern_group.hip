@@ -6,7 +6,8 @@
 // kernel writes the group's q and scale from the members' buffers, and the
 // single-projection entry points do the rest.  Each thread writes one 16-byte
 // span of a q_group row (or the ragged end of one), finding each byte's member
-// from the column offsets; a second grid dimension block copies the scales.
+// from the column offsets (one 16-byte copy when the widths allow it); a second
+// grid dimension copies the scales.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -25,6 +26,10 @@ struct GroupSrc {
     int n;
 };
 
+// VEC: every member's width is a multiple of 16 and every q is 16-byte
+// aligned, so a 16-byte span of a q_group row lies in one member and moves
+// with one load and one store.
+template <bool VEC>
 __global__ __launch_bounds__(256) void group_gather_kernel(GroupSrc s, int64_t in, int8_t *__restrict__ qg,
                                                            float *__restrict__ sg) {
     const int64_t total = s.off[s.n];
@@ -42,6 +47,11 @@ __global__ __launch_bounds__(256) void group_gather_kernel(GroupSrc s, int64_t i
         int i = 0;
         while (i + 1 < s.n && c0 >= s.off[i + 1]) i++;
         int8_t *dst = qg + r * total + c0;
+        if constexpr (VEC) {
+            const int64_t w = s.off[i + 1] - s.off[i];
+            *(uint4 *)dst = *(const uint4 *)(s.q[i] + r * w + (c0 - s.off[i]));
+            continue;
+        }
         for (int j = 0; j < 16 && c0 + j < total; j++) {
             const int64_t c = c0 + j;
             while (i + 1 < s.n && c >= s.off[i + 1]) i++;
@@ -87,8 +97,14 @@ int tern_group_gather(const int8_t *const *q, const float *const *scale, const i
     const int64_t n16 = in * ((total + 15) / 16);
     int64_t blocks = (n16 > total ? n16 : total) / 256 + 1;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(gdev::group_gather_kernel, dim3((unsigned)blocks, 2), dim3(256), 0, (hipStream_t)stream, s,
-                       in, q_group, scale_group);
+    bool vec = ((uintptr_t)q_group & 15u) == 0;
+    for (int i = 0; i < n; i++) vec = vec && out[i] % 16 == 0 && ((uintptr_t)q[i] & 15u) == 0;
+    if (vec)
+        hipLaunchKernelGGL(gdev::group_gather_kernel<true>, dim3((unsigned)blocks, 2), dim3(256), 0,
+                           (hipStream_t)stream, s, in, q_group, scale_group);
+    else
+        hipLaunchKernelGGL(gdev::group_gather_kernel<false>, dim3((unsigned)blocks, 2), dim3(256), 0,
+                           (hipStream_t)stream, s, in, q_group, scale_group);
     return hipGetLastError() == hipSuccess ? TERN_OK : TERN_ERR_HIP;
 }
 
