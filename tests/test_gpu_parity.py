@@ -253,6 +253,32 @@ def test_parity_largest_sampled(o, proj):
     sampled_case(o, "largest", proj)
 
 
+def test_parity_operands_beyond_4gib(o):
+    """X of 4 GiB (T = 262144 tokens x 8192 bf16) and dX of 8 GiB: tile base
+    offsets far past 2^32 bytes, through the same kernels as the benchmark
+    (the 256 x 256 forward / dX and the split-K dW); sampled rows and columns
+    against the oracle."""
+    T, n_in, n_out = 262144, 8192, 256
+    log(f"parity beyond 4 GiB: T={T} in={n_in} out={n_out}")
+    p = synth.make_inputs(T, n_in, n_out, act="bf16", config_id=305)
+    d = DeviceProjection(p)
+    d.step()
+    torch.cuda.synchronize()
+    rows = np.union1d(synth.sample_indices(synth.stream_seed(83, T, n_in, 0), 24, T), [0, T // 2, T - 1])
+    cols = np.union1d(synth.sample_indices(synth.stream_seed(83, T, n_out, 1), 3, n_out), [n_out - 1])
+    rt, ct = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    errs = dict(Y=rel_l2(d.Y[rt].cpu().numpy(), o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows)),
+                dX=rel_l2(d.dX[rt].cpu().numpy(), o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows)))
+    _, gq, sg = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
+    errs["gq"] = rel_l2(d.gq[:, ct].cpu().numpy(), gq)
+    errs["sgrad"] = rel_l2(d.sgrad[ct].cpu().numpy(), sg)
+    log(f"  relL2 {errs}")
+    for k, e in errs.items():
+        assert e <= tol_for("bf16"), f"{k} relL2 {e:.3e}"
+    pk = tl.packed_canonical(d.packed, n_in, n_out).cpu().numpy().view(np.uint32)
+    assert np.array_equal(pk, o.pack(o.tern(p.q, p.theta))), "packing differs"
+
+
 def _frag_copy(tern, M_is_in):
     """The fragment-ordered copy of include/tern.h, built from a tern matrix
     [in, out] of {-1, 0, 1}: operand A[m][k] = tern[k][m] (forward copy,
