@@ -32,18 +32,56 @@ def o():
     return oracle.get()
 
 
+def _abs_act(a: np.ndarray) -> np.ndarray:
+    """|a| for an activation array (bf16 bit patterns: clear the sign bit)."""
+    return a & np.uint16(0x7FFF) if a.dtype == np.uint16 else np.abs(a)
+
+
+def check_elements(o, p, got, want, rows=None, cols=None, tag=""):
+    """Each element within its own rounding bound.
+
+    With the inputs exact in both computations, the device result differs from
+    the oracle's f64 value only by the roundings of its fp32 sums and of the
+    operand it rounds:  |got - want| <= (u_op + 2 (K + 2) 2^-24) * S,  where
+    S = sum |a| |b| over the element's products (the oracle's own product of
+    the absolute values), K the length of that sum (in for Y, out for dX, T for
+    gq and sgrad) and u_op = 2^-8 for dX with bf16 activations (its scale is
+    rounded to bf16 inside the operand), else 0.  A misplaced or stale element
+    is off by about sqrt(K) typical terms, far beyond this bound, even where
+    one element barely moves the relative L2 norm.
+    """
+    T, n_in = p.X.shape
+    n_out = p.q.shape[1]
+    aX, adY = _abs_act(p.X), _abs_act(p.dY)
+    aq = np.minimum(np.abs(p.q.astype(np.int16)), 127).astype(np.int8)
+    asc = np.abs(p.scale)
+    S = dict(Y=o.linear_fwd(aX, aq, p.theta, asc, rows=rows),
+             dX=o.linear_dx(adY, aq, p.theta, asc, rows=rows))
+    _, S["gq"], S["sgrad"] = o.linear_wgrad(aX, adY, aq, p.theta, asc, cols=cols)
+    u_op = dict(Y=0.0, dX=2.0 ** -8 if p.act == "bf16" else 0.0, gq=0.0, sgrad=0.0)
+    K = dict(Y=n_in, dX=n_out, gq=T, sgrad=T)
+    for k in ("Y", "dX", "gq", "sgrad"):
+        err = np.abs(np.asarray(got[k], dtype=np.float64) - want[k])
+        bound = (u_op[k] + 2.0 * (K[k] + 2) * 2.0 ** -24) * S[k] + 1e-30
+        bad = np.argwhere(err > bound)
+        if bad.size:
+            i = tuple(bad[0])
+            raise AssertionError(f"{tag}: {k}{list(i)} off by {err[i]:.3e} > bound {bound[i]:.3e} "
+                                 f"({bad.shape[0]} elements out of bound)")
+
+
 def check_full(o, p, res, tag):
     tol = tol_for(p.act)
-    Y = o.linear_fwd(p.X, p.q, p.theta, p.scale)
-    dX = o.linear_dx(p.dY, p.q, p.theta, p.scale)
-    _, gq, sg = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale)
+    want = dict(Y=o.linear_fwd(p.X, p.q, p.theta, p.scale),
+                dX=o.linear_dx(p.dY, p.q, p.theta, p.scale))
+    _, want["gq"], want["sgrad"] = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale)
     want_pk = o.pack(o.tern(p.q, p.theta))
     assert np.array_equal(res["packed"], want_pk), f"{tag}: packing differs"
-    errs = dict(Y=rel_l2(res["Y"], Y), dX=rel_l2(res["dX"], dX), gq=rel_l2(res["gq"], gq),
-                sgrad=rel_l2(res["sgrad"], sg))
+    errs = {k: rel_l2(res[k], want[k]) for k in ("Y", "dX", "gq", "sgrad")}
     log(f"  {tag}: relL2 {errs}")
     for k, e in errs.items():
         assert e <= tol, f"{tag}: {k} relL2 {e:.3e} > {tol:.1e}"
+    check_elements(o, p, res, want, tag=tag)
     return errs
 
 
@@ -129,6 +167,21 @@ def test_parity_rwkv_small_full(o, proj):
     check_full(o, p, d.results(), f"rwkv_small/{w.projs[proj][0]}")
 
 
+# Shapes that the planner serves with 128-row tiles (the first) and with the
+# persistent 256-row tiles (the other two: dW split in four, and unsplit) in
+# all three products, for both activation types, ragged in every dimension
+# (1000 = 7*128 + 104, 1032 = 4*256 + 8, 4000 = 15*256 + 160, 2056 = 8*256 + 8),
+# compared element by element.
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("T,n_in,n_out", [(1000, 1032, 1032), (4000, 1032, 1032), (2056, 2056, 2056)])
+def test_parity_big_tiles_full(o, T, n_in, n_out, act):
+    log(f"parity big tiles (full) T={T} in={n_in} out={n_out} act={act}")
+    p = synth.make_inputs(T, n_in, n_out, act=act, config_id=870, proj_id=T + n_in)
+    d = DeviceProjection(p)
+    d.step()
+    check_full(o, p, d.results(), f"T={T} in={n_in} out={n_out} {act}")
+
+
 def test_y_bf16_output(o):
     log("forward with bf16 Y")
     p = synth.make_inputs(260, 136, 520, act="bf16", config_id=302)
@@ -199,14 +252,16 @@ def sampled_case(o, wname, proj):
     sgg = d.sgrad[ct].cpu().numpy()
     pk = tl.packed_canonical(d.packed, n_in, n_out).cpu().numpy().view(np.uint32)
     assert np.array_equal(pk, o.pack(o.tern(p.q, p.theta))), "packing differs"
-    Y = o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows)
-    dX = o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows)
-    _, gq, sg = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
-    errs = dict(Y=rel_l2(Yg, Y), dX=rel_l2(dXg, dX), gq=rel_l2(gqg, gq), sgrad=rel_l2(sgg, sg))
+    want = dict(Y=o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows),
+                dX=o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows))
+    _, want["gq"], want["sgrad"] = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
+    got = dict(Y=Yg, dX=dXg, gq=gqg, sgrad=sgg)
+    errs = {k: rel_l2(got[k], want[k]) for k in got}
     log(f"  relL2 {errs}")
     tol = tol_for(p.act)
     for k, e in errs.items():
         assert e <= tol, f"{wname}/{name}: {k} relL2 {e:.3e} > {tol:.1e}"
+    check_elements(o, p, got, want, rows=rows, cols=cols, tag=f"{wname}/{name}")
 
 
 # Shapes on which every product takes the 256 x 256 kernels with ragged edges:
@@ -223,14 +278,16 @@ def test_parity_tile256_ragged_sampled(o, T, n_in, n_out):
     cols = np.union1d(synth.sample_indices(synth.stream_seed(78, T, n_out, 1), 14, n_out), [0, n_out - 1])
     rt = torch.from_numpy(rows).cuda()
     ct = torch.from_numpy(cols).cuda()
-    errs = dict(Y=rel_l2(d.Y[rt].cpu().numpy(), o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows)),
-                dX=rel_l2(d.dX[rt].cpu().numpy(), o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows)))
-    _, gq, sg = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
-    errs["gq"] = rel_l2(d.gq[:, ct].cpu().numpy(), gq)
-    errs["sgrad"] = rel_l2(d.sgrad[ct].cpu().numpy(), sg)
+    want = dict(Y=o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows),
+                dX=o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows))
+    _, want["gq"], want["sgrad"] = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
+    got = dict(Y=d.Y[rt].cpu().numpy(), dX=d.dX[rt].cpu().numpy(), gq=d.gq[:, ct].cpu().numpy(),
+               sgrad=d.sgrad[ct].cpu().numpy())
+    errs = {k: rel_l2(got[k], want[k]) for k in got}
     log(f"  relL2 {errs}")
     for k, e in errs.items():
         assert e <= tol_for("bf16"), f"{k} relL2 {e:.3e}"
+    check_elements(o, p, got, want, rows=rows, cols=cols, tag=f"T={T} in={n_in} out={n_out}")
     # bf16 Y from the same kernel is the round-to-nearest-even of its fp32 Y
     Yb = torch.empty((T, n_out), dtype=torch.bfloat16, device="cuda")
     tl.tern_linear_fwd(d.X, d.packed, d.scale, Yb)
@@ -267,14 +324,16 @@ def test_parity_operands_beyond_4gib(o):
     rows = np.union1d(synth.sample_indices(synth.stream_seed(83, T, n_in, 0), 24, T), [0, T // 2, T - 1])
     cols = np.union1d(synth.sample_indices(synth.stream_seed(83, T, n_out, 1), 3, n_out), [n_out - 1])
     rt, ct = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
-    errs = dict(Y=rel_l2(d.Y[rt].cpu().numpy(), o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows)),
-                dX=rel_l2(d.dX[rt].cpu().numpy(), o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows)))
-    _, gq, sg = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
-    errs["gq"] = rel_l2(d.gq[:, ct].cpu().numpy(), gq)
-    errs["sgrad"] = rel_l2(d.sgrad[ct].cpu().numpy(), sg)
+    want = dict(Y=o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows),
+                dX=o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows))
+    _, want["gq"], want["sgrad"] = o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
+    got = dict(Y=d.Y[rt].cpu().numpy(), dX=d.dX[rt].cpu().numpy(), gq=d.gq[:, ct].cpu().numpy(),
+               sgrad=d.sgrad[ct].cpu().numpy())
+    errs = {k: rel_l2(got[k], want[k]) for k in got}
     log(f"  relL2 {errs}")
     for k, e in errs.items():
         assert e <= tol_for("bf16"), f"{k} relL2 {e:.3e}"
+    check_elements(o, p, got, want, rows=rows, cols=cols, tag=f"T={T} in={n_in} out={n_out}")
     pk = tl.packed_canonical(d.packed, n_in, n_out).cpu().numpy().view(np.uint32)
     assert np.array_equal(pk, o.pack(o.tern(p.q, p.theta))), "packing differs"
 
