@@ -659,8 +659,12 @@ void gemm_kernel(GemmArgs g) {
 // (across tile and split boundaries), and the MFMA fragments come from
 // ds_read_b64_tr_b16 transposing reads.  One barrier per chunk, before the
 // chunk's last K quarter: past it no wave reads the chunk's stage any more, so
-// the loads of the chunk after the next one go out right there, and the last
-// quarter's MFMAs run while the next chunk's first fragments load.
+// the refill with the chunk after the next one starts there.  Its X half goes
+// out during the last quarter's MFMAs and its dY half during the next chunk's
+// first quarter, one load per two MFMAs: a CU's 64 refill loads need about as
+// many address-unit cycles as two quarters of MFMAs, and packed into one
+// quarter they stalled the waves' issue (4 % slower dW).  The next barrier
+// waits for both halves.
 // Epilogue, one split: gq = G * scale[c], and the tile's per-column sum of
 // G * tern over its 256 rows (fixed order) into the partial table; several
 // splits: the split's raw G, summed by dw_reduce_kernel.
@@ -871,19 +875,18 @@ void gemm_dw_kernel(GemmArgs g) {
             }
         }
     };
-    // The 16 MFMAs of the last K quarter with, after each, one of the 16
-    // loads (8 per operand) that refill stage s with the chunk after the next
-    // and one of the next chunk's quarter-0 reads, then the step to that chunk.
+    // The 16 MFMAs of the last K quarter with the X half of the refill of
+    // stage s with the chunk after the next (one load per two MFMAs) and, after
+    // each MFMA, one of the next chunk's quarter-0 reads.
     auto p_mma_dma16 = [&](const u32x4 (&a)[4], const u32x4 (&b)[4], int s) __attribute__((always_inline)) {
         char *st = w_lds + s * W_STAGE;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(ia, nrec(irem, lda)), rb = make_rsrc_n(ib, nrec(irem, ldb));
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(ia, nrec(irem, lda));
         auto one = [&](auto k_c) __attribute__((always_inline)) {
             constexpr int K = decltype(k_c)::value;
             constexpr int i = K >> 2, j = K & 3;
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i]),
                                                                 __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
-            if constexpr (K < 8) da.template issue<K & 7>(ra, st, wave);
-            else db.template issue<K & 7>(rb, st + W_OP, wave);
+            if constexpr (K % 2 == 1) da.template issue<K / 2>(ra, st, wave);
         };
         one(std::integral_constant<int, 0>{}); one(std::integral_constant<int, 1>{});
         one(std::integral_constant<int, 2>{}); one(std::integral_constant<int, 3>{});
@@ -898,7 +901,44 @@ void gemm_dw_kernel(GemmArgs g) {
 #pragma unroll
         for (int k = 0; k < 16; k++) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (k % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // first K quarter of a chunk: its 16 MFMAs with the B half of the refill
+    // begun in the previous chunk's last quarter (stage sc ^ 1, one load per
+    // two MFMAs), then the issue side's step to the next chunk
+    auto p_mma_dmab = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) __attribute__((always_inline)) {
+        char *st = w_lds + (sc ^ 1) * W_STAGE;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc_n(ib, nrec(irem, ldb));
+        auto one = [&](auto k_c) __attribute__((always_inline)) {
+            constexpr int K = decltype(k_c)::value;
+            constexpr int i = K >> 2, j = K & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                                __builtin_bit_cast(bf16x8, b[j]), acc[i][j], 0, 0, 0);
+            if constexpr (K % 2 == 1) db.template issue<K / 2>(rb, st + W_OP, wave);
+        };
+        one(std::integral_constant<int, 0>{});
+        one(std::integral_constant<int, 1>{});
+        one(std::integral_constant<int, 2>{});
+        one(std::integral_constant<int, 3>{});
+        one(std::integral_constant<int, 4>{});
+        one(std::integral_constant<int, 5>{});
+        one(std::integral_constant<int, 6>{});
+        one(std::integral_constant<int, 7>{});
+        one(std::integral_constant<int, 8>{});
+        one(std::integral_constant<int, 9>{});
+        one(std::integral_constant<int, 10>{});
+        one(std::integral_constant<int, 11>{});
+        one(std::integral_constant<int, 12>{});
+        one(std::integral_constant<int, 13>{});
+        one(std::integral_constant<int, 14>{});
+        one(std::integral_constant<int, 15>{});
+#pragma unroll
+        for (int k = 0; k < 16; k++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (k % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -906,11 +946,12 @@ void gemm_dw_kernel(GemmArgs g) {
     };
 
     // one chunk (fragment slot SL): run K quarters 0 .. W_Q - 2, reading each
-    // next quarter's fragments during the current one's MFMAs; wait for the
-    // next chunk's loads in every wave (nothing was issued after them), pass
-    // the barrier, refill this chunk's stage, read the next chunk's quarter 0
-    // fragments, and run the last quarter's MFMAs (its fragments are already
-    // in registers).
+    // next quarter's fragments during the current one's MFMAs (quarter 0 also
+    // issues the dY half of the previous chunk's refill); wait for the next
+    // chunk's loads in every wave (nothing was issued after them), pass the
+    // barrier, start the refill of this chunk's stage, read the next chunk's
+    // quarter 0 fragments, and run the last quarter's MFMAs (its fragments are
+    // already in registers).
     auto chunk = [&](auto sl_c) __attribute__((always_inline)) {
         constexpr int SL = decltype(sl_c)::value, SL1 = SL ^ 1;
         const char *st = w_lds + sc * W_STAGE;
@@ -919,16 +960,19 @@ void gemm_dw_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < W_Q - 1; q++) {
             w_read_q(st, qa[(q + 1) & 1], qb[(q + 1) & 1], wm, wn, lane, q + 1);
-            if (q == 0) p_mma(acc, f0a[SL], f0b[SL]);
-            else p_mma(acc, qa[q & 1], qb[q & 1]);
-            // one MFMA, then one of the next quarter's 16 transposing reads:
-            // the reads issue in the MFMAs' shadow instead of as a burst
+            if (q == 0) {
+                p_mma_dmab(f0a[SL], f0b[SL]);
+            } else {
+                p_mma(acc, qa[q & 1], qb[q & 1]);
+                // one MFMA, then one of the next quarter's 16 transposing reads:
+                // the reads issue in the MFMAs' shadow instead of as a burst
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                for (int i = 0; i < 16; i++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
         w_barrier<0>();
         // every wave has read all of this chunk's stage: its refill with the
@@ -941,7 +985,8 @@ void gemm_dw_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: chunks 0 and 1 in flight; the first one's quarter 0 fragments
+    // prologue: chunk 0 and the X half of chunk 1 in flight; the first one's
+    // quarter 0 fragments
     auto issue_all = [&](int s) __attribute__((always_inline)) {
         char *st = w_lds + s * W_STAGE;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(ia, nrec(irem, lda)), rb = make_rsrc_n(ib, nrec(irem, ldb));
@@ -964,8 +1009,19 @@ void gemm_dw_kernel(GemmArgs g) {
         next_chunk();
     };
     issue_all(0);
-    issue_all(1);
-    w_barrier<2 * W_DR>();
+    {   // A half of chunk 1; its B half goes out in chunk 0's first quarter
+        char *st = w_lds + W_STAGE;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(ia, nrec(irem, lda));
+        da.template issue<0>(ra, st, wave);
+        da.template issue<1>(ra, st, wave);
+        da.template issue<2>(ra, st, wave);
+        da.template issue<3>(ra, st, wave);
+        da.template issue<4>(ra, st, wave);
+        da.template issue<5>(ra, st, wave);
+        da.template issue<6>(ra, st, wave);
+        da.template issue<7>(ra, st, wave);
+    }
+    w_barrier<W_DR>();
     w_read_q(w_lds, f0a[0], f0b[0], wm, wn, lane, 0);
     zero_acc();
     while (cv) {
