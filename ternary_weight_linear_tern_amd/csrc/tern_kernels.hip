@@ -1184,7 +1184,7 @@ __device__ __forceinline__ void derive_block(const int8_t *__restrict__ q, int64
         blk[row * LD + w] = (r < in && wc < wpr) ? tern_word<VEC>(q, out, theta, r, wc) : 0u;
     }
     __syncthreads();
-    const int64_t M = DXOP ? in : out, K = DXOP ? out : in;
+    const int64_t M = DXOP ? in : out;
 #pragma unroll
     for (int o = t; o < 512 * D_G; o += 256) {
         const int sl = o >> 9, d = o & 511;            // chunk within the group, word within the chunk
@@ -1195,16 +1195,30 @@ __device__ __forceinline__ void derive_block(const int8_t *__restrict__ q, int64
         uint32_t word = 0;
         if (tile * 256 + ml < M) {
 #pragma unroll
-            for (int kk = 0; kk < 2; kk++)
+            for (int kk = 0; kk < 2; kk++) {
+                const int k0 = sl * 32 + kk * 16 + (lane >> 5) * 8;   // first of the word's 8 k in the group
+                uint32_t x;   // code of k0 + e at bits 4e and 4e + 1
+                if constexpr (DXOP) {
+                    // the 8 codes are adjacent in one canonical word of row ml
+                    // (k0 % 16 is 0 or 8): spread 2-bit groups to nibbles
+                    x = (blk[ml * LD + (k0 >> 4)] >> (2 * (k0 & 15))) & 0xFFFFu;
+                    x = (x | (x << 8)) & 0x00FF00FFu;
+                    x = (x | (x << 4)) & 0x0F0F0F0Fu;
+                    x = (x | (x << 2)) & 0x33333333u;
+                } else {
+                    // column ml of 8 consecutive rows
+                    const uint32_t *col = blk + k0 * LD + (ml >> 4);
+                    const int sh = 2 * (ml & 15);
+                    x = 0u;
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    const int kl = sl * 32 + kk * 16 + (lane >> 5) * 8 + e;   // k within the group
-                    if (sg * (32 * D_G) + kl >= K) continue;
-                    const int br = DXOP ? ml : kl, bc = DXOP ? kl : ml;    // block row, block column
-                    const uint32_t code = (blk[br * LD + (bc >> 4)] >> (2 * (bc & 15))) & 3u;
-                    const uint32_t nz = code & 1u, neg = (code >> 1) & nz;
-                    word |= ((nz << 1) | (neg << 3)) >> kk << (4 * e);
+                    for (int e = 0; e < 8; e++) x |= ((col[e * LD] >> sh) & 3u) << (4 * e);
                 }
+                // nonzero flag (bit 0 of a code) to bit 1 of the nibble, sign (bit 1,
+                // when nonzero) to bit 3; one lower for the second K half.  Rows and
+                // columns past the matrix are zero words in the block.
+                const uint32_t nz = x & 0x11111111u, neg = (x >> 1) & nz;
+                word |= ((nz << 1) | (neg << 3)) >> kk;
+            }
         }
         frag[(tile * nch + chunk) * 512 + d] = word;
     }
