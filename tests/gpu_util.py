@@ -79,3 +79,48 @@ class DeviceProjection:
         pk = tl.packed_canonical(self.packed, self.n_in, self.n_out)
         return dict(packed=pk.cpu().numpy().view(np.uint32), Y=Y.cpu().numpy(),
                     dX=self.dX.cpu().numpy(), gq=self.gq.cpu().numpy(), sgrad=self.sgrad.cpu().numpy())
+
+
+def _abs_act(a: np.ndarray) -> np.ndarray:
+    """|a| for an activation array (bf16 bit patterns: clear the sign bit)."""
+    return a & np.uint16(0x7FFF) if a.dtype == np.uint16 else np.abs(a)
+
+
+def check_elements(o, p, got, want, rows=None, cols=None, tag="", slack=None):
+    """Each element within its own rounding bound.
+
+    With the inputs exact in both computations, the device result differs from
+    the oracle's f64 value only by the roundings of its fp32 sums and of the
+    operand it rounds:  |got - want| <= (u_op + 2 (K + 2) 2^-24) * S,  where
+    S = sum |a| |b| over the element's products (the oracle's own product of
+    the absolute values), K the length of that sum (in for Y, out for dX, T for
+    gq and sgrad) and u_op = 2^-8 for dX with bf16 activations (its scale is
+    rounded to bf16 inside the operand), else 0.  A misplaced or stale element
+    is off by about sqrt(K) typical terms, far beyond this bound, even where
+    one element barely moves the relative L2 norm.  slack: optional per-output
+    arrays added to the bound (the rounding of a further fp32 operation).
+    """
+    T, n_in = p.X.shape
+    n_out = p.q.shape[1]
+    aX, adY = _abs_act(p.X), _abs_act(p.dY)
+    aq = np.minimum(np.abs(p.q.astype(np.int16)), 127).astype(np.int8)
+    asc = np.abs(p.scale)
+    S = {}
+    if "Y" in got:
+        S["Y"] = o.linear_fwd(aX, aq, p.theta, asc, rows=rows)
+    if "dX" in got:
+        S["dX"] = o.linear_dx(adY, aq, p.theta, asc, rows=rows)
+    if "gq" in got or "sgrad" in got:
+        _, S["gq"], S["sgrad"] = o.linear_wgrad(aX, adY, aq, p.theta, asc, cols=cols)
+    u_op = dict(Y=0.0, dX=2.0 ** -8 if p.act == "bf16" else 0.0, gq=0.0, sgrad=0.0)
+    K = dict(Y=n_in, dX=n_out, gq=T, sgrad=T)
+    for k in [k for k in ("Y", "dX", "gq", "sgrad") if k in got]:
+        err = np.abs(np.asarray(got[k], dtype=np.float64) - want[k])
+        bound = (u_op[k] + 2.0 * (K[k] + 2) * 2.0 ** -24) * S[k] + 1e-30
+        if slack is not None and k in slack:
+            bound = bound + slack[k]
+        bad = np.argwhere(err > bound)
+        if bad.size:
+            i = tuple(bad[0])
+            raise AssertionError(f"{tag}: {k}{list(i)} off by {err[i]:.3e} > bound {bound[i]:.3e} "
+                                 f"({bad.shape[0]} elements out of bound)")

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 import ternary_weight_linear_tern_amd as tl
-from gpu_util import DeviceProjection, log, rel_l2, tol_for
+from gpu_util import DeviceProjection, check_elements, log, rel_l2, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +72,15 @@ def test_acc_matches_oracle(o, T, n_in, n_out, act, alpha):
     log(f"  relL2 {errs}")
     for k, e in errs.items():
         assert e <= tol, f"{k} relL2 {e:.3e} > {tol:.1e}"
+    # each increment element within its own rounding bound, plus the final fp32
+    # add's rounding (at most 2^-24 of the stored value, counted twice for slack)
+    olds = dict(dX=f64(dX0), gq=f64(gq0), sgrad=f64(sg0))
+    news = dict(dX=f64(dX), gq=f64(gq), sgrad=f64(sg))
+    scale = dict(dX=1.0, gq=alpha, sgrad=alpha)
+    inc = {k: (news[k] - olds[k]) / scale[k] for k in olds}
+    slack = {k: 2.0 ** -23 * (np.abs(olds[k]) + np.abs(news[k])) / scale[k] for k in olds}
+    check_elements(o, p, inc, dict(dX=dXo, gq=gqo, sgrad=sgo), tag=f"accumulate T={T} in={n_in} out={n_out}",
+                   slack=slack)
 
 
 @pytest.mark.parametrize("T,n_in,n_out", [(4000, 1032, 4104), (4000, 4104, 1032), (2048, 512, 2048)])

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 import ternary_weight_linear_tern_amd as tl
-from gpu_util import DeviceProjection, log, rel_l2, to_dev, tol_for
+from gpu_util import DeviceProjection, check_elements, log, rel_l2, to_dev, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -30,44 +30,6 @@ def _device():
 @pytest.fixture(scope="module")
 def o():
     return oracle.get()
-
-
-def _abs_act(a: np.ndarray) -> np.ndarray:
-    """|a| for an activation array (bf16 bit patterns: clear the sign bit)."""
-    return a & np.uint16(0x7FFF) if a.dtype == np.uint16 else np.abs(a)
-
-
-def check_elements(o, p, got, want, rows=None, cols=None, tag=""):
-    """Each element within its own rounding bound.
-
-    With the inputs exact in both computations, the device result differs from
-    the oracle's f64 value only by the roundings of its fp32 sums and of the
-    operand it rounds:  |got - want| <= (u_op + 2 (K + 2) 2^-24) * S,  where
-    S = sum |a| |b| over the element's products (the oracle's own product of
-    the absolute values), K the length of that sum (in for Y, out for dX, T for
-    gq and sgrad) and u_op = 2^-8 for dX with bf16 activations (its scale is
-    rounded to bf16 inside the operand), else 0.  A misplaced or stale element
-    is off by about sqrt(K) typical terms, far beyond this bound, even where
-    one element barely moves the relative L2 norm.
-    """
-    T, n_in = p.X.shape
-    n_out = p.q.shape[1]
-    aX, adY = _abs_act(p.X), _abs_act(p.dY)
-    aq = np.minimum(np.abs(p.q.astype(np.int16)), 127).astype(np.int8)
-    asc = np.abs(p.scale)
-    S = dict(Y=o.linear_fwd(aX, aq, p.theta, asc, rows=rows),
-             dX=o.linear_dx(adY, aq, p.theta, asc, rows=rows))
-    _, S["gq"], S["sgrad"] = o.linear_wgrad(aX, adY, aq, p.theta, asc, cols=cols)
-    u_op = dict(Y=0.0, dX=2.0 ** -8 if p.act == "bf16" else 0.0, gq=0.0, sgrad=0.0)
-    K = dict(Y=n_in, dX=n_out, gq=T, sgrad=T)
-    for k in ("Y", "dX", "gq", "sgrad"):
-        err = np.abs(np.asarray(got[k], dtype=np.float64) - want[k])
-        bound = (u_op[k] + 2.0 * (K[k] + 2) * 2.0 ** -24) * S[k] + 1e-30
-        bad = np.argwhere(err > bound)
-        if bad.size:
-            i = tuple(bad[0])
-            raise AssertionError(f"{tag}: {k}{list(i)} off by {err[i]:.3e} > bound {bound[i]:.3e} "
-                                 f"({bad.shape[0]} elements out of bound)")
 
 
 def check_full(o, p, res, tag):
