@@ -15,7 +15,6 @@ come from eager calls, timed with events between them.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -32,8 +31,8 @@ COPY_BYTES = 1 << 30  # calibration copy size
 
 
 def kernel_src_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    from ternary_weight_linear_tern_amd.rocprof_summary import kernel_code_hash
+    return kernel_code_hash(KERNEL_SRC)
 
 
 def parse():

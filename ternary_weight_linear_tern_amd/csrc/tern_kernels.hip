@@ -896,8 +896,9 @@ void gemm_dw_kernel(GemmArgs g) {
         one(std::integral_constant<int, 10>{}); one(std::integral_constant<int, 11>{});
         one(std::integral_constant<int, 12>{}); one(std::integral_constant<int, 13>{});
         one(std::integral_constant<int, 14>{}); one(std::integral_constant<int, 15>{});
-        // each MFMA followed by one refill load and one of the next chunk's
-        // 16 quarter-0 transposing reads (issued just before this call)
+        // each MFMA followed by one of the next chunk's 16 quarter-0
+        // transposing reads (issued just before this call), every second one
+        // also by a refill load
 #pragma unroll
         for (int k = 0; k < 16; k++) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -906,7 +907,7 @@ void gemm_dw_kernel(GemmArgs g) {
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // first K quarter of a chunk: its 16 MFMAs with the B half of the refill
+    // first K quarter of a chunk: its 16 MFMAs with the dY half of the refill
     // begun in the previous chunk's last quarter (stage sc ^ 1, one load per
     // two MFMAs), then the issue side's step to the next chunk
     auto p_mma_dmab = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) __attribute__((always_inline)) {
@@ -976,8 +977,7 @@ void gemm_dw_kernel(GemmArgs g) {
         }
         w_barrier<0>();
         // every wave has read all of this chunk's stage: its refill with the
-        // chunk after the next one goes out during the last quarter, one load
-        // per MFMA
+        // chunk after the next one starts during the last quarter (the X half)
         const int sfree = sc;
         sc ^= 1;
         w_read_q(w_lds + sc * W_STAGE, f0a[SL1], f0b[SL1], wm, wn, lane, 0);

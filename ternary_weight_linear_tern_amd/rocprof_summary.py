@@ -28,6 +28,16 @@ ROOT = os.path.dirname(PKG)
 COPY_KIB = (1 << 30) / 1024.0
 
 
+
+def kernel_code_hash(path: str) -> str:
+    """First 16 hex digits of the SHA-256 of a C++/HIP source with its comments
+    and blank lines removed and each line's surrounding whitespace stripped, so
+    that the hash names the code whose counters were taken, not its comments."""
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", l).strip() for l in text.splitlines())
+    return hashlib.sha256("\n".join(l for l in lines if l).encode()).hexdigest()[:16]
+
 def entry_of(kernel: str) -> str | None:
     k = kernel
     if "materialize_kernel" in k or "derive_kernel" in k:
@@ -89,7 +99,7 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, steps: int, kernel_sr
             ent[e]["write_kib"] += w.get(k, 0.0)
     out = {"kernel_src_sha256_16": None, "entries": {}, "calibration": {"fetch": fscale, "write": wscale}}
     if kernel_src:
-        out["kernel_src_sha256_16"] = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+        out["kernel_src_sha256_16"] = kernel_code_hash(kernel_src)
     lines += ["", "| entry point | HBM read MB/step | HBM write MB/step |", "|---|---|---|"]
     for e, v in sorted(ent.items()):
         rd = v["fetch_kib"] * fscale * 1024 / steps
