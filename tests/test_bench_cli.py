@@ -21,3 +21,22 @@ def test_bench_help_lists_launch_modes():
     assert r.returncode == 0
     for opt in ("--launch", "--streams", "--workload", "--steps", "--warmup"):
         assert opt in r.stdout
+
+
+def test_traffic_key_ignores_comments_only(tmp_path):
+    """The key of the stored HBM counters survives comment and blank-line edits
+    and changes with any edit of the code itself."""
+    sys.path.insert(0, ROOT)
+    from ternary_weight_linear_tern_amd.rocprof_summary import kernel_code_hash
+    base = "// header\n__global__ void k(int *p) {\n    p[0] = 1;   // store\n}\n"
+    variants = {
+        "comments": "// other header\n/* block\n   comment */\n__global__ void k(int *p) {\n\n    p[0] = 1;\n}\n",
+        "code": "// header\n__global__ void k(int *p) {\n    p[0] = 2;   // store\n}\n",
+    }
+    f = tmp_path / "a.hip"
+    f.write_text(base)
+    h0 = kernel_code_hash(str(f))
+    f.write_text(variants["comments"])
+    assert kernel_code_hash(str(f)) == h0
+    f.write_text(variants["code"])
+    assert kernel_code_hash(str(f)) != h0
