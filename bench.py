@@ -56,7 +56,143 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy a 1 GiB buffer 3 times (known bytes, for scaling "
                          "HBM traffic counters)")
+    ap.add_argument("--extras", action="store_true",
+                    help="instead of the step: per-call times of the accumulating backward, the q/k/v "
+                         "group, the health panel and the scale step on the workload's shapes (eager, one "
+                         "JSON line)")
     return ap.parse_args()
+
+
+def extras(a):
+    """Per-call times of the entry points beyond the step, on the workload's
+    projections (eager calls, events on the current stream, median of a few
+    timed repetitions): dX and dW plain against accumulating, the fused q/k/v
+    group against three separate projections, the gather that builds it, the
+    health panel with churn, and the scale's AdamW step.  HBM-bound calls are
+    also given against their algorithmic bytes and the 8 TB/s peak."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import synth
+    import ternary_weight_linear_tern_amd as tl
+
+    w = synth.WORKLOADS[a.workload]
+    torch.cuda.set_device(0)
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    projs = []
+    for i, (name, n_in, n_out) in enumerate(w.projs):
+        p = synth.workload_inputs(w, i)
+        d = dict(name=name, n_in=n_in, n_out=n_out, X=to_dev(p.X), dY=to_dev(p.dY), q=to_dev(p.q),
+                 scale=to_dev(p.scale), theta=p.theta)
+        d["packed"] = tl.empty_packed(n_in, n_out)
+        d["prev"] = tl.empty_packed(n_in, n_out)
+        d["dX"] = torch.empty((w.T, n_in), device="cuda")
+        d["Y"] = torch.empty((w.T, n_out), device="cuda")
+        d["gq"] = torch.zeros((n_in, n_out), device="cuda")
+        d["sgrad"] = torch.zeros((n_out,), device="cuda")
+        d["ws"] = tl.empty_workspace(w.T, n_in, n_out, d["X"].dtype)
+        d["ws_acc"] = tl.empty_workspace(w.T, n_in, n_out, d["X"].dtype, acc=True)
+        d["m"] = torch.zeros((n_out,), device="cuda")
+        d["v"] = torch.zeros((n_out,), device="cuda")
+        tl.tern_materialize(d["q"], d["theta"], d["packed"])
+        tl.tern_materialize(torch.roll(d["q"], 1, 1).contiguous(), d["theta"], d["prev"])
+        projs.append(d)
+    torch.cuda.synchronize()
+    print(f"# extras: inputs ready, workload {w.name}", file=sys.stderr, flush=True)
+
+    def timed(fn, reps=8, warm=2):
+        for _ in range(warm):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)   # ms
+
+    out = {}
+    flops = sum(2.0 * w.T * d["n_in"] * d["n_out"] for d in projs)
+    dx = timed(lambda: [tl.tern_linear_bwd_dx(d["dY"], d["packed"], d["scale"], d["dX"]) for d in projs])
+    dxa = timed(lambda: [tl.tern_linear_bwd_dx_acc(d["dY"], d["packed"], d["scale"], d["dX"]) for d in projs])
+    dw = timed(lambda: [tl.tern_linear_bwd_dw(d["X"], d["dY"], d["packed"], d["scale"], d["gq"], d["sgrad"],
+                                              d["ws"]) for d in projs])
+    dwa = timed(lambda: [tl.tern_linear_bwd_dw_acc(d["X"], d["dY"], d["packed"], d["scale"], d["gq"], d["sgrad"],
+                                                   d["ws_acc"], 0.5) for d in projs])
+    for k, ms in (("bwd_dx", dx), ("bwd_dx_acc", dxa), ("bwd_dw", dw), ("bwd_dw_acc", dwa)):
+        out[k] = {"ms_per_step": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                  "mfma_frac": round(flops / ms / 1e9 / PEAK_TFLOPS["bf16"], 4)}
+
+    # health panel over every projection, churn against a previous handle:
+    # q (1 B), the previous canonical codes (1/4 B) per weight, scale (4 B) per column
+    panel = tl.empty_panel()
+
+    def panel_pass():
+        tl.tern_panel_reset(panel)
+        for d in projs:
+            tl.tern_panel_add(d["q"], d["theta"], d["scale"], panel, prev_packed=d["prev"])
+    ms = timed(panel_pass)
+    nb = sum(d["n_in"] * d["n_out"] * 1.25 + 4 * d["n_out"] for d in projs)
+    out["panel"] = {"ms_per_step": round(ms, 4), "bytes": nb, "gbs": round(nb / ms / 1e6, 1),
+                    "hbm_frac": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+    # scale step: sgrad, scale, m, v read and scale, m, v written (28 B per column)
+    stp = [1]
+
+    def adamw_pass():
+        stp[0] += 1
+        for d in projs:
+            tl.tern_scale_adamw(d["sgrad"], d["scale"], d["m"], d["v"], stp[0], 1e-3, 1e-3)
+    ms = timed(adamw_pass)
+    ncols = sum(d["n_out"] for d in projs)
+    out["scale_adamw"] = {"ms_per_step": round(ms, 4), "us_per_call": round(1000 * ms / len(projs), 2),
+                          "bytes": 28 * ncols}
+
+    # q/k/v as one group: the three square projections of the block that read one input
+    mem = [d for d in projs if d["n_in"] == d["n_out"]][:3]
+    if len(mem) == 3:
+        n_in = mem[0]["n_in"]
+        tot = sum(d["n_out"] for d in mem)
+        qg = torch.empty((n_in, tot), dtype=torch.int8, device="cuda")
+        sg = torch.empty((tot,), device="cuda")
+        ms = timed(lambda: tl.tern_group_gather([d["q"] for d in mem], [d["scale"] for d in mem], qg, sg))
+        nb = 2.0 * (n_in * tot + 4 * tot)
+        out["group_gather"] = {"ms": round(ms, 4), "bytes": nb, "gbs": round(nb / ms / 1e6, 1),
+                               "hbm_frac": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)}
+        pk = tl.empty_packed(n_in, tot)
+        tl.tern_materialize(qg, mem[0]["theta"], pk)
+        X = mem[0]["X"]
+        dYg = torch.cat([d["dY"] for d in mem], dim=1).contiguous()
+        Yg = torch.empty((w.T, tot), device="cuda")
+        dXg = torch.empty((w.T, n_in), device="cuda")
+        gqg = torch.empty((n_in, tot), device="cuda")
+        sgg = torch.empty((tot,), device="cuda")
+        wsg = tl.empty_workspace(w.T, n_in, tot, X.dtype)
+        gf = timed(lambda: tl.tern_linear_fwd(X, pk, sg, Yg))
+        sf = timed(lambda: [tl.tern_linear_fwd(X, d["packed"], d["scale"], d["Y"]) for d in mem])
+        gb = timed(lambda: tl.tern_linear_bwd(X, dYg, pk, sg, dXg, gqg, sgg, wsg))
+
+        def sep_bwd():
+            for j, d in enumerate(mem):
+                (tl.tern_linear_bwd_dx if j == 0 else tl.tern_linear_bwd_dx_acc)(d["dY"], d["packed"], d["scale"],
+                                                                                 dXg)
+                tl.tern_linear_bwd_dw(X, d["dY"], d["packed"], d["scale"], d["gq"], d["sgrad"], d["ws"])
+        sb = timed(sep_bwd)
+        out["qkv_group"] = {"fwd_ms": round(gf, 4), "fwd_separate_ms": round(sf, 4), "bwd_ms": round(gb, 4),
+                            "bwd_separate_ms": round(sb, 4)}
+    torch.cuda.synchronize()
+    print(json.dumps({"metric": "per-call times of the entry points beyond the step", "workload": w.name,
+                      "T": w.T, "projections": [[d["name"], d["n_in"], d["n_out"]] for d in projs],
+                      "launch": "eager", "entries": out}), flush=True)
 
 
 def main():
@@ -65,6 +201,10 @@ def main():
         print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
               "(the library has no multi-GPU path; sharding is described, not built)", file=sys.stderr, flush=True)
         sys.exit(2)
+
+    if a.extras:
+        extras(a)
+        return
 
     import numpy as np
     import torch

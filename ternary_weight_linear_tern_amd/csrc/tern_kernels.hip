@@ -1460,13 +1460,13 @@ void gemm_rd_kernel(GemmArgs g) {
 
     // Epilogue of tile (ctm, ctn): 64 buffer stores per wave whatever the edges
     // (out-of-range stores get an out-of-range offset), so the vmcnt arithmetic
-    // of the main loop holds.  ACC (dX += ...): the 4 old values of each
-    // row segment are loaded first (out-of-range offsets read zero; the
-    // compiler waits for them before the add).  The main loop's waits bound the
-    // number of operations still outstanding, so the 64 extra loads only make
-    // them wait for more than needed.  Lane offsets cover the 4 columns n of the lane;
-    // the row block m goes in the scalar offset.  M is a multiple of 8 and the
-    // 8-row groups are wave-uniform, so the m test is scalar.
+    // of the main loop holds.  ACC (dX += ...): each store's 16 bytes of old
+    // values are loaded first (out-of-range offsets read zero; the compiler
+    // waits for them before the add, so they are done when the epilogue ends
+    // and the main loop's waits still count at most 64 stores).  bf16 Y
+    // stores straight from the MFMA layout: lane offsets cover the 4 columns n
+    // of the lane, the row block m goes in the scalar offset; M is a multiple
+    // of 8 and the 8-row groups are wave-uniform, so the m test is scalar.
     auto epilogue = [&]() __attribute__((always_inline)) {
         const int mw = ctm * 256 + wm * 128, nw = ctn * 256 + wn * 128;
         const int ldo = MODE == MODE_FWD ? g.out : g.in;
@@ -1497,21 +1497,12 @@ void gemm_rd_kernel(GemmArgs g) {
                 }
 #pragma unroll
                 for (int fn = 0; fn < 4; fn++) {
-                    f32x4 old[4];
-                    if constexpr (ACC) {
-#pragma unroll
-                        for (int q = 0; q < 4; q++)
-                            old[q] = __builtin_bit_cast(
-                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, mokq[q] ? vo[fn] : OOB,
-                                                                             (fm * 32 + 8 * q) * esz, 0));
-                    }
 #pragma unroll
                     for (int q = 0; q < 4; q++) {
                         const int so = (fm * 32 + 8 * q) * esz;
                         f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
                                    acc[fm][fn][4 * q + 3]};
                         if constexpr (MODE == MODE_FWD) v = v * scq[q];
-                        if constexpr (ACC) v += old[q];
                         const uint32_t off = mokq[q] ? vo[fn] : OOB;
                         if constexpr (OBF) {
                             const f32x2 a2 = {v.x, v.y}, b2 = {v.z, v.w};
@@ -1522,13 +1513,11 @@ void gemm_rd_kernel(GemmArgs g) {
                             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off, so, 0);
                         }
                     }
-                    // keep each group's loads after the previous group's stores
-                    if constexpr (ACC) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
 
-        // fp32 without accumulation: each 32-row x 64-column piece of the
+        // fp32 (ACC: with the old values added): each 32-row x 64-column piece of the
         // wave's block passes through the LDS stage the last chunk consumed
         // (free until the next chunk's first issue), transposed so that every
         // store writes 4 rows x 256 contiguous bytes (whole 128-byte lines)
@@ -1540,10 +1529,30 @@ void gemm_rd_kernel(GemmArgs g) {
         // so they need not displace the operand panels in L2).
         auto rows_t = [&]() __attribute__((always_inline)) {
             char *eb = wl + ((sc + 3) & 3) * R_STAGE;
+            // store offset of row t = 4 k + lane / 16 of piece (fn, fp), lane's 4 columns
+            auto off_of = [&](int fn, int fp, int k) __attribute__((always_inline)) {
+                const int row = fn * 32 + 4 * k + (lane >> 4), col = fp * 64 + (lane & 15) * 4;
+                return nw + row < g.N && mw + col < g.M ? (uint32_t)((row * ldo + col) * 4) : OOB;
+            };
+            // ACC: the old values of a piece, loaded one piece ahead so that
+            // their latency overlaps the previous piece's round trip
+            f32x4 oldn[8];
+            auto load_old = [&](int fn, int fp) __attribute__((always_inline)) {
+#pragma unroll
+                for (int k = 0; k < 8; k++)
+                    oldn[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, off_of(fn, fp, k), 0, 0));
+            };
+            if constexpr (ACC) load_old(0, 0);
 #pragma unroll
             for (int fn = 0; fn < 4; fn++) {
 #pragma unroll
                 for (int fp = 0; fp < 2; fp++) {
+                    f32x4 oldc[8];
+                    if constexpr (ACC) {
+#pragma unroll
+                        for (int k = 0; k < 8; k++) oldc[k] = oldn[k];
+                        if (fn < 3 || fp == 0) load_old(fp ? fn + 1 : fn, fp ^ 1);
+                    }
 #pragma unroll
                     for (int f2 = 0; f2 < 2; f2++) {
                         const int fm = 2 * fp + f2;
@@ -1563,11 +1572,10 @@ void gemm_rd_kernel(GemmArgs g) {
 #pragma unroll
                     for (int k = 0; k < 8; k++) {
                         const int t = 4 * k + (lane >> 4), pc = lane & 15;
-                        const f32x4 v = *(const f32x4 *)(eb + t * 256 + ((pc ^ (t & 15)) * 16));
-                        const int row = fn * 32 + t, col = fp * 64 + pc * 4;
-                        const uint32_t off =
-                            nw + row < g.N && mw + col < g.M ? (uint32_t)((row * ldo + col) * 4) : OOB;
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off, 0, 2);
+                        f32x4 v = *(const f32x4 *)(eb + t * 256 + ((pc ^ (t & 15)) * 16));
+                        if constexpr (ACC) v += oldc[k];   // out of range: zero
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off_of(fn, fp, k), 0,
+                                                               2);
                     }
                     // every read has returned before the next piece (or the
                     // next chunk's loads) overwrites the stage
@@ -1579,7 +1587,6 @@ void gemm_rd_kernel(GemmArgs g) {
         };
 
         if (obf) rows(std::true_type{});
-        else if constexpr (ACC) rows(std::false_type{});
         else rows_t();
     };
 

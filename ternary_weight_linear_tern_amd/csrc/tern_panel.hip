@@ -31,25 +31,39 @@ __global__ void panel_reset_kernel(tern_panel_t *p) {
     }
 }
 
-// Sum of v over the block (256 threads, 4 waves), valid in thread 0.
+// Sum of v over the block (PANEL_NT threads), valid in every thread: lanes
+// within each wave, then the waves' sums in ascending order.
+constexpr int PANEL_NT = 1024;
 __device__ __forceinline__ uint64_t block_sum(uint64_t v, uint64_t *red) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    return red[0] + red[1] + red[2] + red[3];
+    uint64_t s = 0;
+#pragma unroll
+    for (int w = 0; w < PANEL_NT / 64; w++) s += red[w];
+    return s;
 }
 
+// Counts of one matrix that need its elements: nonzero +1 and -1 codes, rail
+// (|q| == clamp) and churn against the previous handle's canonical words.
+// total, zero (= dead) and churn_total follow from in * out and these, and
+// panel_scale_kernel adds them once the counts are in.  Every block adds its
+// sums with a few integer atomics, exact in any order.
 template <bool VEC>
-__global__ __launch_bounds__(256) void panel_count_kernel(const int8_t *__restrict__ q, int64_t out, int64_t wpr,
-                                                          int64_t nwords, int theta, int clamp,
-                                                          const uint32_t *__restrict__ prev,
-                                                          tern_panel_t *__restrict__ p) {
-    __shared__ uint64_t red[4];
-    uint32_t tot = 0, neg = 0, pos = 0, rail = 0, dead = 0, churn = 0;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nwords; i += (int64_t)gridDim.x * 256) {
-        const int64_t r = i / wpr, wc = i - r * wpr;
+__global__ __launch_bounds__(PANEL_NT) void panel_count_kernel(const int8_t *__restrict__ q, int64_t out,
+                                                               int64_t wpr, int64_t nwords, int theta, int clamp,
+                                                               const uint32_t *__restrict__ prev,
+                                                               tern_panel_t *__restrict__ p) {
+    __shared__ uint64_t red[PANEL_NT / 64];
+    uint32_t neg = 0, pos = 0, rail = 0, churn = 0;
+    // word index -> (row, word column): a 32-bit division when the indices fit
+    // (a 64-bit one is a long software sequence)
+    const bool narrow = nwords <= 0xFFFFFFFFll;
+#pragma unroll 4
+    for (int64_t i = (int64_t)blockIdx.x * PANEL_NT + threadIdx.x; i < nwords; i += (int64_t)gridDim.x * PANEL_NT) {
+        const int64_t r = narrow ? (int64_t)((uint32_t)i / (uint32_t)wpr) : i / wpr, wc = i - r * wpr;
         const int8_t *row = q + r * out + wc * 16;
         const int nc = out - wc * 16 < 16 ? (int)(out - wc * 16) : 16;
         int8_t b[16];
@@ -64,15 +78,13 @@ __global__ __launch_bounds__(256) void panel_count_kernel(const int8_t *__restri
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < 16; j++) {
-            if (j < nc) {
-                const int v = b[j], a = v < 0 ? -v : v;
-                const uint32_t code = v >= theta ? 1u : (v <= -theta ? 3u : 0u);
-                word |= code << (2 * j);
-                rail += a == clamp;
-                dead += a < theta;
-            }
+            // elements past a ragged row end are 0 here: code 00 (theta >= 1),
+            // and left out of the rail count (a clamp of 0 would match them)
+            const int v = b[j];
+            const uint32_t code = v >= theta ? 1u : (v <= -theta ? 3u : 0u);
+            word |= code << (2 * j);
+            rail += (v == clamp || v == -clamp) && j < nc;
         }
-        tot += (uint32_t)nc;
         // code 01 = +1, 11 = -1 (bit 0: nonzero, bit 1: negative)
         pos += (uint32_t)__builtin_popcount(word & ~(word >> 1) & 0x55555555u);
         neg += (uint32_t)__builtin_popcount(word & (word >> 1) & 0x55555555u);
@@ -81,29 +93,22 @@ __global__ __launch_bounds__(256) void panel_count_kernel(const int8_t *__restri
             churn += (uint32_t)__builtin_popcount((d | (d >> 1)) & 0x55555555u);
         }
     }
-    const uint64_t s_tot = block_sum(tot, red);
     const uint64_t s_neg = block_sum(neg, red);
     const uint64_t s_pos = block_sum(pos, red);
     const uint64_t s_rail = block_sum(rail, red);
-    const uint64_t s_dead = block_sum(dead, red);
-    const uint64_t s_churn = block_sum(churn, red);
-    if (threadIdx.x == 0 && s_tot) {
-        atomicAdd((unsigned long long *)&p->total, (unsigned long long)s_tot);
-        atomicAdd((unsigned long long *)&p->neg, (unsigned long long)s_neg);
-        atomicAdd((unsigned long long *)&p->zero, (unsigned long long)(s_tot - s_neg - s_pos));
-        atomicAdd((unsigned long long *)&p->pos, (unsigned long long)s_pos);
-        atomicAdd((unsigned long long *)&p->rail, (unsigned long long)s_rail);
-        atomicAdd((unsigned long long *)&p->dead, (unsigned long long)s_dead);
-        if (prev) {
-            atomicAdd((unsigned long long *)&p->churn, (unsigned long long)s_churn);
-            atomicAdd((unsigned long long *)&p->churn_total, (unsigned long long)s_tot);
-        }
+    const uint64_t s_churn = prev ? block_sum(churn, red) : 0;
+    if (threadIdx.x == 0) {
+        if (s_neg) atomicAdd((unsigned long long *)&p->neg, (unsigned long long)s_neg);
+        if (s_pos) atomicAdd((unsigned long long *)&p->pos, (unsigned long long)s_pos);
+        if (s_rail) atomicAdd((unsigned long long *)&p->rail, (unsigned long long)s_rail);
+        if (s_churn) atomicAdd((unsigned long long *)&p->churn, (unsigned long long)s_churn);
     }
 }
 
 // One block: thread t sums columns t, t + 256, ... in f64 (ascending), then a
 // fixed tree over the threads; thread 0 adds the result to the accumulator.
 __global__ __launch_bounds__(256) void panel_scale_kernel(const float *__restrict__ scale, int64_t out,
+                                                          int64_t elems, int compared,
                                                           tern_panel_t *__restrict__ p) {
     __shared__ double ssum[256];
     __shared__ float smin[256], smax[256];
@@ -129,6 +134,12 @@ __global__ __launch_bounds__(256) void panel_scale_kernel(const float *__restric
         __syncthreads();
     }
     if (t == 0) {
+        // the matrix's element count, and the classes that follow from it
+        // (the counts of this matrix are in: same stream, earlier kernel)
+        p->total += (uint64_t)elems;
+        if (compared) p->churn_total += (uint64_t)elems;
+        p->zero = p->total - p->neg - p->pos;
+        p->dead = p->zero;   // |q| < theta is exactly the zero class
         p->scale_count += (uint64_t)out;
         p->scale_sum += ssum[0];
         if ((double)smin[0] < p->scale_min) p->scale_min = (double)smin[0];
@@ -165,19 +176,23 @@ int tern_panel_add(const int8_t *q, int64_t in, int64_t out, int32_t theta, int3
     hipStream_t st = (hipStream_t)stream;
     const int64_t wpr = (out + 15) / 16, nwords = in * wpr;
     if (nwords > 0) {
-        int64_t blocks = (nwords + 255) / 256;
-        if (blocks > 2048) blocks = 2048;
+        // every block adds its sums to the same 64-bit fields, and those
+        // atomics serialise at one L2 channel (about 8 ns each): 128 blocks
+        // of 1024 threads (two waves per SIMD), each streaming many words
+        int64_t blocks = (nwords + pdev::PANEL_NT - 1) / pdev::PANEL_NT;
+        if (blocks > 128) blocks = 128;
         const bool vec = out % 16 == 0 && ((uintptr_t)q & 15u) == 0;
         if (vec)
-            hipLaunchKernelGGL(pdev::panel_count_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, q, out,
-                               wpr, nwords, (int)theta, (int)q_clamp, prev_packed, panel);
+            hipLaunchKernelGGL(pdev::panel_count_kernel<true>, dim3((unsigned)blocks), dim3(pdev::PANEL_NT), 0, st,
+                               q, out, wpr, nwords, (int)theta, (int)q_clamp, prev_packed, panel);
         else
-            hipLaunchKernelGGL(pdev::panel_count_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, q, out,
-                               wpr, nwords, (int)theta, (int)q_clamp, prev_packed, panel);
+            hipLaunchKernelGGL(pdev::panel_count_kernel<false>, dim3((unsigned)blocks), dim3(pdev::PANEL_NT), 0, st,
+                               q, out, wpr, nwords, (int)theta, (int)q_clamp, prev_packed, panel);
         if (hipGetLastError() != hipSuccess) return TERN_ERR_HIP;
     }
     if (out > 0) {
-        hipLaunchKernelGGL(pdev::panel_scale_kernel, dim3(1), dim3(256), 0, st, scale, out, panel);
+        hipLaunchKernelGGL(pdev::panel_scale_kernel, dim3(1), dim3(256), 0, st, scale, out, in * out,
+                           prev_packed ? 1 : 0, panel);
         if (hipGetLastError() != hipSuccess) return TERN_ERR_HIP;
     }
     return TERN_OK;

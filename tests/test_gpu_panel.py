@@ -83,6 +83,10 @@ def test_panel_matches_oracle(o, misaligned):
     _check(o, mats, 2, 7, "theta 2", misaligned)
     _check(o, mats, 1, 7, "theta 1", misaligned)
     _check(o, mats, 3, 5, "theta 3 clamp 5", misaligned)
+    # the clamp's edges: 0 counts the zeros as rail (never the padding of a
+    # ragged row), 128 the int8 value -128
+    _check(o, mats, 2, 0, "clamp 0", misaligned)
+    _check(o, mats, 2, 128, "clamp 128", misaligned)
     # one matrix without a previous handle: churn is not a fraction of the total
     mixed = [mats[0], (mats[1][0], None, mats[1][2])]
     got = tl.panel_values(_check(o, mixed, 2, 7, "mixed snapshot"))
