@@ -263,7 +263,10 @@ int tern_group_gather(const int8_t *const *q, const float *const *scale, const i
  *   prev_packed a handle of tern_materialize for the same in, out (its
  *   canonical part is read) or NULL.  theta in [1, 127], q_clamp in
  *   [0, 128].  panel is device memory, 8-byte aligned, written in stream
- *   order (calls on one stream accumulate).
+ *   order (calls on one stream accumulate; calls on different streams must
+ *   not overlap on one panel: the class counts are added atomically, but
+ *   total, the derived zero / dead and the scale statistics are updated by
+ *   one thread at the end of each call).
  * Errors: NULL, SHAPE, THETA (theta or q_clamp out of range), ALIGN, ALIAS,
  *   HIP.
  */
