@@ -8,6 +8,8 @@ group's Y equals that member's own forward bit for bit; the group's dX meets
 the gate against the sum of the members' oracle input gradients, and the
 gq / sgrad slices against each member's oracle weight-side gradients.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -15,7 +17,7 @@ import torch
 import oracle
 import synth
 import ternary_weight_linear_tern_amd as tl
-from gpu_util import log, rel_l2, to_dev, tol_for
+from gpu_util import check_elements, log, rel_l2, to_dev, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -101,6 +103,10 @@ def test_group_matches_members(o, act):
         es = rel_l2(g["sgrad"][off:off + w].cpu().numpy(), sgo)
         log(f"  member {k}: gq relL2 {eg:.3e} sgrad relL2 {es:.3e}")
         assert eg <= tol and es <= tol
+        # the member's slices element by element within their rounding bounds
+        check_elements(o, dataclasses.replace(p, X=X), dict(Y=g["Y"][:, off:off + w].cpu().numpy(), gq=g["gq"][:, off:off + w].cpu().numpy(),
+                                  sgrad=g["sgrad"][off:off + w].cpu().numpy()),
+                       dict(Y=o.linear_fwd(X, p.q, theta, p.scale), gq=gqo, sgrad=sgo), tag=f"group member {k}")
         off += w
 
 
