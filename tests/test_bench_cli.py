@@ -19,7 +19,7 @@ def test_bench_help_lists_launch_modes():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 0
-    for opt in ("--launch", "--streams", "--workload", "--steps", "--warmup"):
+    for opt in ("--launch", "--streams", "--workload", "--steps", "--warmup", "--extras"):
         assert opt in r.stdout
 
 
