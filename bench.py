@@ -25,14 +25,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "ternary_weight_linear_tern_amd", "csrc", "tern_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 COPY_BYTES = 1 << 30  # calibration copy size
 
 
 def kernel_src_hash() -> str:
+    """Key of the stored traffic counters: the kernels and the planner's code."""
     from ternary_weight_linear_tern_amd.rocprof_summary import kernel_code_hash
-    return kernel_code_hash(KERNEL_SRC)
+    return kernel_code_hash()
 
 
 def parse():

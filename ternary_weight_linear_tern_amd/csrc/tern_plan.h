@@ -53,7 +53,7 @@ struct BwdLayout {
 BwdLayout plan_bwd(int64_t T, int64_t in, int64_t out, bool bf16, bool acc = false);
 
 // Row-block height of the split-K reduction (and thus of its sgrad partials).
-constexpr int kReduceRows = 16;
+constexpr int kReduceRows = 4;
 
 // Largest accepted dimensions: tile offsets stay well inside 32 bits.
 constexpr int64_t kMaxInOut = int64_t(1) << 20;

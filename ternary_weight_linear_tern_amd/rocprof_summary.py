@@ -4,14 +4,15 @@
     python -m ternary_weight_linear_tern_amd.rocprof_summary counters <counter_collection.csv> [title]
     python -m ternary_weight_linear_tern_amd.rocprof_summary ratios <counter_collection.csv> [title]
     python -m ternary_weight_linear_tern_amd.rocprof_summary traffic <fetch_counter_collection.csv> \\
-        <write_counter_collection.csv> <workload> <dispatch_steps> [kernel_src]
+        <write_counter_collection.csv> <workload> <dispatch_steps> [sources ...]
 
 `traffic` attributes FETCH_SIZE / WRITE_SIZE (KiB per dispatch) to the library's
 entry points, scales both by what the same counters read for the calibration
 copy (bench.py --copy-calibration: 1 GiB read + 1 GiB written by one
 elementwise multiply-by-one kernel per copy), divides by the number of profiled steps, and writes
 profiles/traffic_counters.json, which bench.py reports as roofline.traffic
-while the kernel source is unchanged.
+while the code of the kernels and of the planner (which sets their launch
+shapes) is unchanged.
 """
 from __future__ import annotations
 
@@ -28,15 +29,23 @@ ROOT = os.path.dirname(PKG)
 COPY_KIB = (1 << 30) / 1024.0
 
 
+def kernel_code_hash(*paths: str) -> str:
+    """First 16 hex digits of the SHA-256 of C++/HIP sources (in the order
+    given) with their comments and blank lines removed and each line's
+    surrounding whitespace stripped, so that the hash names the code whose
+    counters were taken, not its comments.  Without paths: the kernels and
+    the planner that sets their launch shapes (tile, split-K, reduce rows)."""
+    if not paths:
+        paths = tuple(os.path.join(PKG, "csrc", f) for f in ("tern_kernels.hip", "tern_plan.h", "tern_plan.cpp"))
+    h = hashlib.sha256()
+    for path in paths:
+        text = open(path, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*", "", l).strip() for l in text.splitlines())
+        h.update("\n".join(l for l in lines if l).encode())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 
-def kernel_code_hash(path: str) -> str:
-    """First 16 hex digits of the SHA-256 of a C++/HIP source with its comments
-    and blank lines removed and each line's surrounding whitespace stripped, so
-    that the hash names the code whose counters were taken, not its comments."""
-    text = open(path, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = (re.sub(r"//.*", "", l).strip() for l in text.splitlines())
-    return hashlib.sha256("\n".join(l for l in lines if l).encode()).hexdigest()[:16]
 
 def entry_of(kernel: str) -> str | None:
     k = kernel
@@ -99,7 +108,8 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, steps: int, kernel_sr
             ent[e]["write_kib"] += w.get(k, 0.0)
     out = {"kernel_src_sha256_16": None, "entries": {}, "calibration": {"fetch": fscale, "write": wscale}}
     if kernel_src:
-        out["kernel_src_sha256_16"] = kernel_code_hash(kernel_src)
+        out["kernel_src_sha256_16"] = kernel_code_hash(*kernel_src) if isinstance(kernel_src, (list, tuple)) \
+            else kernel_code_hash(kernel_src)
     lines += ["", "| entry point | HBM read MB/step | HBM write MB/step |", "|---|---|---|"]
     for e, v in sorted(ent.items()):
         rd = v["fetch_kib"] * fscale * 1024 / steps
@@ -190,7 +200,8 @@ if __name__ == "__main__":
     elif cmd == "counters":
         print(counters(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
     elif cmd == "traffic":
-        src = sys.argv[6] if len(sys.argv) > 6 else os.path.join(PKG, "csrc", "tern_kernels.hip")
+        src = sys.argv[6:] if len(sys.argv) > 6 else \
+            [os.path.join(PKG, "csrc", f) for f in ("tern_kernels.hip", "tern_plan.h", "tern_plan.cpp")]
         data, text = traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), src)
         print(text)
         dst = os.path.join(ROOT, "profiles", "traffic_counters.json")
