@@ -1713,11 +1713,10 @@ __global__ __launch_bounds__(256) void materialize_kernel(const int8_t *__restri
 
 // Split-K finish of dW: G = sum over splits (ascending), gq = G * scale (acc:
 // gq + alpha * G * scale), and the sgrad partial of a block of kReduceRows rows
-// (ascending r).  The row and split loops are unrolled so that several rows'
-// loads are in flight per thread (one block per compute unit at the usual
-// sizes, so the loads' latency would otherwise set the pace).  Each thread
-// owns 4 consecutive columns (16-byte loads and stores); a block covers 1024
-// columns of kReduceRows rows.
+// (ascending r).  Each thread owns 4 consecutive columns (16-byte loads and
+// stores); a block covers 1024 columns of kReduceRows rows, few enough rows
+// that a 2048 x 2048 reduce has 2048 blocks (several waves per SIMD to hide
+// the loads' latency), with its split loop unrolled.
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ ws, int splits,
                                                         const float *__restrict__ scale,
                                                         const uint32_t *__restrict__ packed, int in,
