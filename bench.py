@@ -97,8 +97,8 @@ def extras(a):
         d["Y"] = torch.empty((w.T, n_out), device="cuda")
         d["gq"] = torch.zeros((n_in, n_out), device="cuda")
         d["sgrad"] = torch.zeros((n_out,), device="cuda")
-        d["ws"] = tl.empty_workspace(w.T, n_in, n_out, d["X"].dtype)
-        d["ws_acc"] = tl.empty_workspace(w.T, n_in, n_out, d["X"].dtype, acc=True)
+        d["ws"] = tl.empty_workspace(w.T, n_in, n_out)
+        d["ws_acc"] = tl.empty_workspace(w.T, n_in, n_out, acc=True)
         d["m"] = torch.zeros((n_out,), device="cuda")
         d["v"] = torch.zeros((n_out,), device="cuda")
         tl.tern_materialize(d["q"], d["theta"], d["packed"])
@@ -176,7 +176,7 @@ def extras(a):
         dXg = torch.empty((w.T, n_in), device="cuda")
         gqg = torch.empty((n_in, tot), device="cuda")
         sgg = torch.empty((tot,), device="cuda")
-        wsg = tl.empty_workspace(w.T, n_in, tot, X.dtype)
+        wsg = tl.empty_workspace(w.T, n_in, tot)
         gf = timed(lambda: tl.tern_linear_fwd(X, pk, sg, Yg))
         sf = timed(lambda: [tl.tern_linear_fwd(X, d["packed"], d["scale"], d["Y"]) for d in mem])
         gb = timed(lambda: tl.tern_linear_bwd(X, dYg, pk, sg, dXg, gqg, sgg, wsg))
@@ -233,7 +233,7 @@ def main():
         d["dX"] = torch.empty((w.T, n_in), dtype=torch.float32, device=dev)
         d["gq"] = torch.empty((n_in, n_out), dtype=torch.float32, device=dev)
         d["sgrad"] = torch.empty((n_out,), dtype=torch.float32, device=dev)
-        d["ws"] = tl.empty_workspace(w.T, n_in, n_out, d["X"].dtype)
+        d["ws"] = tl.empty_workspace(w.T, n_in, n_out)
         d["host"] = p if not a.no_cpu_baseline else None
         projs.append(d)
     torch.cuda.synchronize()

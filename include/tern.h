@@ -106,10 +106,12 @@ int tern_linear_fwd(const void *X, int32_t act_dtype, const uint32_t *tern_packe
 
 /*
  * tern_linear_bwd_workspace_bytes -- device workspace (bytes) that
- * tern_linear_bwd needs for these sizes and this activation type.  Returns
+ * tern_linear_bwd and tern_linear_bwd_dw need for these sizes, with either
+ * activation type (the larger of the two types' plans: the split of the
+ * weight-gradient product over tokens depends on the element size).  Returns
  * 0 for invalid sizes.  The value depends only on its arguments.
  */
-size_t tern_linear_bwd_workspace_bytes(int64_t T, int64_t in, int64_t out, int32_t act_dtype);
+size_t tern_linear_bwd_workspace_bytes(int64_t T, int64_t in, int64_t out);
 
 /*
  * tern_linear_bwd -- all gradients of the projection.
@@ -119,7 +121,7 @@ size_t tern_linear_bwd_workspace_bytes(int64_t T, int64_t in, int64_t out, int32
  *   gq          fp32 [in, out] = (X^T . dY)[r, c] * scale[c].
  *   sgrad       fp32 [out]     = sum_r (X^T . dY)[r, c] * tern[r, c].
  *   workspace   device scratch of at least
- *               tern_linear_bwd_workspace_bytes(T, in, out, act_dtype) bytes
+ *               tern_linear_bwd_workspace_bytes(T, in, out) bytes
  *               (may be NULL when that is 0).  Its contents on entry are
  *               ignored and on return are unspecified.
  * Arithmetic: fp32 accumulation on the matrix cores.  With bf16 activations
@@ -173,8 +175,9 @@ int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype,
  *   Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, HIP.
  *
  * tern_linear_bwd_acc_workspace_bytes -- device workspace (bytes) that
- *   tern_linear_bwd_dw_acc needs (at least that of tern_linear_bwd: G always
- *   goes through the workspace here).  0 for invalid sizes.
+ *   tern_linear_bwd_dw_acc needs with either activation type (at least that
+ *   of tern_linear_bwd: G always goes through the workspace here).  0 for
+ *   invalid sizes.
  *
  * tern_linear_bwd_dw_acc -- with G = X^T . dY as in tern_linear_bwd:
  *   gq[r, c] += alpha * (G[r, c] * scale[c])   (fp32, read and written),
@@ -188,7 +191,7 @@ int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype,
 int tern_linear_bwd_dx_acc(const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
                            const float *scale, int64_t T, int64_t in, int64_t out,
                            float *dX, void *stream);
-size_t tern_linear_bwd_acc_workspace_bytes(int64_t T, int64_t in, int64_t out, int32_t act_dtype);
+size_t tern_linear_bwd_acc_workspace_bytes(int64_t T, int64_t in, int64_t out);
 int tern_linear_bwd_dw_acc(const void *X, const void *dY, int32_t act_dtype,
                            const uint32_t *tern_packed, const float *scale,
                            int64_t T, int64_t in, int64_t out, float alpha,
@@ -253,10 +256,9 @@ int tern_group_gather(const int8_t *const *q, const float *const *scale, const i
  *                prev_packed (the previous step's handle), over churn_total
  *                elements compared (calls with prev_packed NULL add none);
  *   scale_count, scale_sum, scale_min, scale_max  over the scale columns.
- * The page's fractions are the counts over total (churn over total when every
- * matrix was compared, else 0) and scale_sum / scale_count.  Integer counts
- * are exact; the scale sum is a fixed-order f64 sum per call, so repeated runs
- * give identical panels.
+ * The page's fractions of these counts come from tern_panel_fractions.
+ * Integer counts are exact; the scale sum is a fixed-order f64 sum per call,
+ * so repeated runs give identical panels.
  *
  * tern_panel_reset -- zero the accumulator (min +inf, max -inf).
  * tern_panel_add -- add one matrix: q int8 [in, out], scale fp32 [out],
@@ -280,6 +282,23 @@ int tern_panel_reset(tern_panel_t *panel, void *stream);
 int tern_panel_add(const int8_t *q, int64_t in, int64_t out, int32_t theta, int32_t q_clamp,
                    const uint32_t *prev_packed, const float *scale, tern_panel_t *panel,
                    void *stream);
+
+/*
+ * tern_panel_fractions -- the page's panel fractions (sr4_panel_compute's
+ * pct_neg, pct_zero, pct_pos, rail_pct, dead_pct, churn, and the scale mean)
+ * of an accumulator.  A HOST function: panel is a host copy of the device
+ * accumulator (copied after the adds have completed), out a host struct.
+ *   pct_neg, pct_zero, pct_pos, rail, dead = the count / total (0 when total
+ *   is 0); churn = churn / total when every counted element was compared
+ *   with a previous handle (churn_total == total > 0), else 0, as the page
+ *   reports churn only when a previous snapshot exists; scale_mean =
+ *   scale_sum / scale_count (0 when no column was counted).
+ * Errors: NULL.
+ */
+typedef struct tern_panel_fractions {
+    double pct_neg, pct_zero, pct_pos, rail, dead, churn, scale_mean;
+} tern_panel_fractions_t;
+int tern_panel_fractions(const tern_panel_t *panel, tern_panel_fractions_t *out);
 
 /*
  * Graphs of library calls.  The page's trainer launches every glue kernel and

@@ -34,20 +34,21 @@ SIGNATURES = {
     "tern_packed_words": (_i64, [_i64, _i64]),
     "tern_materialize": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp]),
     "tern_linear_fwd": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp]),
-    "tern_linear_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "tern_linear_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "tern_linear_bwd": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp,
                                        _vp, _vp, _sz, _vp]),
     "tern_linear_bwd_dx": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp]),
     "tern_linear_bwd_dw": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
                                           _vp, _sz, _vp]),
     "tern_linear_bwd_dx_acc": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp]),
-    "tern_linear_bwd_acc_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "tern_linear_bwd_acc_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "tern_linear_bwd_dw_acc": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, ctypes.c_float,
                                               _vp, _vp, _vp, _sz, _vp]),
     "tern_group_gather": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _vp, _vp, _vp]),
     "tern_scale_adamw": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32] + [ctypes.c_float] * 6 + [_vp]),
     "tern_panel_reset": (ctypes.c_int, [_vp, _vp]),
     "tern_panel_add": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "tern_panel_fractions": (ctypes.c_int, [_vp, _vp]),
     "tern_graph_begin": (ctypes.c_int, [_vp]),
     "tern_graph_end": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
     "tern_graph_launch": (ctypes.c_int, [_vp, _vp]),
@@ -115,6 +116,44 @@ def _check(fn: str, rc: int):
         raise TernError(fn, rc)
 
 
+_F32 = (torch.float32,)
+_ACT = (torch.bfloat16, torch.float32)
+
+
+def _need(fn: str, name: str, t, shape, dtypes) -> None:
+    """t must be a tensor of this shape and one of these dtypes."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {name} must be a tensor")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{fn}: {name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _need_bytes(fn: str, name: str, t, nbytes: int) -> None:
+    """t must hold at least nbytes (a packed handle, a workspace, a panel)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {name} must be a tensor")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{fn}: {name} holds {have} bytes, needs {nbytes}")
+
+
+def _need_packed(fn: str, t, n_in: int, n_out: int) -> None:
+    if not isinstance(t, torch.Tensor) or t.dtype not in (torch.int32, torch.uint32):
+        raise TypeError(f"{fn}: tern_packed must be an int32 tensor (see empty_packed)")
+    _need_bytes(fn, "tern_packed", t, 4 * max(tern_packed_words(n_in, n_out), 0))
+
+
+def _need_device(fn: str, *ts) -> None:
+    """Every tensor passed to the library lives on one GPU."""
+    devs = {t.device for t in ts if isinstance(t, torch.Tensor)}
+    if any(d.type != "cuda" for d in devs):
+        raise ValueError(f"{fn}: every tensor must be on a GPU (got {sorted(map(str, devs))})")
+    if len(devs) > 1:
+        raise ValueError(f"{fn}: tensors on several devices {sorted(map(str, devs))}")
+
+
 # ---------------------------------------------------------------------------
 # entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
@@ -131,15 +170,19 @@ def tern_packed_words(n_in: int, n_out: int) -> int:
     return int(lib().tern_packed_words(n_in, n_out))
 
 
-def tern_linear_bwd_workspace_bytes(T: int, n_in: int, n_out: int, act_dtype) -> int:
-    code = act_dtype if isinstance(act_dtype, int) else (
-        TERN_BF16 if act_dtype == torch.bfloat16 else TERN_F32)
-    return int(lib().tern_linear_bwd_workspace_bytes(T, n_in, n_out, code))
+def tern_linear_bwd_workspace_bytes(T: int, n_in: int, n_out: int) -> int:
+    return int(lib().tern_linear_bwd_workspace_bytes(T, n_in, n_out))
 
 
 def tern_materialize(q: torch.Tensor, theta: int, tern_packed: torch.Tensor, stream=None) -> None:
     """q int8 [in, out] -> packed ternary handle (see empty_packed)."""
+    fn = "tern_materialize"
+    if q.dim() != 2:
+        raise ValueError(f"{fn}: q must be [in, out]")
     n_in, n_out = q.shape
+    _need(fn, "q", q, (n_in, n_out), (torch.int8,))
+    _need_packed(fn, tern_packed, n_in, n_out)
+    _need_device(fn, q, tern_packed)
     rc = lib().tern_materialize(_ptr(q), n_in, n_out, int(theta), _ptr(tern_packed), _stream(stream))
     _check("tern_materialize", rc)
 
@@ -147,16 +190,42 @@ def tern_materialize(q: torch.Tensor, theta: int, tern_packed: torch.Tensor, str
 def tern_linear_fwd(X: torch.Tensor, tern_packed: torch.Tensor, scale: torch.Tensor, Y: torch.Tensor,
                     stream=None) -> None:
     """Y [T, out] (fp32 or bf16) = X [T, in] . (scale * tern)."""
+    fn = "tern_linear_fwd"
+    if X.dim() != 2 or scale.dim() != 1:
+        raise ValueError(f"{fn}: X must be [T, in] and scale [out]")
     T, n_in = X.shape
     n_out = scale.shape[0]
+    _need(fn, "X", X, (T, n_in), _ACT)
+    _need(fn, "scale", scale, (n_out,), _F32)
+    _need(fn, "Y", Y, (T, n_out), (torch.float32, X.dtype))
+    _need_packed(fn, tern_packed, n_in, n_out)
+    _need_device(fn, X, tern_packed, scale, Y)
     rc = lib().tern_linear_fwd(_ptr(X), _act_code(X), _ptr(tern_packed), _ptr(scale), T, n_in, n_out,
                                _ptr(Y), _act_code(Y), _stream(stream))
     _check("tern_linear_fwd", rc)
 
 
-def tern_linear_bwd(X, dY, tern_packed, scale, dX, gq, sgrad, workspace, stream=None) -> None:
+def _bwd_dw_checks(fn, X, dY, tern_packed, scale, gq, sgrad, workspace):
+    if X.dim() != 2 or scale.dim() != 1:
+        raise ValueError(f"{fn}: X must be [T, in] and scale [out]")
     T, n_in = X.shape
     n_out = scale.shape[0]
+    _need(fn, "X", X, (T, n_in), _ACT)
+    _need(fn, "dY", dY, (T, n_out), (X.dtype,))
+    _need(fn, "scale", scale, (n_out,), _F32)
+    _need(fn, "gq", gq, (n_in, n_out), _F32)
+    _need(fn, "sgrad", sgrad, (n_out,), _F32)
+    _need_packed(fn, tern_packed, n_in, n_out)
+    if workspace is not None:
+        _need_bytes(fn, "workspace", workspace, 0)
+    return T, n_in, n_out
+
+
+def tern_linear_bwd(X, dY, tern_packed, scale, dX, gq, sgrad, workspace, stream=None) -> None:
+    fn = "tern_linear_bwd"
+    T, n_in, n_out = _bwd_dw_checks(fn, X, dY, tern_packed, scale, gq, sgrad, workspace)
+    _need(fn, "dX", dX, (T, n_in), _F32)
+    _need_device(fn, X, dY, tern_packed, scale, dX, gq, sgrad, workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib().tern_linear_bwd(_ptr(X), _ptr(dY), _act_code(X), _ptr(tern_packed), _ptr(scale), T,
                                n_in, n_out, _ptr(dX), _act_code(dX), _ptr(gq), _ptr(sgrad),
@@ -164,17 +233,30 @@ def tern_linear_bwd(X, dY, tern_packed, scale, dX, gq, sgrad, workspace, stream=
     _check("tern_linear_bwd", rc)
 
 
-def tern_linear_bwd_dx(dY, tern_packed, scale, dX, n_in: int | None = None, stream=None) -> None:
+def _bwd_dx_checks(fn, dY, tern_packed, scale, dX, n_in):
+    if dY.dim() != 2 or scale.dim() != 1 or dX.dim() != 2:
+        raise ValueError(f"{fn}: dY must be [T, out], scale [out] and dX [T, in]")
     T, n_out = dY.shape
     n_in = dX.shape[1] if n_in is None else n_in
+    _need(fn, "dY", dY, (T, n_out), _ACT)
+    _need(fn, "scale", scale, (n_out,), _F32)
+    _need(fn, "dX", dX, (T, n_in), _F32)
+    _need_packed(fn, tern_packed, n_in, n_out)
+    _need_device(fn, dY, tern_packed, scale, dX)
+    return T, n_in, n_out
+
+
+def tern_linear_bwd_dx(dY, tern_packed, scale, dX, n_in: int | None = None, stream=None) -> None:
+    T, n_in, n_out = _bwd_dx_checks("tern_linear_bwd_dx", dY, tern_packed, scale, dX, n_in)
     rc = lib().tern_linear_bwd_dx(_ptr(dY), _act_code(dY), _ptr(tern_packed), _ptr(scale), T, n_in,
                                   n_out, _ptr(dX), _act_code(dX), _stream(stream))
     _check("tern_linear_bwd_dx", rc)
 
 
 def tern_linear_bwd_dw(X, dY, tern_packed, scale, gq, sgrad, workspace, stream=None) -> None:
-    T, n_in = X.shape
-    n_out = scale.shape[0]
+    fn = "tern_linear_bwd_dw"
+    T, n_in, n_out = _bwd_dw_checks(fn, X, dY, tern_packed, scale, gq, sgrad, workspace)
+    _need_device(fn, X, dY, tern_packed, scale, gq, sgrad, workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib().tern_linear_bwd_dw(_ptr(X), _ptr(dY), _act_code(X), _ptr(tern_packed), _ptr(scale), T,
                                   n_in, n_out, _ptr(gq), _ptr(sgrad), _ptr(workspace), ws_bytes,
@@ -184,26 +266,22 @@ def tern_linear_bwd_dw(X, dY, tern_packed, scale, gq, sgrad, workspace, stream=N
 
 def tern_linear_bwd_dx_acc(dY, tern_packed, scale, dX, n_in: int | None = None, stream=None) -> None:
     """dX (fp32) += dY . (scale * tern)^T."""
-    T, n_out = dY.shape
-    n_in = dX.shape[1] if n_in is None else n_in
-    if dX.dtype != torch.float32:
-        raise TypeError("dX must be float32")
+    T, n_in, n_out = _bwd_dx_checks("tern_linear_bwd_dx_acc", dY, tern_packed, scale, dX, n_in)
     rc = lib().tern_linear_bwd_dx_acc(_ptr(dY), _act_code(dY), _ptr(tern_packed), _ptr(scale), T, n_in, n_out,
                                       _ptr(dX), _stream(stream))
     _check("tern_linear_bwd_dx_acc", rc)
 
 
-def tern_linear_bwd_acc_workspace_bytes(T: int, n_in: int, n_out: int, act_dtype) -> int:
-    code = act_dtype if isinstance(act_dtype, int) else (
-        TERN_BF16 if act_dtype == torch.bfloat16 else TERN_F32)
-    return int(lib().tern_linear_bwd_acc_workspace_bytes(T, n_in, n_out, code))
+def tern_linear_bwd_acc_workspace_bytes(T: int, n_in: int, n_out: int) -> int:
+    return int(lib().tern_linear_bwd_acc_workspace_bytes(T, n_in, n_out))
 
 
 def tern_linear_bwd_dw_acc(X, dY, tern_packed, scale, gq, sgrad, workspace, alpha: float = 1.0,
                            stream=None) -> None:
     """gq += alpha * G * scale, sgrad += alpha * sum_r G * tern (G = X^T . dY)."""
-    T, n_in = X.shape
-    n_out = scale.shape[0]
+    fn = "tern_linear_bwd_dw_acc"
+    T, n_in, n_out = _bwd_dw_checks(fn, X, dY, tern_packed, scale, gq, sgrad, workspace)
+    _need_device(fn, X, dY, tern_packed, scale, gq, sgrad, workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib().tern_linear_bwd_dw_acc(_ptr(X), _ptr(dY), _act_code(X), _ptr(tern_packed), _ptr(scale), T,
                                       n_in, n_out, float(alpha), _ptr(gq), _ptr(sgrad), _ptr(workspace),
@@ -214,8 +292,20 @@ def tern_linear_bwd_dw_acc(X, dY, tern_packed, scale, gq, sgrad, workspace, alph
 def tern_group_gather(qs, scales, q_group: torch.Tensor, scale_group: torch.Tensor, stream=None) -> None:
     """q_group [in, sum out] and scale_group [sum out] from the members' q
     [in, out_i] and scale [out_i] (projections that read one input)."""
+    fn = "tern_group_gather"
     n = len(qs)
+    if n != len(scales):
+        raise ValueError(f"{fn}: {n} q matrices but {len(scales)} scales")
     n_in = qs[0].shape[0] if n else 0
+    for i, (qi, si) in enumerate(zip(qs, scales)):
+        if qi.dim() != 2:
+            raise ValueError(f"{fn}: q[{i}] must be [in, out_i]")
+        _need(fn, f"q[{i}]", qi, (n_in, qi.shape[1]), (torch.int8,))
+        _need(fn, f"scale[{i}]", si, (qi.shape[1],), _F32)
+    tot = sum(int(t.shape[1]) for t in qs)
+    _need(fn, "q_group", q_group, (n_in, tot), (torch.int8,))
+    _need(fn, "scale_group", scale_group, (tot,), _F32)
+    _need_device(fn, *qs, *scales, q_group, scale_group)
     qa = (_vp * max(n, 1))(*[_ptr(t) for t in qs])
     sa = (_vp * max(n, 1))(*[_ptr(t) for t in scales])
     oa = (_i64 * max(n, 1))(*[int(t.shape[1]) for t in qs])
@@ -227,6 +317,12 @@ def tern_scale_adamw(sgrad, scale, m, v, step: int, lr: float, scale_lr: float |
                      b2: float = 0.999, eps: float = 1e-8, wd: float = 0.0, stream=None) -> None:
     """AdamW step of the per-column scale from its gradient (in place on
     scale, m, v; scale_lr defaults to lr)."""
+    fn = "tern_scale_adamw"
+    if scale.dim() != 1:
+        raise ValueError(f"{fn}: scale must be [out]")
+    for name, t in (("sgrad", sgrad), ("scale", scale), ("m", m), ("v", v)):
+        _need(fn, name, t, scale.shape, _F32)
+    _need_device(fn, sgrad, scale, m, v)
     sl = lr if scale_lr is None else scale_lr
     rc = lib().tern_scale_adamw(_ptr(sgrad), _ptr(scale), _ptr(m), _ptr(v), int(scale.shape[0]), int(step),
                                 float(lr), float(sl), float(b1), float(b2), float(eps), float(wd),
@@ -243,7 +339,13 @@ def empty_panel(device="cuda") -> torch.Tensor:
     return torch.empty((len(PANEL_COUNTS) + len(PANEL_STATS),), dtype=torch.float64, device=device)
 
 
+def _need_panel(fn, panel):
+    _need(fn, "panel", panel, (len(PANEL_COUNTS) + len(PANEL_STATS),), (torch.float64,))
+
+
 def tern_panel_reset(panel: torch.Tensor, stream=None) -> None:
+    _need_panel("tern_panel_reset", panel)
+    _need_device("tern_panel_reset", panel)
     _check("tern_panel_reset", lib().tern_panel_reset(_ptr(panel), _stream(stream)))
 
 
@@ -251,25 +353,43 @@ def tern_panel_add(q: torch.Tensor, theta: int, scale: torch.Tensor, panel: torc
                    q_clamp: int = 7, stream=None) -> None:
     """Add one ternary matrix (q int8 [in, out], scale [out]) to the panel;
     prev_packed: the previous step's handle for churn, or None."""
+    fn = "tern_panel_add"
+    if q.dim() != 2:
+        raise ValueError(f"{fn}: q must be [in, out]")
     n_in, n_out = q.shape
+    _need(fn, "q", q, (n_in, n_out), (torch.int8,))
+    _need(fn, "scale", scale, (n_out,), _F32)
+    _need_panel(fn, panel)
+    if prev_packed is not None:
+        _need_packed(fn, prev_packed, n_in, n_out)
+    _need_device(fn, q, scale, panel, prev_packed)
     rc = lib().tern_panel_add(_ptr(q), n_in, n_out, int(theta), int(q_clamp), _ptr(prev_packed), _ptr(scale),
                               _ptr(panel), _stream(stream))
     _check("tern_panel_add", rc)
 
 
+PANEL_FRACTIONS = ("pct_neg", "pct_zero", "pct_pos", "rail_pct", "dead_pct", "churn_frac", "scale_mean")
+
+
+def tern_panel_fractions(panel_host: torch.Tensor) -> dict:
+    """The page's fractions of an accumulator (host copy), computed by the
+    library's tern_panel_fractions."""
+    h = panel_host.contiguous()
+    if h.device.type != "cpu" or h.numel() != len(PANEL_COUNTS) + len(PANEL_STATS) or h.dtype != torch.float64:
+        raise ValueError("tern_panel_fractions needs a host copy of one panel (12 x 8 bytes)")
+    out = (ctypes.c_double * len(PANEL_FRACTIONS))()
+    _check("tern_panel_fractions", lib().tern_panel_fractions(ctypes.c_void_p(h.data_ptr()), out))
+    return dict(zip(PANEL_FRACTIONS, list(out)))
+
+
 def panel_values(panel: torch.Tensor) -> dict:
-    """The accumulator's fields, and the page's fractions of them (churn only
-    when every element was compared with a previous handle)."""
+    """The accumulator's fields (copied to the host) and the page's fractions
+    of them from tern_panel_fractions."""
     h = panel.cpu()
     n = len(PANEL_COUNTS)
-    counts = h[:n].view(torch.int64).tolist()
-    r = dict(zip(PANEL_COUNTS, counts))
+    r = dict(zip(PANEL_COUNTS, h[:n].view(torch.int64).tolist()))
     r.update(zip(PANEL_STATS, h[n:].tolist()))
-    dt = float(r["total"]) if r["total"] else 1.0
-    valid = r["total"] > 0 and r["churn_total"] == r["total"]
-    r.update(pct_neg=r["neg"] / dt, pct_zero=r["zero"] / dt, pct_pos=r["pos"] / dt, rail_pct=r["rail"] / dt,
-             dead_pct=r["dead"] / dt, churn_frac=r["churn"] / dt if valid else 0.0,
-             scale_mean=r["scale_sum"] / r["scale_count"] if r["scale_count"] else 0.0)
+    r.update(tern_panel_fractions(h))
     return r
 
 
@@ -312,8 +432,9 @@ def packed_canonical(tern_packed: torch.Tensor, n_in: int, n_out: int) -> torch.
     return tern_packed.reshape(-1)[: n_in * wpr].view(n_in, wpr)
 
 
-def empty_workspace(T: int, n_in: int, n_out: int, act_dtype, device="cuda", acc: bool = False) -> torch.Tensor:
-    """Workspace of tern_linear_bwd / tern_linear_bwd_dw (acc: of tern_linear_bwd_dw_acc)."""
+def empty_workspace(T: int, n_in: int, n_out: int, device="cuda", acc: bool = False) -> torch.Tensor:
+    """Workspace of tern_linear_bwd / tern_linear_bwd_dw (acc: of
+    tern_linear_bwd_dw_acc), for either activation type."""
     q = tern_linear_bwd_acc_workspace_bytes if acc else tern_linear_bwd_workspace_bytes
-    nbytes = q(T, n_in, n_out, act_dtype)
+    nbytes = q(T, n_in, n_out)
     return torch.empty((max(nbytes, 16) // 16, 16), dtype=torch.uint8, device=device)

@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtern.so")
-SOURCES = ["tern_kernels.hip", "tern_panel.hip", "tern_group.hip", "tern_optim.hip", "tern_api.cpp", "tern_plan.cpp"]
+SOURCES = ["tern_kernels.hip", "tern_panel.hip", "tern_group.hip", "tern_optim.hip", "tern_api.cpp",
+           "tern_plan.cpp"]
 ARCH = "gfx950"
 
 # Packed FP32 VALU forms are turned off for all device code.

@@ -117,23 +117,23 @@ int tern_linear_fwd(const void *X, int32_t act_dtype, const uint32_t *tern_packe
     a.y_bf16 = y_dtype == TERN_BF16;
     a.frag = tern_packed + packed_layout(in, out).fwd_off;
     a.nch = (int)((in + kFragChunk - 1) / kFragChunk);
+    rc = check_gemm_args(p, a);
+    if (rc) return rc;
     return hip_status(launch_gemm(p, bf, a, st));
 }
 
-size_t tern_linear_bwd_workspace_bytes(int64_t T, int64_t in, int64_t out, int32_t act_dtype) {
-    if (validate_shape(T, in, out) != TERN_OK || !act_ok(act_dtype)) return 0;
-    return plan_bwd(T, in, out, act_dtype == TERN_BF16).total;
+size_t tern_linear_bwd_workspace_bytes(int64_t T, int64_t in, int64_t out) {
+    return bwd_workspace_bytes(T, in, out, false);
 }
 
-namespace {
+}  // extern "C"
 
-// Shared argument checks of the backward entry points.  Sizes of absent parts
-// (want_dx / want_dw false) are not checked; acc sizes the workspace for the
-// accumulating dW variant.
+namespace tern {
+
 int check_bwd(const void *X, const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
               const float *scale, int64_t T, int64_t in, int64_t out, void *dX, int32_t dx_dtype,
               float *gq, float *sgrad, void *workspace, size_t workspace_bytes, bool want_dx,
-              bool want_dw, bool acc, BwdLayout &L) {
+              bool want_dw, bool acc, BwdLayout &L, size_t ws_limit, bool check_ws) {
     int rc = validate_shape(T, in, out);
     if (rc) return rc;
     if (!act_ok(act_dtype) || (want_dx && dx_dtype != TERN_F32)) return TERN_ERR_DTYPE;
@@ -144,8 +144,8 @@ int check_bwd(const void *X, const void *dY, int32_t act_dtype, const uint32_t *
     const size_t sb = (size_t)out * 4;
     const size_t dxb = want_dx ? (size_t)T * in * 4 : 0;
     const size_t gqb = want_dw ? (size_t)in * out * 4 : 0, sgb = want_dw ? (size_t)out * 4 : 0;
-    L = plan_bwd(T, in, out, bf, acc);
-    const size_t wsb = want_dw ? L.total : 0;
+    L = plan_bwd(T, in, out, bf, acc, ws_limit);
+    const size_t wsb = want_dw && check_ws ? L.total : 0;
     if ((xb && !X) || (dyb && !dY) || (pb && !tern_packed) || (sb && !scale) || (dxb && !dX) ||
         (gqb && !gq) || (sgb && !sgrad))
         return TERN_ERR_NULL;
@@ -161,6 +161,8 @@ int check_bwd(const void *X, const void *dY, int32_t act_dtype, const uint32_t *
     return TERN_OK;
 }
 
+namespace {
+
 GemmArgs args_for(const GemmPlan &p, const uint32_t *tern_packed, const float *scale, int64_t T,
                   int64_t in, int64_t out) {
     GemmArgs a{};
@@ -173,34 +175,42 @@ GemmArgs args_for(const GemmPlan &p, const uint32_t *tern_packed, const float *s
     return a;
 }
 
-// acc: dX += dY . W_eff^T instead of dX = ...
-hipError_t enqueue_dx(const void *dY, bool bf, const uint32_t *tern_packed, const float *scale, int64_t T,
-                      int64_t in, int64_t out, void *dX, const BwdLayout &L, hipStream_t st, bool acc = false) {
+// host check, then the launch
+int checked_launch(const GemmPlan &p, bool bf, const GemmArgs &a, hipStream_t st) {
+    const int rc = check_gemm_args(p, a);
+    if (rc) return rc;
+    return hip_status(launch_gemm(p, bf, a, st));
+}
+
+}  // namespace
+
+int enqueue_dx(const void *dY, bool bf, const uint32_t *tern_packed, const float *scale, int64_t T,
+               int64_t in, int64_t out, void *dX, const BwdLayout &L, hipStream_t st, bool acc) {
     const size_t dxb = (size_t)T * in * 4;
-    if (dxb == 0) return hipSuccess;
-    if (out == 0) return acc ? hipSuccess : launch_zero(dX, dxb, st);  // empty sum
+    if (dxb == 0) return TERN_OK;
+    if (out == 0) return acc ? TERN_OK : hip_status(launch_zero(dX, dxb, st));  // empty sum
     GemmArgs a = args_for(L.dx, tern_packed, scale, T, in, out);
     a.acc = acc;
+    a.exact_scale = bf && dx_exact_scale(T, in, out);
     a.frag = tern_packed + packed_layout(in, out).dx_off;
     a.nch = (int)((out + kFragChunk - 1) / kFragChunk);
     a.act0 = dY;
     a.out_ptr = dX;
-    return launch_gemm(L.dx, bf, a, st);
+    return checked_launch(L.dx, bf, a, st);
 }
 
-// acc: gq += alpha * G * scale and sgrad += alpha * sum_r G * tern; G then
-// always goes through the workspace (L planned with acc).
-hipError_t enqueue_dw(const void *X, const void *dY, bool bf, const uint32_t *tern_packed, const float *scale,
-                      int64_t T, int64_t in, int64_t out, float *gq, float *sgrad, void *workspace,
-                      const BwdLayout &L, hipStream_t st, bool acc = false, float alpha = 1.0f) {
-    if (acc && (T == 0 || in == 0 || out == 0)) return hipSuccess;   // nothing to add
+int enqueue_dw(const void *X, const void *dY, bool bf, const uint32_t *tern_packed, const float *scale,
+               int64_t T, int64_t in, int64_t out, float *gq, float *sgrad, void *workspace,
+               const BwdLayout &L, hipStream_t st, bool acc, float alpha) {
+    if (acc && (T == 0 || in == 0 || out == 0)) return TERN_OK;   // nothing to add
     if (T == 0 || in == 0 || out == 0) {
         // G is an empty sum (T == 0) or empty: gq = 0 and sgrad = 0 where they exist
         hipError_t e = hipSuccess;
         if ((size_t)in * out) e = launch_zero(gq, (size_t)in * out * 4, st);
         if (e == hipSuccess && out) e = launch_zero(sgrad, (size_t)out * 4, st);
-        return e;
+        return hip_status(e);
     }
+    if (!workspace) return TERN_ERR_WORKSPACE;   // the partial table (and split partials) live there
     float *part = (float *)((char *)workspace + L.part_off);
     GemmArgs a = args_for(L.dw, tern_packed, scale, T, in, out);
     a.frag = tern_packed + packed_layout(in, out).fwd_off;   // tern codes for the sgrad partials
@@ -208,45 +218,49 @@ hipError_t enqueue_dw(const void *X, const void *dY, bool bf, const uint32_t *te
     a.act1 = dY;
     a.part = part;
     a.acc = acc;
-    hipError_t e;
+    int rc;
     if (L.dw.splits > 1 || acc) {
         float *ws = (float *)((char *)workspace + L.ws_off);
         a.out_ptr = ws;
-        e = launch_gemm(L.dw, bf, a, st);
-        if (e == hipSuccess)
-            e = launch_dw_reduce(ws, (int)L.dw.splits, scale, tern_packed, in, out, gq, part, acc, alpha, st);
+        rc = checked_launch(L.dw, bf, a, st);
+        if (rc == TERN_OK)
+            rc = hip_status(
+                launch_dw_reduce(ws, (int)L.dw.splits, scale, tern_packed, in, out, gq, part, acc, alpha, st));
     } else {
         a.out_ptr = gq;
-        e = launch_gemm(L.dw, bf, a, st);
+        rc = checked_launch(L.dw, bf, a, st);
     }
-    if (e == hipSuccess) e = launch_sgrad_reduce(part, L.part_rows, out, sgrad, acc, alpha, st);
-    return e;
+    if (rc == TERN_OK) rc = hip_status(launch_sgrad_reduce(part, L.part_rows, out, sgrad, acc, alpha, st));
+    return rc;
 }
 
-}  // namespace
+}  // namespace tern
+
+extern "C" {
 
 int tern_linear_bwd(const void *X, const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
                     const float *scale, int64_t T, int64_t in, int64_t out, void *dX, int32_t dx_dtype,
                     float *gq, float *sgrad, void *workspace, size_t workspace_bytes, void *stream) {
     BwdLayout L;
     int rc = check_bwd(X, dY, act_dtype, tern_packed, scale, T, in, out, dX, dx_dtype, gq, sgrad,
-                       workspace, workspace_bytes, true, true, false, L);
+                       workspace, workspace_bytes, true, true, false, L, ~size_t(0), true);
     if (rc) return rc;
     const bool bf = act_dtype == TERN_BF16;
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = enqueue_dx(dY, bf, tern_packed, scale, T, in, out, dX, L, st);
-    if (e == hipSuccess) e = enqueue_dw(X, dY, bf, tern_packed, scale, T, in, out, gq, sgrad, workspace, L, st);
-    return hip_status(e);
+    rc = enqueue_dx(dY, bf, tern_packed, scale, T, in, out, dX, L, st, false);
+    if (rc == TERN_OK)
+        rc = enqueue_dw(X, dY, bf, tern_packed, scale, T, in, out, gq, sgrad, workspace, L, st, false, 1.0f);
+    return rc;
 }
 
 int tern_linear_bwd_dx(const void *dY, int32_t act_dtype, const uint32_t *tern_packed, const float *scale,
                        int64_t T, int64_t in, int64_t out, void *dX, int32_t dx_dtype, void *stream) {
     BwdLayout L;
     int rc = check_bwd(nullptr, dY, act_dtype, tern_packed, scale, T, in, out, dX, dx_dtype, nullptr,
-                       nullptr, nullptr, 0, true, false, false, L);
+                       nullptr, nullptr, 0, true, false, false, L, ~size_t(0), true);
     if (rc) return rc;
-    return hip_status(enqueue_dx(dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, dX, L,
-                                 (hipStream_t)stream));
+    return enqueue_dx(dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, dX, L, (hipStream_t)stream,
+                      false);
 }
 
 int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
@@ -254,27 +268,26 @@ int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype, const u
                        void *workspace, size_t workspace_bytes, void *stream) {
     BwdLayout L;
     int rc = check_bwd(X, dY, act_dtype, tern_packed, scale, T, in, out, nullptr, TERN_F32, gq, sgrad,
-                       workspace, workspace_bytes, false, true, false, L);
+                       workspace, workspace_bytes, false, true, false, L, ~size_t(0), true);
     if (rc) return rc;
-    return hip_status(enqueue_dw(X, dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, gq, sgrad,
-                                 workspace, L, (hipStream_t)stream));
+    return enqueue_dw(X, dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, gq, sgrad, workspace, L,
+                      (hipStream_t)stream, false, 1.0f);
 }
 
 // ---- accumulating variants
 
-size_t tern_linear_bwd_acc_workspace_bytes(int64_t T, int64_t in, int64_t out, int32_t act_dtype) {
-    if (validate_shape(T, in, out) != TERN_OK || !act_ok(act_dtype)) return 0;
-    return plan_bwd(T, in, out, act_dtype == TERN_BF16, true).total;
+size_t tern_linear_bwd_acc_workspace_bytes(int64_t T, int64_t in, int64_t out) {
+    return bwd_workspace_bytes(T, in, out, true);
 }
 
 int tern_linear_bwd_dx_acc(const void *dY, int32_t act_dtype, const uint32_t *tern_packed, const float *scale,
                            int64_t T, int64_t in, int64_t out, float *dX, void *stream) {
     BwdLayout L;
     int rc = check_bwd(nullptr, dY, act_dtype, tern_packed, scale, T, in, out, dX, TERN_F32, nullptr, nullptr,
-                       nullptr, 0, true, false, false, L);
+                       nullptr, 0, true, false, false, L, ~size_t(0), true);
     if (rc) return rc;
-    return hip_status(enqueue_dx(dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, dX, L,
-                                 (hipStream_t)stream, true));
+    return enqueue_dx(dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, dX, L, (hipStream_t)stream,
+                      true);
 }
 
 int tern_linear_bwd_dw_acc(const void *X, const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
@@ -282,10 +295,27 @@ int tern_linear_bwd_dw_acc(const void *X, const void *dY, int32_t act_dtype, con
                            float *sgrad, void *workspace, size_t workspace_bytes, void *stream) {
     BwdLayout L;
     int rc = check_bwd(X, dY, act_dtype, tern_packed, scale, T, in, out, nullptr, TERN_F32, gq, sgrad, workspace,
-                       workspace_bytes, false, true, true, L);
+                       workspace_bytes, false, true, true, L, ~size_t(0), true);
     if (rc) return rc;
-    return hip_status(enqueue_dw(X, dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, gq, sgrad,
-                                 workspace, L, (hipStream_t)stream, true, alpha));
+    return enqueue_dw(X, dY, act_dtype == TERN_BF16, tern_packed, scale, T, in, out, gq, sgrad, workspace, L,
+                      (hipStream_t)stream, true, alpha);
+}
+
+// ---- the panel's fractions (host arithmetic on a host copy of the accumulator)
+
+int tern_panel_fractions(const tern_panel_t *panel, tern_panel_fractions_t *out) {
+    if (!panel || !out) return TERN_ERR_NULL;
+    const double total = (double)panel->total;
+    auto frac = [&](uint64_t n) { return panel->total ? (double)n / total : 0.0; };
+    out->pct_neg = frac(panel->neg);
+    out->pct_zero = frac(panel->zero);
+    out->pct_pos = frac(panel->pos);
+    out->rail = frac(panel->rail);
+    out->dead = frac(panel->dead);
+    // churn is a fraction only when every counted element had a previous code
+    out->churn = (panel->total && panel->churn_total == panel->total) ? frac(panel->churn) : 0.0;
+    out->scale_mean = panel->scale_count ? panel->scale_sum / (double)panel->scale_count : 0.0;
+    return TERN_OK;
 }
 
 // ---- graphs of library calls: stream capture, instantiation, replay

@@ -10,23 +10,6 @@
 
 namespace tern {
 
-// Kernel arguments of the three MFMA GEMMs (see tern_plan.h for M, N, K).
-struct GemmArgs {
-    const void *act0;        // FWD: X, DX: dY, DW: X
-    const void *act1;        // DW: dY
-    const uint32_t *packed;  // tern, 2-bit packed [in][wpr]
-    const uint32_t *frag;    // FWD / DX: this product's fragment-ordered copy of tern
-    const float *scale;      // [out]
-    void *out_ptr;           // FWD: Y, DX: dX, DW: gq (1 split) or split partials
-    float *part;             // DW with 1 split: sgrad partials [tiles_m][out]
-    int M, N, K;
-    int tiles_m, tiles_n, splits, kps;
-    int in, out, wpr, T;
-    int y_bf16;
-    int nch;                 // FWD / DX: chunks of 32 K per tile in the fragment copy
-    int acc;                 // DX: add to the existing dX; DW: raw G into out_ptr even with one split
-};
-
 hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStream_t st);
 // The whole packed handle (canonical words, padding, both fragment-ordered
 // copies; see PackedLayout) from q in one launch.
@@ -40,5 +23,23 @@ hipError_t launch_dw_reduce(const float *ws, int splits, const float *scale, con
 hipError_t launch_sgrad_reduce(const float *part, int64_t nparts, int64_t out, float *sgrad, bool acc, float alpha,
                                hipStream_t st);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
+
+// Backward pieces shared by the entry points (tern_api.cpp, tern_noalloc.hip).
+// check_bwd validates the arguments of a backward call (want_dx / want_dw
+// select the parts) and plans it with a workspace of at most ws_limit bytes;
+// check_ws false leaves the workspace pointer and size out of the checks (the
+// caller supplies the workspace itself).  The enqueue functions return a
+// TERN_* status.
+int check_bwd(const void *X, const void *dY, int32_t act_dtype, const uint32_t *tern_packed,
+              const float *scale, int64_t T, int64_t in, int64_t out, void *dX, int32_t dx_dtype,
+              float *gq, float *sgrad, void *workspace, size_t workspace_bytes, bool want_dx,
+              bool want_dw, bool acc, BwdLayout &L, size_t ws_limit, bool check_ws);
+int enqueue_dx(const void *dY, bool bf, const uint32_t *tern_packed, const float *scale, int64_t T,
+               int64_t in, int64_t out, void *dX, const BwdLayout &L, hipStream_t st, bool acc);
+// acc: gq += alpha * G * scale and sgrad += alpha * sum_r G * tern; G then
+// always goes through the workspace (L planned with acc).
+int enqueue_dw(const void *X, const void *dY, bool bf, const uint32_t *tern_packed, const float *scale,
+               int64_t T, int64_t in, int64_t out, float *gq, float *sgrad, void *workspace,
+               const BwdLayout &L, hipStream_t st, bool acc, float alpha);
 
 }  // namespace tern

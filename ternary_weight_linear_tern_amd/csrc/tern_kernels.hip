@@ -300,7 +300,10 @@ struct StageTernT {
 // dX weight operand: rows m = input rows r, K = output columns c (contiguous in
 // the packed words), values tern * scale[c].  Each unit is one packed word
 // (16 consecutive c of one r); the unit's K quarter is fixed per thread, so the
-// 16 scales are loaded (and rounded to bf16) once per K step.
+// 16 scales are loaded (and rounded to bf16) once per K step.  bf16: a step of
+// the first pass over K uses hi = bf16(scale), a step of the second pass (exact
+// scale) lo = bf16(scale - hi), so the two passes together carry the scale to
+// about 16 significant bits.
 template <bool BF, int R>
 struct StageTernS {
     static constexpr int WPK = BF ? 4 : 2;   // packed words per row per K step
@@ -315,6 +318,7 @@ struct StageTernS {
     uint32_t roff[UPT];
     uint32_t w[2][UPT];
     f32x4 s[2][4];
+    bool lo[2];         // register set S holds a second-pass (scale - hi) step
 
     __device__ __forceinline__ void init(const uint32_t *p, int64_t wpr_, int rows_valid,
                                          const float *sc, int out_) {
@@ -330,9 +334,11 @@ struct StageTernS {
             roff[i] = (act && row < rows_valid) ? (uint32_t)(row * wpr * 4) : OOB;
         }
     }
-    // k0: first output column of this K step (multiple of 16)
+    // k0: first output column of this K step (multiple of 16); second: the
+    // step belongs to the second pass over K
     template <int S>
-    __device__ __forceinline__ void fetch(int k0) {
+    __device__ __forceinline__ void fetch(int k0, bool second = false) {
+        lo[S] = second;
         const int wq = threadIdx.x % WPK;
         const int wcol = (k0 >> 4) + wq;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)(k0 >> 4) * 4);
@@ -359,7 +365,14 @@ struct StageTernS {
             uint32_t s2[4];
 #pragma unroll
             for (int q = 0; q < 2; q++) {
-                const f32x4 sq = s[S][2 * c + q];
+                f32x4 sq = s[S][2 * c + q];
+                if (lo[S]) {
+                    // the part of the scale that bf16 rounding dropped
+                    const f32x2 a0 = {sq.x, sq.y}, b0 = {sq.z, sq.w};
+                    const f32x2 ah = __builtin_convertvector(__builtin_convertvector(a0, bf16x2), f32x2);
+                    const f32x2 bh = __builtin_convertvector(__builtin_convertvector(b0, bf16x2), f32x2);
+                    sq = f32x4{sq.x - ah.x, sq.y - ah.y, sq.z - bh.x, sq.w - bh.y};
+                }
                 f32x2 a = {sq.x, sq.y}, b = {sq.z, sq.w};
                 s2[2 * q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
                 s2[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2));
@@ -449,6 +462,11 @@ void gemm_kernel(GemmArgs g) {
     const int64_t kbeg = (int64_t)sp * g.kps;
     const int64_t kend = min((int64_t)g.K, kbeg + g.kps);
     const int nk = (int)((kend - kbeg + BK - 1) / BK);
+    // dX with bf16 activations and the exact scale: the K steps run twice,
+    // the second time with the scale's bf16 remainder (steps past the last
+    // load nothing)
+    const int passes = (MODE == MODE_DX && BF && g.exact_scale) ? 2 : 1;
+    const int nsteps = passes * nk;
 
     using SA = typename std::conditional<
         MODE == MODE_FWD, StageTernT<BF, BM>,
@@ -471,15 +489,17 @@ void gemm_kernel(GemmArgs g) {
     }
     const int64_t klen = kend - kbeg;
 
-    auto fetch = [&](auto set_c, int it) {
+    auto fetch = [&](auto set_c, int it_all) {
         constexpr int S = decltype(set_c)::value;
+        const bool second = it_all >= nk && it_all < nsteps;
+        const int it = it_all < nsteps ? it_all - (second ? nk : 0) : nk;   // nk: past the end
         const int64_t k0 = (int64_t)it * BK;  // relative to kbeg
         const int krem = (int)max<int64_t>(-1, min<int64_t>(BK, klen - k0));
         if constexpr (MODE == MODE_FWD) {
             sa.template fetch<S>(k0, krem);
             sb.template fetch<S>((int)(k0 * ES));
         } else if constexpr (MODE == MODE_DX) {
-            sa.template fetch<S>((int)k0);
+            sa.template fetch<S>((int)k0, second);
             sb.template fetch<S>((int)(k0 * ES));
         } else {
             sa.template fetch<S>(k0, krem);
@@ -535,7 +555,7 @@ void gemm_kernel(GemmArgs g) {
         };
         // pairs of steps keep the register sets static; an odd count runs one
         // extra step on an all-zero buffer, which adds nothing
-        for (int it = 0; it < nk; it += 2) {
+        for (int it = 0; it < nsteps; it += 2) {
             body(I0{}, it);
             body(I1{}, it + 1);
         }
@@ -1311,6 +1331,7 @@ void gemm_rd_kernel(GemmArgs g) {
     const int nch = g.nch;
     const int nch2 = (nch + 1) & ~1;   // chunks per tile, padded to even for the 2-way unroll
     const int64_t ld = (int64_t)g.K * ES;   // bytes per activation row
+    const int ld32 = g.K * ES;              // the same (K <= 2^20)
     char *wl = r_lds + wave * R_WAVE;
     // slot of this lane's 16 bytes in every DMA row group, and its logical chunk
     const int cb = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
@@ -1323,8 +1344,9 @@ void gemm_rd_kernel(GemmArgs g) {
     // offsets per lane, so every byte past an edge reads as zero: the ragged
     // K end of the tensor's last row, the even-padding chunk of the fragment
     // words, and (record counts 0) every issue after the last tile.  Inside
-    // the tensor, bytes past K belong to the next row; they meet zero ternary
-    // codes and add nothing for finite inputs.  Four activation loads share
+    // the tensor, bytes past K belong to the next row: in a chunk that reaches
+    // past K, the lanes whose 16 bytes lie there get an out-of-range offset
+    // (a wave-uniform test, taken only in such chunks).  Four activation loads share
     // one M0: the immediate offset 1024 i moves the LDS destination and the
     // global address alike, and the lane offsets are stored less 1024 i
     // (which needs K >= 32: 16 rows of 2 K bytes span 1024 bytes).
@@ -1376,8 +1398,19 @@ void gemm_rd_kernel(GemmArgs g) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(pa, na);
             const int so = ic * R_KC * ES;
             char *d = st + (P >> 1) * 4096;
-            dma16_imm<(P & 1) * 2048>(ra, d, boff[2 * P], so);
-            dma16_imm<(P & 1) * 2048 + 1024>(ra, d, boff[2 * P + 1], so);
+            uint32_t o0 = boff[2 * P], o1 = boff[2 * P + 1];
+            if (so + R_KC * ES > ld32) {
+                // a chunk reaching past K (the ragged last one or the padding
+                // one): a lane whose 16 bytes lie past K loads nothing, so no
+                // byte of the next token row meets the zero ternary codes (a
+                // non-finite value there would turn the sum into NaN)
+                if (so + cb >= ld32) {
+                    o0 = OOB - 1024u * (uint32_t)((2 * P) & 3);
+                    o1 = OOB - 1024u * (uint32_t)((2 * P + 1) & 3);
+                }
+            }
+            dma16_imm<(P & 1) * 2048>(ra, d, o0, so);
+            dma16_imm<(P & 1) * 2048 + 1024>(ra, d, o1, so);
         } else {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(pf, nf), (LDS_AS void *)(st + R_B), 16,
                                                      (uint32_t)lane * 16u, ic * 2048, 0, 0);
@@ -1811,7 +1844,9 @@ hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)p.grid), block(dev::NT);
     if constexpr (BF) {
         // the shared-M0 loads need K >= 32 (forward / dX) and M, N >= 256 (dW)
-        if (p.tile == TILE_256 && (MODE == MODE_DW ? a.M >= 256 && a.N >= 256 : a.K >= 32)) {
+        // (the exact two-term dX scale runs on the LDS-staged kernel)
+        if (p.tile == TILE_256 && (MODE == MODE_DW ? a.M >= 256 && a.N >= 256 : a.K >= 32) &&
+            !(MODE == MODE_DX && a.exact_scale)) {
             // persistent: at most one workgroup per compute unit
             const int64_t cus = device_cus();
             const dim3 pgrid((unsigned)(p.grid < cus ? p.grid : cus));
@@ -1835,6 +1870,8 @@ hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStream_t st) {
     if (p.grid <= 0) return hipSuccess;
+    // no kernel is enqueued with a pointer it dereferences missing
+    if (check_gemm_args(p, a) != 0) return hipErrorInvalidValue;
     if (bf16) {
         if (p.mode == MODE_FWD) return launch_mode<true, MODE_FWD>(p, a, st);
         if (p.mode == MODE_DX) return launch_mode<true, MODE_DX>(p, a, st);

@@ -55,7 +55,7 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-GemmPlan plan_gemm(int mode, int64_t T, int64_t in, int64_t out, bool bf16) {
+GemmPlan plan_gemm(int mode, int64_t T, int64_t in, int64_t out, bool bf16, int64_t max_splits) {
     GemmPlan p;
     p.mode = mode;
     if (mode == MODE_FWD) { p.M = out; p.N = T; p.K = in; }
@@ -77,6 +77,7 @@ GemmPlan plan_gemm(int mode, int64_t T, int64_t in, int64_t out, bool bf16) {
             max_s = ksteps / 8;  // keep >= 8 K steps per split
             if (max_s < 1) max_s = 1;
             if (max_s > 32) max_s = 32;
+            if (max_splits > 0 && max_s > max_splits) max_s = max_splits;
         }
         for (int64_t s = 1; s <= max_s; s *= 2) {
             const int64_t kps = cdiv(ksteps, s) * kstep;
@@ -105,22 +106,50 @@ GemmPlan plan_gemm(int mode, int64_t T, int64_t in, int64_t out, bool bf16) {
     return p;
 }
 
-BwdLayout plan_bwd(int64_t T, int64_t in, int64_t out, bool bf16, bool acc) {
+bool dx_exact_scale(int64_t T, int64_t in, int64_t out) {
+    return out < kFoldMinCols || T * in < kFoldMinOutputs;
+}
+
+int check_gemm_args(const GemmPlan &p, const GemmArgs &a) {
+    if (p.grid <= 0) return TERN_OK;   // nothing is launched
+    if (!a.act0 || !a.scale || !a.out_ptr) return TERN_ERR_NULL;
+    if (p.mode == MODE_DW && !a.act1) return TERN_ERR_NULL;
+    if (!a.packed) return TERN_ERR_NULL;
+    // the 256-tile kernels read the fragment-ordered copies (the dW epilogue
+    // its tern codes)
+    if (p.tile == TILE_256 && !a.frag) return TERN_ERR_NULL;
+    if (p.mode == MODE_DW && p.splits == 1 && !a.acc && !a.part) return TERN_ERR_WORKSPACE;
+    return TERN_OK;
+}
+
+BwdLayout plan_bwd(int64_t T, int64_t in, int64_t out, bool bf16, bool acc, size_t ws_limit) {
     BwdLayout L;
     L.dx = plan_gemm(MODE_DX, T, in, out, bf16);
-    L.dw = plan_gemm(MODE_DW, T, in, out, bf16);
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
-    if (T > 0 && in > 0 && out > 0) {
-        const int64_t bm = tile_bm(L.dw.tile);
-        const bool raw = L.dw.splits > 1 || acc;   // G through the workspace and the reduce kernel
-        L.part_rows = raw ? cdiv(in, kReduceRows) : cdiv(in, bm);
-        L.part_off = 0;
-        L.part_bytes = al(size_t(L.part_rows) * size_t(out) * 4);
-        L.ws_off = L.part_bytes;
-        L.ws_bytes = raw ? al(size_t(L.dw.splits) * size_t(in) * size_t(out) * 4) : 0;
+    for (int64_t cap = 0;;) {
+        L.dw = plan_gemm(MODE_DW, T, in, out, bf16, cap);
+        L.part_rows = 0;
+        L.part_off = L.part_bytes = L.ws_off = L.ws_bytes = 0;
+        if (T > 0 && in > 0 && out > 0) {
+            const int64_t bm = tile_bm(L.dw.tile);
+            const bool raw = L.dw.splits > 1 || acc;   // G through the workspace and the reduce kernel
+            L.part_rows = raw ? cdiv(in, kReduceRows) : cdiv(in, bm);
+            L.part_off = 0;
+            L.part_bytes = al(size_t(L.part_rows) * size_t(out) * 4);
+            L.ws_off = L.part_bytes;
+            L.ws_bytes = raw ? al(size_t(L.dw.splits) * size_t(in) * size_t(out) * 4) : 0;
+        }
+        L.total = L.part_bytes + L.ws_bytes;
+        if (L.total <= ws_limit || L.dw.splits <= 1) break;
+        cap = L.dw.splits - 1;   // the next plan has fewer splits
     }
-    L.total = L.part_bytes + L.ws_bytes;
     return L;
+}
+
+size_t bwd_workspace_bytes(int64_t T, int64_t in, int64_t out, bool acc) {
+    if (validate_shape(T, in, out) != TERN_OK) return 0;
+    const size_t a = plan_bwd(T, in, out, true, acc).total, b = plan_bwd(T, in, out, false, acc).total;
+    return a > b ? a : b;
 }
 
 }  // namespace tern

@@ -37,7 +37,48 @@ struct GemmPlan {
 // K step of the main loop per element type: 64 bf16 or 32 fp32 (128 bytes).
 inline int k_step(bool bf16) { return bf16 ? 64 : 32; }
 
-GemmPlan plan_gemm(int mode, int64_t T, int64_t in, int64_t out, bool bf16);
+// max_splits caps the dW split-K count (the planner picks the best count up to
+// it; 0 means no cap).
+GemmPlan plan_gemm(int mode, int64_t T, int64_t in, int64_t out, bool bf16, int64_t max_splits = 0);
+
+// Kernel arguments of the three MFMA GEMMs (M, N, K as above).
+struct GemmArgs {
+    const void *act0;        // FWD: X, DX: dY, DW: X
+    const void *act1;        // DW: dY
+    const uint32_t *packed;  // tern, 2-bit packed [in][wpr]
+    const uint32_t *frag;    // FWD / DX: this product's fragment-ordered copy of tern;
+                             // DW: the forward copy (tern codes of the sgrad partials)
+    const float *scale;      // [out]
+    void *out_ptr;           // FWD: Y, DX: dX, DW: gq (1 split) or split partials
+    float *part;             // DW with 1 split: sgrad partials [tiles_m][out]
+    int M, N, K;
+    int tiles_m, tiles_n, splits, kps;
+    int in, out, wpr, T;
+    int y_bf16;
+    int nch;                 // FWD / DX: chunks of 32 K per tile in the fragment copy
+    int acc;                 // DX: add to the existing dX; DW: raw G into out_ptr even with one split
+    int exact_scale;         // DX, bf16: the scale as the sum of two bf16 terms (two passes over K)
+};
+
+// dX with bf16 activations: does the scale go into the operand as the sum of
+// two bf16 terms (hi = bf16(scale), lo = bf16(scale - hi), two passes over K)
+// instead of one rounded term?  One rounded term has a relative error of up to
+// 2^-8 per column (rms 1.6e-3), and the rel-L2 of dX is a weighted mean of
+// those errors, which concentrates near 1.66e-3 only with many reduction
+// columns and many outputs; with few of either it exceeds 2e-3 for a sizeable
+// fraction of inputs.  Two terms bring it to about 1e-5 at twice the dX
+// product's matrix work, so they are used where that work is small: fewer
+// than 512 columns (out) or fewer than 65536 outputs (T * in).
+bool dx_exact_scale(int64_t T, int64_t in, int64_t out);
+constexpr int64_t kFoldMinCols = 512;
+constexpr int64_t kFoldMinOutputs = 65536;
+
+// Host check of the pointers a launch of plan p dereferences: every operand,
+// the output, the fragment copy, and the sgrad partial table wherever the dW
+// epilogue writes partials (one split, not accumulating).  TERN_OK, or
+// TERN_ERR_NULL for a missing operand or output, TERN_ERR_WORKSPACE for a
+// missing partial table.  Every launcher calls it before enqueueing a kernel.
+int check_gemm_args(const GemmPlan &p, const GemmArgs &a);
 
 // Backward workspace layout (byte offsets, 256-byte aligned).
 struct BwdLayout {
@@ -49,8 +90,15 @@ struct BwdLayout {
 };
 
 // acc: the accumulating dW variant, whose G always goes through the split
-// workspace (raw G, then the reduce kernel adds to gq).
-BwdLayout plan_bwd(int64_t T, int64_t in, int64_t out, bool bf16, bool acc = false);
+// workspace (raw G, then the reduce kernel adds to gq).  ws_limit: the largest
+// workspace the caller has; the dW split count is lowered until the layout
+// fits (total > ws_limit only if even one split does not fit).
+BwdLayout plan_bwd(int64_t T, int64_t in, int64_t out, bool bf16, bool acc = false,
+                   size_t ws_limit = ~size_t(0));
+
+// Workspace bytes that serve either activation type: the larger of the two
+// plans (0 for invalid sizes).
+size_t bwd_workspace_bytes(int64_t T, int64_t in, int64_t out, bool acc);
 
 // Row-block height of the split-K reduction (and thus of its sgrad partials).
 constexpr int kReduceRows = 4;

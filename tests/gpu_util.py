@@ -57,7 +57,7 @@ class DeviceProjection:
         self.dX = torch.empty((T, n_in), dtype=torch.float32, device="cuda")
         self.gq = torch.empty((n_in, n_out), dtype=torch.float32, device="cuda")
         self.sgrad = torch.empty((n_out,), dtype=torch.float32, device="cuda")
-        self.ws = tl.empty_workspace(T, n_in, n_out, self.X.dtype)
+        self.ws = tl.empty_workspace(T, n_in, n_out)
 
     def materialize(self, theta=None):
         tl.tern_materialize(self.q, self.p.theta if theta is None else theta, self.packed)

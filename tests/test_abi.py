@@ -118,7 +118,7 @@ def test_bwd_rejects(L):
     X, dY, pk, sc = P(0x1000000), P(0x2000000), P(0x3000000), P(0x4000000)
     dX, gq, sg = P(0x5000000), P(0x6000000), P(0x7000000)
     T, n_in, n_out = 4096, 2048, 2048
-    need = tl.tern_linear_bwd_workspace_bytes(T, n_in, n_out, BF16)
+    need = tl.tern_linear_bwd_workspace_bytes(T, n_in, n_out)
     ws = P(0x10000000)
     assert b(X, dY, BF16, pk, sc, T, n_in, n_out, dX, BF16, gq, sg, ws, need, s) == DTYPE
     assert b(X, dY, 3, pk, sc, T, n_in, n_out, dX, F32, gq, sg, ws, need, s) == DTYPE
@@ -146,17 +146,39 @@ def test_bwd_parts_reject(L):
 
 
 def test_workspace_bytes(L):
-    assert tl.tern_linear_bwd_workspace_bytes(-1, 8, 8, BF16) == 0
-    assert tl.tern_linear_bwd_workspace_bytes(8, 12, 8, BF16) == 0
-    assert tl.tern_linear_bwd_workspace_bytes(8, 8, 8, 9) == 0
-    assert tl.tern_linear_bwd_workspace_bytes(0, 64, 64, BF16) == 0
+    """Three arguments, as the boundary states it: the workspace serves either
+    activation type."""
+    assert tl.SIGNATURES["tern_linear_bwd_workspace_bytes"][1] == [ctypes.c_int64] * 3
+    assert tl.SIGNATURES["tern_linear_bwd_acc_workspace_bytes"][1] == [ctypes.c_int64] * 3
+    assert tl.tern_linear_bwd_workspace_bytes(-1, 8, 8) == 0
+    assert tl.tern_linear_bwd_workspace_bytes(8, 12, 8) == 0
+    assert tl.tern_linear_bwd_workspace_bytes(0, 64, 64) == 0
     for (T, i, o) in [(64, 64, 64), (2048, 512, 512), (16384, 2048, 2048), (32768, 4096, 16384),
-                      (1000, 200, 72)]:
+                      (1000, 200, 72), (4000, 1032, 1032)]:
+        w = tl.tern_linear_bwd_workspace_bytes(T, i, o)
+        # always room for at least one row of sgrad partials, 256-byte granular
+        assert w >= 4 * o and w % 256 == 0, (T, i, o, w)
+        assert tl.tern_linear_bwd_workspace_bytes(T, i, o) == w  # pure function
+
+
+def test_bwd_accepts_the_three_argument_workspace(L):
+    """A workspace of tern_linear_bwd_workspace_bytes(T, in, out) bytes passes
+    the backward's workspace check for both activation types.  The checks run
+    NULL, WORKSPACE, ALIGN, ALIAS in that order, so a misaligned dX reports
+    ALIGN once the workspace is accepted, and one byte less reports
+    WORKSPACE; nothing is launched either way."""
+    s = P(0)
+    b = L.tern_linear_bwd
+    X, dY, pk, sc = P(0x1000000), P(0x2000000), P(0x3000000), P(0x4000000)
+    gq, sg, ws, dX_bad = P(0x6000000), P(0x7000000), P(0x10000000), P(0x5000004)
+    for (T, i, o) in [(4000, 1032, 1032), (16384, 2048, 2048), (2048, 512, 2048), (64, 64, 64)]:
+        need = tl.tern_linear_bwd_workspace_bytes(T, i, o)
+        assert need > 0
         for dt in (F32, BF16):
-            w = tl.tern_linear_bwd_workspace_bytes(T, i, o, dt)
-            # always room for at least one row of sgrad partials, 256-byte granular
-            assert w >= 4 * o and w % 256 == 0, (T, i, o, dt, w)
-            assert tl.tern_linear_bwd_workspace_bytes(T, i, o, dt) == w  # pure function
+            assert b(X, dY, dt, pk, sc, T, i, o, dX_bad, F32, gq, sg, ws, need, s) == ALIGN, (T, i, o, dt)
+        # at least one type needs every byte of it
+        assert any(b(X, dY, dt, pk, sc, T, i, o, dX_bad, F32, gq, sg, ws, need - 1, s) == WORKSPACE
+                   for dt in (F32, BF16)), (T, i, o)
 
 
 def test_graph_calls_reject_missing_handles(L):
@@ -186,8 +208,8 @@ def test_acc_variants_reject(L):
     assert dx(dY, BF16, pk, sc, T, n_in, n_out, P(0x5000004), s) == ALIGN
     assert dx(dY, BF16, pk, sc, T, n_in, n_out, P(0x2000000 + 4096), s) == ALIAS   # dX over dY
     dw = L.tern_linear_bwd_dw_acc
-    need = tl.tern_linear_bwd_acc_workspace_bytes(T, n_in, n_out, BF16)
-    plain = tl.tern_linear_bwd_workspace_bytes(T, n_in, n_out, BF16)
+    need = tl.tern_linear_bwd_acc_workspace_bytes(T, n_in, n_out)
+    plain = tl.tern_linear_bwd_workspace_bytes(T, n_in, n_out)
     assert need >= plain and need >= 4 * n_in * n_out   # room for G itself
     ws, gq2 = P(0x10000000), P(0x30000000)
     a = ctypes.c_float(0.5)
@@ -200,12 +222,10 @@ def test_acc_variants_reject(L):
 
 
 def test_acc_workspace_bytes(L):
-    assert tl.tern_linear_bwd_acc_workspace_bytes(8, 12, 8, BF16) == 0
-    assert tl.tern_linear_bwd_acc_workspace_bytes(8, 8, 8, 9) == 0
+    assert tl.tern_linear_bwd_acc_workspace_bytes(8, 12, 8) == 0
     for (T, i, o) in [(64, 64, 64), (2048, 512, 2048), (16384, 8192, 2048), (1000, 200, 72)]:
-        for dt in (F32, BF16):
-            w = tl.tern_linear_bwd_acc_workspace_bytes(T, i, o, dt)
-            assert w >= tl.tern_linear_bwd_workspace_bytes(T, i, o, dt) and w >= 4 * i * o and w % 256 == 0
+        w = tl.tern_linear_bwd_acc_workspace_bytes(T, i, o)
+        assert w >= tl.tern_linear_bwd_workspace_bytes(T, i, o) and w >= 4 * i * o and w % 256 == 0
 
 
 def test_panel_rejects(L):

@@ -40,7 +40,7 @@ def _like(ref: np.ndarray, seed: int) -> torch.Tensor:
 
 
 def _acc_dw(d, gq, sg, alpha):
-    ws = tl.empty_workspace(d.T, d.n_in, d.n_out, d.X.dtype, acc=True)
+    ws = tl.empty_workspace(d.T, d.n_in, d.n_out, acc=True)
     tl.tern_linear_bwd_dw_acc(d.X, d.dY, d.packed, d.scale, gq, sg, ws, alpha)
 
 
@@ -150,7 +150,7 @@ def test_acc_empty_sums_leave_outputs():
     tl.tern_materialize(q, 2, pk2)
     gq = torch.full((64, 32), 5.0, device=dev)
     sg = torch.full((32,), 7.0, device=dev)
-    ws = tl.empty_workspace(0, 64, 32, torch.bfloat16, acc=True)
+    ws = tl.empty_workspace(0, 64, 32, acc=True)
     tl.tern_linear_bwd_dw_acc(X, dY2, pk2, sc, gq, sg, ws, 0.5)
     torch.cuda.synchronize()
     assert bool((dX == 3.0).all()) and bool((gq == 5.0).all()) and bool((sg == 7.0).all())

@@ -58,7 +58,7 @@ def _run_group(X, ps, theta):
     dX = torch.empty((T, n_in), device="cuda")
     gq = torch.empty((n_in, tot), device="cuda")
     sgr = torch.empty((tot,), device="cuda")
-    ws = tl.empty_workspace(T, n_in, tot, Xd.dtype)
+    ws = tl.empty_workspace(T, n_in, tot)
     tl.tern_linear_fwd(Xd, pk, sg, Y)
     tl.tern_linear_bwd(Xd, dYg, pk, sg, dX, gq, sgr, ws)
     torch.cuda.synchronize()

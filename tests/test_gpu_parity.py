@@ -399,7 +399,7 @@ def test_zero_sizes():
     dX = torch.empty((0, 64), device=dev)
     gq = torch.full((64, 32), 7.0, device=dev)
     sg = torch.full((32,), 7.0, device=dev)
-    ws = tl.empty_workspace(0, 64, 32, torch.bfloat16)
+    ws = tl.empty_workspace(0, 64, 32)
     tl.tern_linear_bwd(X, dY, pk, sc, dX, gq, sg, ws)
     torch.cuda.synchronize()
     assert torch.all(gq == 0) and torch.all(sg == 0)
@@ -412,7 +412,7 @@ def test_zero_sizes():
     dX = torch.empty((16, 0), device=dev)
     gq = torch.empty((0, 32), device=dev)
     sg = torch.full((32,), 7.0, device=dev)
-    tl.tern_linear_bwd(X, dY, pk, sc, dX, gq, sg, tl.empty_workspace(16, 0, 32, torch.bfloat16))
+    tl.tern_linear_bwd(X, dY, pk, sc, dX, gq, sg, tl.empty_workspace(16, 0, 32))
     torch.cuda.synchronize()
     assert torch.all(Y == 0) and torch.all(sg == 0)
     # out = 0: dX = 0 (empty sum over c)
@@ -425,7 +425,7 @@ def test_zero_sizes():
     sg = torch.empty((0,), device=dev)
     Y = torch.empty((16, 0), device=dev)
     tl.tern_linear_fwd(X, pk, sc0, Y)
-    tl.tern_linear_bwd(X, dY, pk, sc0, dX, gq, sg, tl.empty_workspace(16, 24, 0, torch.bfloat16))
+    tl.tern_linear_bwd(X, dY, pk, sc0, dX, gq, sg, tl.empty_workspace(16, 24, 0))
     torch.cuda.synchronize()
     assert torch.all(dX == 0)
 
