@@ -58,6 +58,7 @@ extern "C" {
 #define TERN_ERR_ALIAS     -7  /* an output overlaps an input or another output */
 #define TERN_ERR_HIP       -8  /* the HIP runtime refused a launch */
 #define TERN_ERR_VALUE     -9  /* a scalar argument outside its range (optimizer step, learning rate) */
+#define TERN_ERR_SCRATCH  -10  /* the sizes need more than the library's static scratch */
 
 /* Number of uint32 words of a packed ternary handle for an [in, out] matrix
  * (0 if in or out is 0, -1 for negative sizes).  The caller allocates this
@@ -160,6 +161,30 @@ int tern_linear_bwd_dw(const void *X, const void *dY, int32_t act_dtype,
                        int64_t T, int64_t in, int64_t out,
                        float *gq, float *sgrad, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * tern_linear_bwd_noalloc -- tern_linear_bwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, results
+ * and errors as tern_linear_bwd, minus the workspace.  The backward's scratch
+ * (sgrad partial table, split partial products of G) lives in a static device
+ * array of 64 MiB that the library holds on each GPU it runs on until the
+ * process ends; where the usual plan needs more, the weight-gradient product
+ * is split over fewer token ranges (the results then differ from
+ * tern_linear_bwd's by fp32 rounding only).  The call allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine.  Its first call on a
+ * device looks up that device's array (make it outside a graph capture).
+ * Calls on one GPU share the array, so calls that overlap in time on one GPU
+ * (on different streams, or from different threads) race; calls in one
+ * stream's order do not.  No part of the array needs to start at zero.
+ * Errors: as tern_linear_bwd, plus SCRATCH when even the smallest plan needs
+ *   more than 64 MiB (in / 256 * out * 4 bytes of sgrad partials, that is
+ *   in * out above 4 Gi elements), HIP.
+ */
+int tern_linear_bwd_noalloc(const void *X, const void *dY, int32_t act_dtype,
+                            const uint32_t *tern_packed, const float *scale,
+                            int64_t T, int64_t in, int64_t out,
+                            void *dX, int32_t dx_dtype, float *gq, float *sgrad, void *stream);
 
 /*
  * Accumulating variants of the backward.  dX += adds one projection's input

@@ -25,7 +25,7 @@ TERN_BF16 = 1
 STATUS = {
     0: "TERN_OK", -1: "TERN_ERR_NULL", -2: "TERN_ERR_SHAPE", -3: "TERN_ERR_THETA",
     -4: "TERN_ERR_DTYPE", -5: "TERN_ERR_ALIGN", -6: "TERN_ERR_WORKSPACE", -7: "TERN_ERR_ALIAS",
-    -8: "TERN_ERR_HIP", -9: "TERN_ERR_VALUE",
+    -8: "TERN_ERR_HIP", -9: "TERN_ERR_VALUE", -10: "TERN_ERR_SCRATCH",
 }
 
 # Every symbol include/tern.h declares: name -> (restype, argtypes)
@@ -37,6 +37,8 @@ SIGNATURES = {
     "tern_linear_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "tern_linear_bwd": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp,
                                        _vp, _vp, _sz, _vp]),
+    "tern_linear_bwd_noalloc": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp,
+                                               _vp, _vp]),
     "tern_linear_bwd_dx": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _i32, _vp]),
     "tern_linear_bwd_dw": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
                                           _vp, _sz, _vp]),
@@ -231,6 +233,19 @@ def tern_linear_bwd(X, dY, tern_packed, scale, dX, gq, sgrad, workspace, stream=
                                n_in, n_out, _ptr(dX), _act_code(dX), _ptr(gq), _ptr(sgrad),
                                _ptr(workspace), ws_bytes, _stream(stream))
     _check("tern_linear_bwd", rc)
+
+
+def tern_linear_bwd_noalloc(X, dY, tern_packed, scale, dX, gq, sgrad, stream=None) -> None:
+    """tern_linear_bwd without a workspace: the library's static scratch is
+    used (calls that overlap on one GPU race)."""
+    fn = "tern_linear_bwd_noalloc"
+    T, n_in, n_out = _bwd_dw_checks(fn, X, dY, tern_packed, scale, gq, sgrad, None)
+    _need(fn, "dX", dX, (T, n_in), _F32)
+    _need_device(fn, X, dY, tern_packed, scale, dX, gq, sgrad)
+    rc = lib().tern_linear_bwd_noalloc(_ptr(X), _ptr(dY), _act_code(X), _ptr(tern_packed), _ptr(scale), T,
+                                       n_in, n_out, _ptr(dX), _act_code(dX), _ptr(gq), _ptr(sgrad),
+                                       _stream(stream))
+    _check(fn, rc)
 
 
 def _bwd_dx_checks(fn, dY, tern_packed, scale, dX, n_in):

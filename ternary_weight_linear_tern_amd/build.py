@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtern.so")
-SOURCES = ["tern_kernels.hip", "tern_panel.hip", "tern_group.hip", "tern_optim.hip", "tern_api.cpp",
+SOURCES = ["tern_kernels.hip", "tern_panel.hip", "tern_group.hip", "tern_optim.hip", "tern_noalloc.hip", "tern_api.cpp",
            "tern_plan.cpp"]
 ARCH = "gfx950"
 

@@ -58,6 +58,7 @@ const char *tern_status_str(int status) {
         case TERN_ERR_ALIAS: return "output overlaps an input or another output";
         case TERN_ERR_HIP: return "HIP launch failed";
         case TERN_ERR_VALUE: return "scalar argument out of range (optimizer step or learning rate)";
+        case TERN_ERR_SCRATCH: return "sizes need more than the library's static scratch (64 MiB)";
         default: return "unknown status";
     }
 }

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         s = tl.tern_status_str(code)
         assert s and s != "unknown status"
     assert tl.tern_status_str(-99) == "unknown status"
@@ -278,3 +278,24 @@ def test_scale_adamw_rejects(L):
     assert f(sg, P(0x2000002), m, v, 64, 1, *hp, s) == ALIGN
     assert f(sg, sc, P(0x2000000 + 128), v, 64, 1, *hp, s) == ALIAS   # m overlaps scale
     assert f(sg, sc, m, v, 0, 1, *hp, s) == OK                       # nothing to update
+
+
+def test_noalloc_rejects_before_any_hip_call(L):
+    """The allocation-free backward applies tern_linear_bwd's checks before it
+    looks up its scratch (no GPU here: any HIP call would fail with HIP)."""
+    s = P(0)
+    f = L.tern_linear_bwd_noalloc
+    X, dY, pk, sc = P(0x1000000), P(0x2000000), P(0x3000000), P(0x4000000)
+    dX, gq, sg = P(0x5000000), P(0x6000000), P(0x7000000)
+    T, n_in, n_out = 4096, 1024, 1024
+    assert f(X, dY, BF16, pk, sc, T, n_in, n_out, dX, BF16, gq, sg, s) == DTYPE
+    assert f(X, dY, 3, pk, sc, T, n_in, n_out, dX, F32, gq, sg, s) == DTYPE
+    assert f(X, dY, BF16, pk, sc, T, 100, n_out, dX, F32, gq, sg, s) == SHAPE
+    assert f(None, dY, BF16, pk, sc, T, n_in, n_out, dX, F32, gq, sg, s) == NULL
+    assert f(X, dY, BF16, pk, sc, T, n_in, n_out, dX, F32, None, sg, s) == NULL
+    assert f(X, dY, BF16, pk, sc, T, n_in, n_out, P(0x5000004), F32, gq, sg, s) == ALIGN
+    assert f(X, dY, BF16, pk, sc, T, n_in, n_out, P(0x2000000 + 4096), F32, P(0x20000000), sg, s) == ALIAS
+    # the largest in * out with an sgrad partial table above 64 MiB
+    big = [P(k << 40) for k in range(1, 8)]   # far apart: no overlap at these sizes
+    assert f(big[0], big[1], BF16, big[2], big[3], 64, 1 << 20, 1 << 14, big[4], F32, big[5], big[6], s) == -10
+
