@@ -17,6 +17,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -53,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="oracle sample: token rows per projection")
     ap.add_argument("--cpu-cols", type=int, default=768, help="oracle sample: output columns per projection")
+    ap.add_argument("--cpu-1t-div", type=int, default=16,
+                    help="the 1-thread oracle runs on 1/N of the all-thread sample's rows and columns")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy a 1 GiB buffer 3 times (known bytes, for scaling "
                          "HBM traffic counters)")
@@ -322,6 +325,8 @@ def main():
             fork(sx, s0)
 
     eager_ms_per_step = ms_per_step
+    # per-step times of the eager region (first event of a step to its last)
+    step_ms = [evs[k][0][0].elapsed_time(evs[k][-1][4]) for k in range(a.steps)]
     if a.streams == "auto":
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         tiles = lambda m, n: -(-m // 256) * -(-n // 256)
@@ -347,21 +352,29 @@ def main():
                 tl.tern_graph_launch(graph, gs)
             torch.cuda.synchronize()
             g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(a.steps)]
             g0.record(gs)
-            for _ in range(a.steps):
+            for k in range(a.steps):
+                rev[k][0].record(gs)
                 tl.tern_graph_launch(graph, gs)
+                rev[k][1].record(gs)
             g1.record(gs)
             torch.cuda.synchronize()
             ms_per_step = g0.elapsed_time(g1) / a.steps
+            step_ms = [e0.elapsed_time(e1) for e0, e1 in rev]
         finally:
             tl.tern_graph_destroy(graph)
 
-    part_ms = {p: 0.0 for p in PARTS}
+    # per step, summed over projections: the mean over the timed steps, and
+    # each part's median over the steps
+    per_step = {p: [0.0] * a.steps for p in PARTS}
     for k in range(a.steps):
         for j in range(len(projs)):
             for pi, pname in enumerate(PARTS):
-                part_ms[pname] += evs[k][j][pi].elapsed_time(evs[k][j][pi + 1])
-    part_ms = {k: v / a.steps for k, v in part_ms.items()}  # per step, summed over projections
+                per_step[pname][k] += evs[k][j][pi].elapsed_time(evs[k][j][pi + 1])
+    part_ms = {p: sum(v) / a.steps for p, v in per_step.items()}
+    part_med = {p: statistics.median(v) for p, v in per_step.items()}
 
     flops_step = w.flops
     gemm_flops = {p: 2.0 * w.T * w.sum_in_out for p in ("fwd", "bwd_dx", "bwd_dw")}
@@ -385,9 +398,15 @@ def main():
                 traffic = ent["bytes_per_step"]
         except Exception:  # noqa: BLE001 - a stale or malformed file means no counter data
             traffic = None
+    es = 2 if dt == "bf16" else 4
+    alg_bytes = {p: sum(algorithmic_bytes(p, w.T, i, o, es) for _, i, o in w.projs) for p in PARTS}
+    alg_gbs = alg_bytes[dom] / (part_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom_kernels,
-                "flops_per_step": gemm_flops[dom], "ms_per_step": round(part_ms[dom], 4)}
+                "flops_per_step": gemm_flops[dom], "ms_per_step": round(part_ms[dom], 4),
+                "ms_per_step_median": round(part_med[dom], 4),
+                "alg_bytes_per_step": alg_bytes[dom], "alg_hbm_gbs": round(alg_gbs, 1),
+                "alg_hbm_frac": round(alg_gbs / PEAK_HBM_GBS, 4)}
     if traffic is not None:
         # the same kernel against the HBM roof: its counted bytes over its time
         gbs = traffic / (part_ms[dom] * 1e-3) / 1e9
@@ -406,7 +425,7 @@ def main():
 
     cpu = None
     if not a.no_cpu_baseline:
-        cpu = cpu_baseline(w, projs, a.cpu_rows, a.cpu_cols)
+        cpu = cpu_baseline(w, projs, a.cpu_rows, a.cpu_cols, a.cpu_1t_div)
 
     line = {
         "metric": "ternary-linear fwd+bwd TFLOP/s and tokens/s at d=2048; % of MFMA peak",
@@ -431,13 +450,44 @@ def main():
         "mfma_frac": round(tflops / peak, 4),
         "flops_per_step": flops_step,
         "part_ms_per_step": {k: round(v, 4) for k, v in part_ms.items()},
+        "part_ms_median": {k: round(v, 4) for k, v in part_med.items()},
+        "step_stats": step_stats(step_ms, flops_step, w.T, peak),
+        "part_alg_hbm_gbs": {p: round(alg_bytes[p] / (part_ms[p] * 1e-3) / 1e9, 1) for p in PARTS},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, projs, n_rows, n_cols):
+def algorithmic_bytes(part: str, T: int, n_in: int, n_out: int, es: int) -> float:
+    """HBM bytes one entry point must move for one projection: its inputs read
+    once, its outputs written once (activations es bytes, tern 1/4 byte per
+    weight, scale, Y / dX / gq / sgrad fp32; q one byte per weight)."""
+    w = n_in * n_out
+    if part == "materialize":
+        return 1.0 * w + 0.25 * w
+    if part == "fwd":
+        return es * T * n_in + 0.25 * w + 4 * n_out + 4 * T * n_out
+    if part == "bwd_dx":
+        return es * T * n_out + 0.25 * w + 4 * n_out + 4 * T * n_in
+    return es * T * (n_in + n_out) + 0.25 * w + 4 * n_out + 4 * w + 4 * n_out   # bwd_dw
+
+
+def step_stats(step_ms, flops, T, peak):
+    """Median, min, max and spread of the per-step times, with the rates at the
+    median."""
+    s = sorted(step_ms)
+    med = statistics.median(s)
+    q = lambda f: s[min(len(s) - 1, max(0, int(round(f * (len(s) - 1)))))]
+    return {"n": len(s), "median_ms": round(med, 4), "min_ms": round(s[0], 4), "max_ms": round(s[-1], 4),
+            "p10_ms": round(q(0.1), 4), "p90_ms": round(q(0.9), 4),
+            "spread_pct": round(100.0 * (q(0.9) - q(0.1)) / med, 2),
+            "tflops_at_median": round(flops / (med * 1e-3) / 1e12, 3),
+            "mfma_frac_at_median": round(flops / (med * 1e-3) / 1e12 / peak, 4),
+            "tokens_per_s_at_median": round(T / (med * 1e-3), 1)}
+
+
+def cpu_baseline(w, projs, n_rows, n_cols, div_1t=16):
     """The oracle, as it stands, on a bounded sample of the same workload:
     n_rows token rows of Y and dX and n_cols output columns of gq / sgrad per
     projection.  Reported as the oracle's throughput (TFLOP/s) and the tokens/s
@@ -459,11 +509,34 @@ def cpu_baseline(w, projs, n_rows, n_cols):
     sec = time.perf_counter() - t0
     rate = flops / sec
     full_s = w.flops / rate
-    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": o.num_threads(), "kind": "oracle",
+    cores = o.num_threads()
+    # the same oracle on one thread, on 1/div_1t of the sample
+    r1, c1 = max(1, n_rows // div_1t), max(1, n_cols // div_1t)
+    o.set_num_threads(1)
+    try:
+        flops1 = 0.0
+        t1 = time.perf_counter()
+        for i, d in enumerate(projs):
+            p = d["host"]
+            rows = synth.sample_indices(synth.stream_seed(92, w.config_id, i, 0), r1, w.T)
+            cols = synth.sample_indices(synth.stream_seed(92, w.config_id, i, 1), c1, d["n_out"])
+            o.linear_fwd(p.X, p.q, p.theta, p.scale, rows=rows)
+            o.linear_dx(p.dY, p.q, p.theta, p.scale, rows=rows)
+            o.linear_wgrad(p.X, p.dY, p.q, p.theta, p.scale, cols=cols)
+            flops1 += 2.0 * 2 * rows.size * d["n_in"] * d["n_out"] + 2.0 * w.T * d["n_in"] * cols.size
+        sec1 = time.perf_counter() - t1
+    finally:
+        o.set_num_threads(cores)
+    rate1 = flops1 / sec1
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{n_rows} token rows of Y and dX and {n_cols} output columns of gq/sgrad per "
                       f"projection, all {len(projs)} projections of {w.name}; {sec:.1f}s",
             "seconds": round(sec, 2), "extrapolated_step_s": round(full_s, 1),
-            "tokens_per_s": round(w.T / full_s, 3)}
+            "tokens_per_s": round(w.T / full_s, 3),
+            "value_1thread": round(rate1 / 1e12, 6),
+            "sample_1thread": f"{r1} token rows and {c1} columns per projection; {sec1:.1f}s",
+            "extrapolated_step_s_1thread": round(w.flops / rate1, 1),
+            "thread_speedup": round(rate / rate1, 2)}
 
 
 if __name__ == "__main__":

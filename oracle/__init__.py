@@ -73,6 +73,8 @@ class Oracle:
         L.oracle_scale_adamw.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = ctypes.c_int
         self.L = L
 
     # -- helpers --------------------------------------------------------
@@ -92,6 +94,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.L.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> int:
+        """Use n threads from now on; returns the count in effect."""
+        return int(self.L.oracle_set_num_threads(int(n)))
 
     # -- ternarisation and packing -----------------------------------------
     def tern(self, q: np.ndarray, theta: int) -> np.ndarray:

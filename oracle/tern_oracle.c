@@ -39,6 +39,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+int oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 /* ---- input widening: exact fp32 / bf16 -> double ---- */
 
 static double widen_one(const void *src, int32_t dtype, int64_t i) {
@@ -257,31 +267,44 @@ int oracle_linear_wgrad(const void *X, const void *dY, int32_t dtype, const int8
     return 0;
 }
 
-/* ---- SR4 health panel (page "train_gpu.cu", sr4_panel_compute) ---- */
-
+/* ---- SR4 health panel (page "train_gpu.cu", the sr4_panel fields) ----
+ * Every field but churn depends on an element only through its value of q,
+ * so the matrix is first reduced to a histogram over the 256 int8 values and
+ * the fields are sums of bins: the class of a value by the threshold rule,
+ * the rail (|v| equal to the clamp) and the dead zone (|v| below theta).
+ * Churn needs the element's position: a second pass compares each element's
+ * class with the previous classification.  The scale statistics run over the
+ * columns in ascending order. */
 int oracle_panel_add(const int8_t *q, int64_t in, int64_t out, int32_t theta, int32_t q_clamp,
                      const int8_t *prev_tern, const float *scale, int64_t counts[7],
                      double sstat[4]) {
     if (theta < 1) return -1;
     const int64_t n = in * out;
-    for (int64_t k = 0; k < n; k++) {
-        const int v = q[k];
-        const int t = v >= theta ? 1 : (v <= -theta ? -1 : 0);
-        const int a = v < 0 ? -v : v;
-        counts[0] += 1;
-        if (t < 0) counts[1] += 1;
-        else if (t > 0) counts[3] += 1;
-        else counts[2] += 1;
-        if (a == q_clamp) counts[4] += 1;
-        if (a < theta) counts[5] += 1;
-        if (prev_tern && prev_tern[k] != t) counts[6] += 1;
+    int64_t bins[256];
+    memset(bins, 0, sizeof bins);
+    for (int64_t k = 0; k < n; k++) bins[(int)q[k] + 128]++;
+    for (int v = -128; v <= 127; v++) {
+        const int64_t h = bins[v + 128];
+        const int mag = abs(v);
+        counts[0] += h;                          /* total */
+        if (v <= -theta) counts[1] += h;         /* class -1 */
+        if (-theta < v && v < theta) counts[2] += h;   /* class 0 */
+        if (v >= theta) counts[3] += h;          /* class +1 */
+        if (mag == q_clamp) counts[4] += h;      /* on the rail */
+        if (mag < theta) counts[5] += h;         /* in the dead zone */
+    }
+    if (prev_tern) {
+        for (int64_t k = 0; k < n; k++) {
+            const int8_t now = q[k] >= theta ? 1 : (q[k] <= -theta ? -1 : 0);
+            counts[6] += prev_tern[k] != now;
+        }
     }
     for (int64_t c = 0; c < out; c++) {
-        const double s = (double)scale[c];
+        const double sv = (double)scale[c];
         sstat[0] += 1.0;
-        sstat[1] += s;
-        if (s < sstat[2]) sstat[2] = s;
-        if (s > sstat[3]) sstat[3] = s;
+        sstat[1] += sv;
+        sstat[2] = sv < sstat[2] ? sv : sstat[2];
+        sstat[3] = sv > sstat[3] ? sv : sstat[3];
     }
     return 0;
 }

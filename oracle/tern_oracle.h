@@ -118,6 +118,10 @@ int oracle_scale_adamw(const double *sgrad, double *scale, double *m, double *v,
 /* Threads the OpenMP build uses (1 without OpenMP). */
 int oracle_num_threads(void);
 
+/* Use n >= 1 threads from now on (results do not depend on it: every output
+ * element keeps its own summation order); returns the new count. */
+int oracle_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -131,6 +131,7 @@ int main(void) {
     for (int i = 0; i < 5; i++) CHECK(idx[i] >= 0 && idx[i] < 11);
     for (int i = 0; i < 37; i++) CHECK(z[i] == 0 || (abs(z[i]) >= 1 && abs(z[i]) <= 7));
     (void)synth_u64(9, 3);
+    CHECK(oracle_set_num_threads(1) == 1 && oracle_num_threads() == 1);
 
     /* all int8 values through the threshold rule */
     int8_t all[256], t[256];

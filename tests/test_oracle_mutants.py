@@ -45,13 +45,13 @@ MUTANTS = [
     ("adamw_coupled_decay", "const double g = sgrad[c] * scale_lr / lr;",
      "const double g = sgrad[c] * scale_lr / lr + wd * scale[c];"),
     ("adamw_dropped_lr_ratio", "const double g = sgrad[c] * scale_lr / lr;", "const double g = sgrad[c];"),
-    ("panel_dead_inclusive", "if (a < theta) counts[5] += 1;", "if (a <= theta) counts[5] += 1;"),
-    ("panel_rail_uses_theta", "if (a == q_clamp) counts[4] += 1;", "if (a == theta) counts[4] += 1;"),
-    ("panel_churn_ignores_sign", "if (prev_tern && prev_tern[k] != t) counts[6] += 1;",
-     "if (prev_tern && (prev_tern[k] != 0) != (t != 0)) counts[6] += 1;"),
-    ("panel_zero_counted_as_pos", "else if (t > 0) counts[3] += 1;", "else if (t >= 0) counts[3] += 1;"),
-    ("panel_scale_min_skips_first", "for (int64_t c = 0; c < out; c++) {\n        const double s",
-     "for (int64_t c = 1; c < out; c++) {\n        const double s"),
+    ("panel_dead_inclusive", "if (mag < theta) counts[5] += h;", "if (mag <= theta) counts[5] += h;"),
+    ("panel_rail_uses_theta", "if (mag == q_clamp) counts[4] += h;", "if (mag == theta) counts[4] += h;"),
+    ("panel_churn_ignores_sign", "counts[6] += prev_tern[k] != now;", "counts[6] += (prev_tern[k] != 0) != (now != 0);"),
+    ("panel_zero_counted_as_pos", "if (v >= theta) counts[3] += h;", "if (v >= 0) counts[3] += h;"),
+    ("panel_scale_min_skips_first", "for (int64_t c = 0; c < out; c++) {\n        const double sv",
+     "for (int64_t c = 1; c < out; c++) {\n        const double sv"),
+    ("panel_histogram_off_by_one", "bins[(int)q[k] + 128]++;", "bins[(int)q[k] + 127 + (q[k] == -128)]++;"),
 ]
 
 
