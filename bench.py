@@ -7,10 +7,12 @@ HBM.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large] [--launch eager|graph]
 
-By default one step's library calls are recorded as a HIP graph (tern_graph_*)
-whose dW launches form a branch of their own (--streams), and its replays are
-timed (--launch eager times the calls themselves); the per-part times always
-come from eager calls, timed with events between them.
+By default a step is the layer calls (tern_layer_*: one call per product for
+all projections; --api projection uses the single-projection calls), recorded
+once as a HIP graph (tern_graph_*) with the dW call (and, for small products,
+the dX call) on branches of their own (--streams), and its replays are timed
+(--launch eager times the calls themselves); the per-part times always come
+from eager calls, timed with events between them.
 """
 from __future__ import annotations
 
@@ -45,12 +47,15 @@ def parse():
     ap.add_argument("--launch", default="graph", choices=["eager", "graph"],
                     help="graph (default): time replays of one recorded step; eager: time the calls")
     ap.add_argument("--streams", default="auto", choices=["auto", "1", "2", "3", "p3"],
-                    help="graph branches of the recorded step: 1 = one chain; 2 = dW of every projection on "
-                         "its own branch; 3 = dX and dW each on their own branch (each branch waits only for "
-                         "its projection's materialize); p3 = whole projections (materialize, forward, dX, "
-                         "dW) dealt over three branches; auto = p3 when some projection's forward or dX has "
-                         "fewer 256 x 256 tiles than the GPU has compute units (small products, whose "
-                         "latencies then overlap), else 2")
+                    help="graph branches of the recorded step: 1 = one chain; 2 = dW on its own branch; 3 = dX "
+                         "and dW each on their own branch (after the materialize); p3 (single-projection "
+                         "calls only) = whole projections dealt over three branches; auto = 3 (layer calls) or "
+                         "p3 (single calls) when some projection's forward or dX has fewer 256 x 256 tiles "
+                         "than the GPU has compute units (small products, whose latencies then overlap), "
+                         "else 2")
+    ap.add_argument("--api", default="layer", choices=["layer", "projection"],
+                    help="layer (default): one call per product for all projections (tern_layer_*); "
+                         "projection: the single-projection calls, one per projection and product")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="oracle sample: token rows per projection")
     ap.add_argument("--cpu-cols", type=int, default=768, help="oracle sample: output columns per projection")
@@ -244,8 +249,31 @@ def main():
           f"projections {[(d['name'], d['n_in'], d['n_out']) for d in projs]}", file=sys.stderr, flush=True)
 
     PARTS = ("materialize", "fwd", "bwd_dx", "bwd_dw")
+    layer = a.api == "layer"
+    layer_ws = tl.empty_layer_workspace([(d["n_in"], d["n_out"]) for d in projs], w.T) if layer else None
+    theta = projs[0]["theta"]
+
+    def step_layer(evs=None, stream=stream):
+        # one call per product for all projections; the events of a step sit
+        # in slot 0 (the parts of the whole layer)
+        if evs is not None:
+            evs[0][0].record(stream)
+        tl.tern_layer_materialize(projs, theta, stream)
+        if evs is not None:
+            evs[0][1].record(stream)
+        tl.tern_layer_fwd(projs, stream)
+        if evs is not None:
+            evs[0][2].record(stream)
+        tl.tern_layer_bwd_dx(projs, stream)
+        if evs is not None:
+            evs[0][3].record(stream)
+        tl.tern_layer_bwd_dw(projs, layer_ws, stream)
+        if evs is not None:
+            evs[0][4].record(stream)
 
     def step(evs=None, stream=stream):
+        if layer:
+            return step_layer(evs, stream)
         for j, d in enumerate(projs):
             if evs is not None:
                 evs[j][0].record(stream)
@@ -303,6 +331,28 @@ def main():
         for sx in streams[1:]:
             fork(sx, s0)
 
+    def record_layer(streams):
+        """The layer step as a DAG: materialize, then the forward, dX and dW
+        calls, each on its own branch when there are three streams."""
+        s0 = streams[0]
+        # 2 streams: forward and dX on the first, dW on the second; 3: one each
+        sdx = streams[1] if len(streams) == 3 else s0
+        sdw = streams[-1]
+
+        def fork(src, dst):
+            e = torch.cuda.Event()
+            e.record(src)
+            dst.wait_event(e)
+
+        tl.tern_layer_materialize(projs, theta, s0)
+        for sx in streams[1:]:
+            fork(s0, sx)
+        tl.tern_layer_fwd(projs, s0)
+        tl.tern_layer_bwd_dx(projs, sdx)
+        tl.tern_layer_bwd_dw(projs, layer_ws, sdw)
+        for sx in streams[1:]:
+            fork(sx, s0)
+
     def record_projections(streams):
         """The step as independent chains: projection j's materialize, forward,
         dX and dW in order on branch j % len(streams)."""
@@ -326,14 +376,17 @@ def main():
 
     eager_ms_per_step = ms_per_step
     # per-step times of the eager region (first event of a step to its last)
-    step_ms = [evs[k][0][0].elapsed_time(evs[k][-1][4]) for k in range(a.steps)]
+    last = 0 if layer else -1
+    step_ms = [evs[k][0][0].elapsed_time(evs[k][last][4]) for k in range(a.steps)]
     if a.streams == "auto":
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         tiles = lambda m, n: -(-m // 256) * -(-n // 256)
         small = any(min(tiles(d["n_out"], w.T), tiles(d["n_in"], w.T)) < cus for d in projs)
-        mode = "p3" if small else "2"
+        mode = ("3" if small else "2") if layer else ("p3" if small else "2")
     else:
         mode = a.streams
+        if layer and mode.startswith("p"):
+            mode = mode[1:]
     by_projection = mode.startswith("p")
     n_streams = int(mode[1:] if by_projection else mode)
     if a.launch == "graph":
@@ -344,7 +397,10 @@ def main():
         branches = [torch.cuda.Stream() for _ in range(n_streams - 1)]
         tl.tern_graph_begin(gs)
         try:
-            (record_projections if by_projection else record_dag)([gs] + branches)
+            if layer:
+                record_layer([gs] + branches)
+            else:
+                (record_projections if by_projection else record_dag)([gs] + branches)
         finally:
             graph = tl.tern_graph_end(gs)
         try:
@@ -370,7 +426,7 @@ def main():
     # each part's median over the steps
     per_step = {p: [0.0] * a.steps for p in PARTS}
     for k in range(a.steps):
-        for j in range(len(projs)):
+        for j in range(1 if layer else len(projs)):
             for pi, pname in enumerate(PARTS):
                 per_step[pname][k] += evs[k][j][pi].elapsed_time(evs[k][j][pi + 1])
     part_ms = {p: sum(v) / a.steps for p, v in per_step.items()}
@@ -385,9 +441,12 @@ def main():
 
     # dominant kernel: the GEMM entry point with the largest share of the step
     dom = max(("fwd", "bwd_dx", "bwd_dw"), key=lambda p: part_ms[p])
-    dom_kernels = {"fwd": "gemm_rd_kernel<MODE_FWD> (tern_linear_fwd)",
-                   "bwd_dx": "gemm_rd_kernel<MODE_DX> (tern_linear_bwd_dx)",
-                   "bwd_dw": "gemm_dw_kernel + dw_reduce + sgrad_reduce (tern_linear_bwd_dw)"}[dom]
+    dom_kernels = {"fwd": "gemm_rd_kernel<MODE_FWD> (tern_layer_fwd)" if layer else
+                   "gemm_rd_kernel<MODE_FWD> (tern_linear_fwd)",
+                   "bwd_dx": "gemm_rd_kernel<MODE_DX> (tern_layer_bwd_dx)" if layer else
+                   "gemm_rd_kernel<MODE_DX> (tern_linear_bwd_dx)",
+                   "bwd_dw": "gemm_dw_kernel + dw_reduce + sgrad_reduce (tern_layer_bwd_dw)" if layer else
+                   "gemm_dw_kernel + dw_reduce + sgrad_reduce (tern_linear_bwd_dw)"}[dom]
     achieved = gemm_flops[dom] / (part_ms[dom] * 1e-3) / 1e12
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -444,7 +503,9 @@ def main():
                    "projections": [[n, i, o] for n, i, o in w.projs],
                    "theta": w.theta, "q": w.q_law, "scale": w.scale_law, "act": w.act,
                    "launch": (f"hipgraph, {n_streams} branch(es)" + (" by projection" if by_projection else ""))
-                   if a.launch == "graph" else "eager"},
+                   if a.launch == "graph" else "eager",
+                   "api": "tern_layer_* (one call per product for all projections)" if layer
+                   else "single-projection calls"},
         "eager_ms_per_step": round(eager_ms_per_step, 4),
         "tokens_per_s": round(tokens_per_s, 1),
         "mfma_frac": round(tflops / peak, 4),

@@ -326,6 +326,76 @@ typedef struct tern_panel_fractions {
 int tern_panel_fractions(const tern_panel_t *panel, tern_panel_fractions_t *out);
 
 /*
+ * The projections of one layer, one launch per product.  The page's trainer
+ * launches every projection's kernels in turn (its own note: launch-bound).
+ * Here the tiles of all projections of one product (and, for the weight
+ * gradient, their splits over tokens) form one work list that a persistent
+ * grid walks: small projections fill the chip together, and a layer step is
+ * four launches (materialize, forward, dX, dW) plus the dW finish.  Each call
+ * computes exactly what the single-projection call computes for every
+ * projection (forward and dX bitwise alike; gq and sgrad to fp32 rounding,
+ * since the split over tokens is planned for the layer).  Projections the
+ * grouped kernels do not take (fp32 activations, in or out below 32 for the
+ * forward / dX reduction, a dX whose scale is carried as two bf16 terms, in
+ * or out below 256 for dW, empty sizes) run through the single-projection
+ * path within the same call.
+ *
+ * tern_proj_t describes one projection: its sizes and the device buffers of
+ * the calls that use them (members a call does not use may be NULL):
+ *   in, out       sizes (multiples of 8); all projections share T;
+ *   q             int8 [in, out]           (tern_layer_materialize)
+ *   tern_packed   handle of tern_packed_words(in, out) words (written by
+ *                 tern_layer_materialize, read by the other calls)
+ *   scale         fp32 [out]
+ *   X             [T, in]   act_dtype      (forward, dW)
+ *   dY            [T, out]  act_dtype      (dX, dW)
+ *   Y             [T, out]  y_dtype        (forward)
+ *   dX            fp32 [T, in]             (dX)
+ *   gq, sgrad     fp32 [in, out], [out]    (dW)
+ * Inputs may be shared between projections (one X for several); no output
+ * may overlap any input or any other output of the call (TERN_ERR_ALIAS).
+ * n: 1 to 8 projections (TERN_ERR_SHAPE otherwise); the array is host
+ * memory, read during the call only.
+ */
+typedef struct tern_proj {
+    int64_t in, out;
+    const int8_t *q;
+    uint32_t *tern_packed;
+    const float *scale;
+    const void *X;
+    const void *dY;
+    void *Y;
+    float *dX;
+    float *gq;
+    float *sgrad;
+} tern_proj_t;
+
+/* tern_layer_materialize -- tern_materialize of every projection (q ->
+ * tern_packed), one launch.  Errors: NULL, SHAPE, THETA, ALIGN, ALIAS, HIP. */
+int tern_layer_materialize(const tern_proj_t *projs, int32_t n, int32_t theta, void *stream);
+
+/* tern_layer_fwd -- tern_linear_fwd of every projection (Y = X . W_eff).
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, HIP. */
+int tern_layer_fwd(const tern_proj_t *projs, int32_t n, int64_t T, int32_t act_dtype, int32_t y_dtype,
+                   void *stream);
+
+/* tern_layer_bwd_dx -- tern_linear_bwd_dx of every projection (dX = dY .
+ * W_eff^T, fp32).  Errors: NULL, SHAPE, DTYPE, ALIGN, ALIAS, HIP. */
+int tern_layer_bwd_dx(const tern_proj_t *projs, int32_t n, int64_t T, int32_t act_dtype, void *stream);
+
+/* tern_layer_bwd_dw_workspace_bytes -- workspace of tern_layer_bwd_dw for
+ * these projections and T, with either activation type (0 for invalid
+ * sizes; only in and out of each projection are read). */
+size_t tern_layer_bwd_dw_workspace_bytes(const tern_proj_t *projs, int32_t n, int64_t T);
+
+/* tern_layer_bwd_dw -- tern_linear_bwd_dw of every projection (gq, sgrad),
+ * sgrad in the same fixed order per projection, bitwise repeatable.
+ * workspace: at least tern_layer_bwd_dw_workspace_bytes(projs, n, T) bytes.
+ * Errors: NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, ALIAS, HIP. */
+int tern_layer_bwd_dw(const tern_proj_t *projs, int32_t n, int64_t T, int32_t act_dtype, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
  * Graphs of library calls.  The page's trainer launches every glue kernel and
  * GEMM of a step separately and notes that it is launch-bound; a caller can
  * instead record any sequence of the calls above (for example materialize,

@@ -51,6 +51,11 @@ SIGNATURES = {
     "tern_panel_reset": (ctypes.c_int, [_vp, _vp]),
     "tern_panel_add": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "tern_panel_fractions": (ctypes.c_int, [_vp, _vp]),
+    "tern_layer_materialize": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
+    "tern_layer_fwd": (ctypes.c_int, [_vp, _i32, _i64, _i32, _i32, _vp]),
+    "tern_layer_bwd_dx": (ctypes.c_int, [_vp, _i32, _i64, _i32, _vp]),
+    "tern_layer_bwd_dw_workspace_bytes": (_sz, [_vp, _i32, _i64]),
+    "tern_layer_bwd_dw": (ctypes.c_int, [_vp, _i32, _i64, _i32, _vp, _sz, _vp]),
     "tern_graph_begin": (ctypes.c_int, [_vp]),
     "tern_graph_end": (ctypes.c_int, [_vp, ctypes.POINTER(_vp)]),
     "tern_graph_launch": (ctypes.c_int, [_vp, _vp]),
@@ -406,6 +411,96 @@ def panel_values(panel: torch.Tensor) -> dict:
     r.update(zip(PANEL_STATS, h[n:].tolist()))
     r.update(tern_panel_fractions(h))
     return r
+
+
+class TernProj(ctypes.Structure):
+    """tern_proj_t: one projection of a layer call."""
+    _fields_ = [("in_", _i64), ("out", _i64), ("q", _vp), ("tern_packed", _vp), ("scale", _vp), ("X", _vp),
+                ("dY", _vp), ("Y", _vp), ("dX", _vp), ("gq", _vp), ("sgrad", _vp)]
+
+
+LAYER_MEMBERS = ("q", "packed", "scale", "X", "dY", "Y", "dX", "gq", "sgrad")
+
+
+def _layer(fn: str, projs, T: int | None, need, act=None):
+    """Marshal a list of projections (dicts with n_in, n_out and the device
+    tensors the call uses: q, packed, scale, X, dY, Y, dX, gq, sgrad) into a
+    tern_proj_t array, checking every tensor the call uses."""
+    n = len(projs)
+    if not 1 <= n <= 8:
+        raise ValueError(f"{fn}: 1 to 8 projections, got {n}")
+    arr = (TernProj * n)()
+    used = []
+    for i, d in enumerate(projs):
+        ni, no = int(d["n_in"]), int(d["n_out"])
+        shapes = {"q": ((ni, no), (torch.int8,)), "scale": ((no,), _F32), "X": ((T, ni), act),
+                  "dY": ((T, no), act), "Y": ((T, no), (torch.float32, act[0] if act else None)),
+                  "dX": ((T, ni), _F32), "gq": ((ni, no), _F32), "sgrad": ((no,), _F32)}
+        for k in need:
+            if k == "packed":
+                _need_packed(fn, d.get("packed"), ni, no)
+            else:
+                shape, dts = shapes[k]
+                _need(fn, f"{k}[{i}]", d.get(k), shape, dts)
+            used.append(d.get(k))
+        arr[i].in_, arr[i].out = ni, no
+        for k, field in (("q", "q"), ("packed", "tern_packed"), ("scale", "scale"), ("X", "X"), ("dY", "dY"),
+                         ("Y", "Y"), ("dX", "dX"), ("gq", "gq"), ("sgrad", "sgrad")):
+            if k in need:
+                p = _ptr(d[k])
+                setattr(arr[i], field, p.value if p is not None else None)
+    _need_device(fn, *used)
+    return arr
+
+
+def tern_layer_materialize(projs, theta: int, stream=None) -> None:
+    """tern_materialize of every projection (q -> packed), one launch."""
+    arr = _layer("tern_layer_materialize", projs, None, ("q", "packed"))
+    _check("tern_layer_materialize", lib().tern_layer_materialize(arr, len(projs), int(theta), _stream(stream)))
+
+
+def tern_layer_fwd(projs, stream=None) -> None:
+    """tern_linear_fwd of every projection (they share T and X's dtype)."""
+    X0 = projs[0]["X"]
+    act = (X0.dtype,)
+    arr = _layer("tern_layer_fwd", projs, X0.shape[0], ("packed", "scale", "X", "Y"), act)
+    ydt = _act_code(projs[0]["Y"])
+    if any(_act_code(d["Y"]) != ydt for d in projs):
+        raise TypeError("tern_layer_fwd: every Y must have the same dtype")
+    _check("tern_layer_fwd", lib().tern_layer_fwd(arr, len(projs), X0.shape[0], _act_code(X0), ydt, _stream(stream)))
+
+
+def tern_layer_bwd_dx(projs, stream=None) -> None:
+    """tern_linear_bwd_dx of every projection."""
+    dY0 = projs[0]["dY"]
+    arr = _layer("tern_layer_bwd_dx", projs, dY0.shape[0], ("packed", "scale", "dY", "dX"), (dY0.dtype,))
+    _check("tern_layer_bwd_dx", lib().tern_layer_bwd_dx(arr, len(projs), dY0.shape[0], _act_code(dY0),
+                                                       _stream(stream)))
+
+
+def tern_layer_bwd_dw_workspace_bytes(shapes, T: int) -> int:
+    """Workspace of tern_layer_bwd_dw for projections of these (n_in, n_out)."""
+    n = len(shapes)
+    arr = (TernProj * max(n, 1))()
+    for i, (ni, no) in enumerate(shapes):
+        arr[i].in_, arr[i].out = int(ni), int(no)
+    return int(lib().tern_layer_bwd_dw_workspace_bytes(arr, n, int(T)))
+
+
+def empty_layer_workspace(shapes, T: int, device="cuda") -> torch.Tensor:
+    nbytes = tern_layer_bwd_dw_workspace_bytes(shapes, T)
+    return torch.empty((max(nbytes, 16) // 16, 16), dtype=torch.uint8, device=device)
+
+
+def tern_layer_bwd_dw(projs, workspace, stream=None) -> None:
+    """tern_linear_bwd_dw of every projection (gq, sgrad)."""
+    X0 = projs[0]["X"]
+    arr = _layer("tern_layer_bwd_dw", projs, X0.shape[0], ("packed", "scale", "X", "dY", "gq", "sgrad"),
+                 (X0.dtype,))
+    _need_device("tern_layer_bwd_dw", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("tern_layer_bwd_dw", lib().tern_layer_bwd_dw(arr, len(projs), X0.shape[0], _act_code(X0),
+                                                       _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def tern_graph_begin(stream) -> None:

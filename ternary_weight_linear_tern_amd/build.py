@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtern.so")
 SOURCES = ["tern_kernels.hip", "tern_panel.hip", "tern_group.hip", "tern_optim.hip", "tern_noalloc.hip", "tern_api.cpp",
-           "tern_plan.cpp"]
+           "tern_layer.cpp", "tern_plan.cpp"]
 ARCH = "gfx950"
 
 # Packed FP32 VALU forms are turned off for all device code.

@@ -11,6 +11,10 @@
 namespace tern {
 
 hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStream_t st);
+// One persistent launch over the items of several problems of one mode (bf16
+// activations, 256 x 256 tiles; each problem's arguments complete and checked,
+// forward / dX with K >= 32, dW with M, N >= 256).
+hipError_t launch_gemm_group(int mode, const GroupArgs &ga, hipStream_t st);
 // The whole packed handle (canonical words, padding, both fragment-ordered
 // copies; see PackedLayout) from q in one launch.
 hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int theta, bool vec,
@@ -23,6 +27,28 @@ hipError_t launch_dw_reduce(const float *ws, int splits, const float *scale, con
 hipError_t launch_sgrad_reduce(const float *part, int64_t nparts, int64_t out, float *sgrad, bool acc, float alpha,
                                hipStream_t st);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
+
+// Several handles in one launch (n <= kMaxGroup matrices; vec: the 16-byte
+// path, which needs out % 16 == 0 and q 16-byte aligned).
+struct MatOneHost {
+    const int8_t *q;
+    uint32_t *packed;
+    int64_t in, out;
+    bool vec;
+};
+hipError_t launch_materialize_group(const MatOneHost *m, int n, int theta, hipStream_t st);
+
+// The dW finish of several projections in two launches: the split-K reduce of
+// those with splits > 1 (gq = G * scale and the 4-row sgrad partials), then
+// the fixed-order sgrad sum of all (nparts rows of partials each).
+struct DwFinishHost {
+    const float *ws;
+    const float *scale;
+    const uint32_t *packed;
+    float *gq, *part, *sgrad;
+    int64_t in, out, splits, nparts;
+};
+hipError_t launch_dw_finish_group(const DwFinishHost *f, int n, hipStream_t st);
 
 // Backward pieces shared by the entry points (tern_api.cpp, tern_noalloc.hip).
 // check_bwd validates the arguments of a backward call (want_dx / want_dw

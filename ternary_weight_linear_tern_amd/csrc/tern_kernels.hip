@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "tern_kernels.h"
 
 namespace tern {
@@ -718,16 +720,32 @@ __device__ __forceinline__ void wait_vm0() {
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Persistent tile walk: WG b, round j -> logical item; consecutive logical
-// items go to one XCD and are grouped 8 tiles along M.
-__device__ __forceinline__ bool p_item(int j, int total, int tiles_m, int tiles_n, int &tm, int &tn,
-                                       int &sp) {
+// Persistent walk over the items of a group of problems: workgroup b, round j
+// -> logical item L (consecutive items go to one XCD), then its problem (the
+// one whose items start at or before L), its split and its tile, grouped 8
+// tiles along M within the problem so that the tiles resident on one XCD
+// share operand panels in its L2.
+__device__ __forceinline__ bool g_item(const GroupArgs &ga, int j, int &pi, int &tm, int &tn, int &sp) {
     const int G = gridDim.x, b = blockIdx.x;
-    const int L = (G & 7) == 0 ? j * G + (b & 7) * (G >> 3) + (b >> 3) : j * G + b;
-    if (L >= total) return false;
+    int L;
+    if (ga.dyn) {
+        // one item per workgroup; within each full run of 256 consecutive
+        // workgroups (dispatched together, round-robin over the XCDs) the
+        // items of one XCD are consecutive
+        const int base = b & ~255, c = b & 255;
+        L = j * G + base + (base + 256 <= G ? (c & 7) * 32 + (c >> 3) : c);
+    } else {
+        L = (G & 7) == 0 ? j * G + (b & 7) * (G >> 3) + (b >> 3) : j * G + b;
+    }
+    if (L >= ga.start[ga.n]) return false;
+    int p = 0;
+    while (p + 1 < ga.n && L >= ga.start[p + 1]) p++;
+    pi = p;
+    const int tiles_m = ga.p[p].tiles_m, tiles_n = ga.p[p].tiles_n;
     const int tiles = tiles_m * tiles_n;
-    sp = L / tiles;
-    const int t = L - sp * tiles;
+    const int local = L - ga.start[p];
+    sp = local / tiles;
+    const int t = local - sp * tiles;
     constexpr int GM = 8;
     const int group = t / (GM * tiles_n);
     const int first = group * GM;
@@ -821,38 +839,43 @@ __device__ __forceinline__ void w_barrier() {
 }
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_dw_kernel(GemmArgs g) {
+void gemm_dw_kernel(GroupArgs ga) {
     constexpr int ES = 2;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, h = lane >> 5;
-    const int total = g.tiles_m * g.tiles_n * g.splits;
-    const int64_t lda = (int64_t)g.in * ES, ldb = (int64_t)g.out * ES;   // bytes per token row
 
-    // chunks of item (tile, split) sp: its tokens, rounded up to an even count
-    auto item_chunks = [&](int sp, int64_t &kbeg, int64_t &klen) __attribute__((always_inline)) {
-        kbeg = (int64_t)sp * g.kps;
-        klen = min((int64_t)g.K, kbeg + g.kps) - kbeg;
+    // chunks of item (tile, split) sp of problem pi: its tokens, rounded up
+    // to an even count
+    auto item_chunks = [&](int pi, int sp, int64_t &kbeg, int64_t &klen) __attribute__((always_inline)) {
+        const int64_t kps = ga.p[pi].kps;
+        kbeg = (int64_t)sp * kps;
+        klen = min((int64_t)ga.p[pi].K, kbeg + kps) - kbeg;
         const int n = (int)((klen + W_KC - 1) / W_KC);
         return (n + 1) & ~1;
     };
 
-    // ---- issue side: chunk ic of item ij; iv false once the items run out
-    // (every record count is then 0: zeros into LDS, no memory access)
-    int ij = 0, ic = 0, itm = 0, itn = 0, isp = 0, inch = 0;
+    // ---- issue side: chunk ic of item ij (problem ipi); iv false once the
+    // items run out (every record count is then 0: zeros into LDS, no memory
+    // access)
+    int ij = 0, ic = 0, itm = 0, itn = 0, isp = 0, ipi = 0, inch = 0;
     const char *ia = nullptr, *ib = nullptr;   // token row of chunk ic in each operand
     int64_t irem = 0;                          // token rows of the item from chunk ic on
+    int64_t lda = 0, ldb = 0;                  // bytes per token row of the item's operands
     DmaTok da, db;
-    bool iv = p_item(0, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+    bool iv = g_item(ga, 0, ipi, itm, itn, isp);
     auto set_itile = [&]() __attribute__((always_inline)) {
+        const GemmArgs &ig = ga.p[ipi];
+        lda = (int64_t)ig.in * ES;
+        ldb = (int64_t)ig.out * ES;
         int64_t ikbeg = 0, iklen = 0;
-        inch = item_chunks(isp, ikbeg, iklen);
+        inch = item_chunks(ipi, isp, ikbeg, iklen);
         irem = iv ? iklen : 0;
-        ia = (const char *)g.act0 + ikbeg * lda + (int64_t)itm * 256 * ES;
-        ib = (const char *)g.act1 + ikbeg * ldb + (int64_t)itn * 256 * ES;
-        da.init(lda, g.M - itm * 256, wave);
-        db.init(ldb, g.N - itn * 256, wave);
+        ia = (const char *)ig.act0 + ikbeg * lda + (int64_t)itm * 256 * ES;
+        ib = (const char *)ig.act1 + ikbeg * ldb + (int64_t)itn * 256 * ES;
+        da.init(lda, ig.M - itm * 256, wave);
+        db.init(ldb, ig.N - itn * 256, wave);
     };
     set_itile();
     // record count of rows bytes (rows of ld bytes), saturated to the 31-bit range
@@ -860,11 +883,11 @@ void gemm_dw_kernel(GemmArgs g) {
         const int64_t b = rows * ld;
         return __builtin_amdgcn_readfirstlane((uint32_t)(b <= 0 ? 0 : (b > 0x7FFFFFF0 ? 0x7FFFFFF0 : b)));
     };
-    // ---- compute side: item cj
-    int cj = 0, ctm = 0, ctn = 0, csp = 0;
+    // ---- compute side: item cj (problem cpi)
+    int cj = 0, ctm = 0, ctn = 0, csp = 0, cpi = 0;
     int64_t ckbeg = 0, cklen = 0;
-    bool cv = p_item(0, total, g.tiles_m, g.tiles_n, ctm, ctn, csp);
-    int cnch = cv ? item_chunks(csp, ckbeg, cklen) : 0;
+    bool cv = g_item(ga, 0, cpi, ctm, ctn, csp);
+    int cnch = cv ? item_chunks(cpi, csp, ckbeg, cklen) : 0;
 
     f32x16 acc[4][4];
     u32x4 f0a[2][4], f0b[2][4];   // K quarter 0 fragments of the current / next chunk
@@ -890,7 +913,7 @@ void gemm_dw_kernel(GemmArgs g) {
             ic = 0;
             if (iv) {
                 ++ij;
-                iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+                iv = g_item(ga, ij, ipi, itm, itn, isp);
                 set_itile();
             }
         }
@@ -1051,6 +1074,7 @@ void gemm_dw_kernel(GemmArgs g) {
         }
         // ---- epilogue of item (ctm, ctn, csp).  acc[fm][fn][i] is C[m][n] with
         //   m = m0 + wm*128 + fm*32 + 8*(i/4) + 4*h + i%4,  n = n0 + wn*128 + fn*32 + l32
+        const GemmArgs &g = ga.p[cpi];
         const int mw = ctm * 256 + wm * 128, nw = ctn * 256 + wn * 128;
         // buffer stores over this wave's 128 x 128 block: the lane offset holds
         // its column and 4h rows, the scalar offset the row group.  M is a
@@ -1127,8 +1151,8 @@ void gemm_dw_kernel(GemmArgs g) {
         }
         zero_acc();
         ++cj;
-        cv = p_item(cj, total, g.tiles_m, g.tiles_n, ctm, ctn, csp);
-        if (cv) cnch = item_chunks(csp, ckbeg, cklen);
+        cv = g_item(ga, cj, cpi, ctm, ctn, csp);
+        if (cv) cnch = item_chunks(cpi, csp, ckbeg, cklen);
     }
     // the last issues were out-of-range loads still writing zeros into the
     // stages: drain them before the workgroup ends
@@ -1318,7 +1342,7 @@ __device__ __forceinline__ uint32_t r_scaled_pair(uint32_t v, uint32_t q) {
 
 template <int MODE, bool ACC = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_rd_kernel(GemmArgs g) {
+void gemm_rd_kernel(GroupArgs ga) {
     static_assert(MODE == MODE_FWD || MODE == MODE_DX, "forward and dX only");
     static_assert(!ACC || MODE == MODE_DX, "accumulation is a dX variant");
     constexpr int ES = 2;
@@ -1327,11 +1351,6 @@ void gemm_rd_kernel(GemmArgs g) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
-    const int total = g.tiles_m * g.tiles_n;
-    const int nch = g.nch;
-    const int nch2 = (nch + 1) & ~1;   // chunks per tile, padded to even for the 2-way unroll
-    const int64_t ld = (int64_t)g.K * ES;   // bytes per activation row
-    const int ld32 = g.K * ES;              // the same (K <= 2^20)
     char *wl = r_lds + wave * R_WAVE;
     // slot of this lane's 16 bytes in every DMA row group, and its logical chunk
     const int cb = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
@@ -1350,14 +1369,23 @@ void gemm_rd_kernel(GemmArgs g) {
     // one M0: the immediate offset 1024 i moves the LDS destination and the
     // global address alike, and the lane offsets are stored less 1024 i
     // (which needs K >= 32: 16 rows of 2 K bytes span 1024 bytes).
-    int ij = 0, ic = 0, itm = 0, itn = 0, isp = 0;
-    bool iv = p_item(0, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+    int ij = 0, ic = 0, itm = 0, itn = 0, isp = 0, ipi = 0;
+    bool iv = g_item(ga, 0, ipi, itm, itn, isp);
+    int i_nch2 = 0;             // chunks per tile of the issue side's problem, padded to even
+    int ld32 = 0;               // bytes per activation row of that problem (K <= 2^20)
+    const float *i_scale = nullptr;   // its scales
     const char *pa = nullptr;   // activation rows of tile ij (this wave's first row)
     const uint32_t *pf = nullptr;   // this wave's fragment words of tile ij
     uint32_t na = 0, nf = 0, ns = 0;   // record counts of the three resources
     uint32_t boff[8];   // activation load i: lane's row * ld + 16-byte column - 1024 (i % 4), or OOB
     const uint32_t soff_lane = lane < 32 ? (uint32_t)lane * 4u : OOB;   // dX scales: 32 per chunk
     auto set_itile = [&]() __attribute__((always_inline)) {
+        const GemmArgs &g = ga.p[ipi];
+        const int nch = g.nch;
+        i_nch2 = (nch + 1) & ~1;
+        const int64_t ld = (int64_t)g.K * ES;
+        ld32 = g.K * ES;
+        i_scale = g.scale;
         const int n0 = itn * 256 + wn * 128;
         // bytes from this wave's first row to the end of the tensor (integer
         // arithmetic only: the int64 min / max overloads go through f64)
@@ -1415,13 +1443,13 @@ void gemm_rd_kernel(GemmArgs g) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(pf, nf), (LDS_AS void *)(st + R_B), 16,
                                                      (uint32_t)lane * 16u, ic * 2048, 0, 0);
             if constexpr (MODE == MODE_DX)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(g.scale, ns), (LDS_AS void *)(st + R_B + R_A), 4,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(i_scale, ns), (LDS_AS void *)(st + R_B + R_A), 4,
                                                          soff_lane, ic * R_KC * 4, 0, 0);
-            if (++ic == nch2) {
+            if (++ic == i_nch2) {
                 ic = 0;
                 if (iv) {
                     ++ij;
-                    iv = p_item(ij, total, g.tiles_m, g.tiles_n, itm, itn, isp);
+                    iv = g_item(ga, ij, ipi, itm, itn, isp);
                     set_itile();
                 }
             }
@@ -1435,9 +1463,10 @@ void gemm_rd_kernel(GemmArgs g) {
         issue_part(s, std::integral_constant<int, 4>{});
     };
 
-    // ---- compute side: tile cj
-    int cj = 0, ctm = 0, ctn = 0, csp = 0;
-    bool cv = p_item(0, total, g.tiles_m, g.tiles_n, ctm, ctn, csp);
+    // ---- compute side: tile cj (problem cpi)
+    int cj = 0, ctm = 0, ctn = 0, csp = 0, cpi = 0;
+    bool cv = g_item(ga, 0, cpi, ctm, ctn, csp);
+    int c_nch2 = cv ? (ga.p[cpi].nch + 1) & ~1 : 0;
     int hist = 0;   // bit 0: this chunk is one of a tile's first two after an epilogue
 
     f32x16 acc[4][4];
@@ -1501,6 +1530,7 @@ void gemm_rd_kernel(GemmArgs g) {
     // of the lane, the row block m goes in the scalar offset; M is a multiple
     // of 8 and the 8-row groups are wave-uniform, so the m test is scalar.
     auto epilogue = [&]() __attribute__((always_inline)) {
+        const GemmArgs &g = ga.p[cpi];
         const int mw = ctm * 256 + wm * 128, nw = ctn * 256 + wn * 128;
         const int ldo = MODE == MODE_FWD ? g.out : g.in;
         const bool obf = MODE == MODE_FWD && g.y_bf16;
@@ -1689,14 +1719,15 @@ void gemm_rd_kernel(GemmArgs g) {
     // tiles, then their chunks (the issue side runs three chunks ahead, across
     // tile boundaries)
     while (cv) {
-        for (int c = 0; c < nch2; c += 2) {
+        for (int c = 0; c < c_nch2; c += 2) {
             chunk(I0{});
             chunk(I1{});
         }
         epilogue();
         zero_acc();
         ++cj;
-        cv = p_item(cj, total, g.tiles_m, g.tiles_n, ctm, ctn, csp);
+        cv = g_item(ga, cj, cpi, ctm, ctn, csp);
+        if (cv) c_nch2 = (ga.p[cpi].nch + 1) & ~1;
         hist = 3;
     }
     // the last issues were out-of-range loads still writing zeros into this
@@ -1720,11 +1751,9 @@ struct MatGrid {
     int nb_canon, ngf, nb_fwd, ngd;   // blocks: canonical part; chunk groups and blocks of the copies
 };
 template <bool VEC>
-__global__ __launch_bounds__(256) void materialize_kernel(const int8_t *__restrict__ q, int64_t in, int64_t out,
-                                                          int64_t wpr, int theta, uint32_t *__restrict__ packed,
-                                                          MatGrid mg) {
-    __shared__ uint32_t blk[D_LDS];
-    int b = blockIdx.x;
+__device__ __forceinline__ void materialize_block(const int8_t *__restrict__ q, int64_t in, int64_t out, int64_t wpr,
+                                                  int theta, uint32_t *__restrict__ packed, const MatGrid &mg, int b,
+                                                  uint32_t *blk) {
     if (b < mg.nb_canon) {
         const int64_t i = (int64_t)b * 256 + threadIdx.x;
         if (i < mg.nwords) {
@@ -1744,20 +1773,54 @@ __global__ __launch_bounds__(256) void materialize_kernel(const int8_t *__restri
     derive_block<VEC, true>(q, in, out, wpr, theta, mg.nchd, b / mg.ngd, b % mg.ngd, packed + mg.dx_off, blk);
 }
 
+template <bool VEC>
+__global__ __launch_bounds__(256) void materialize_kernel(const int8_t *__restrict__ q, int64_t in, int64_t out,
+                                                          int64_t wpr, int theta, uint32_t *__restrict__ packed,
+                                                          MatGrid mg) {
+    __shared__ uint32_t blk[D_LDS];
+    materialize_block<VEC>(q, in, out, wpr, theta, packed, mg, (int)blockIdx.x, blk);
+}
+
+// Several matrices in one launch: block b belongs to the matrix whose blocks
+// start at or before it, and runs that matrix's block b - start.
+struct MatOne {
+    const int8_t *q;
+    uint32_t *packed;
+    int64_t in, out, wpr;
+    int vec;
+    MatGrid mg;
+};
+struct MatGroup {
+    int n, theta;
+    int start[kMaxGroup + 1];
+    MatOne m[kMaxGroup];
+};
+__global__ __launch_bounds__(256) void materialize_group_kernel(MatGroup g) {
+    __shared__ uint32_t blk[D_LDS];
+    const int b = blockIdx.x;
+    int p = 0;
+    while (p + 1 < g.n && b >= g.start[p + 1]) p++;
+    const MatOne &m = g.m[p];
+    if (m.vec)
+        materialize_block<true>(m.q, m.in, m.out, m.wpr, g.theta, m.packed, m.mg, b - g.start[p], blk);
+    else
+        materialize_block<false>(m.q, m.in, m.out, m.wpr, g.theta, m.packed, m.mg, b - g.start[p], blk);
+}
+
 // Split-K finish of dW: G = sum over splits (ascending), gq = G * scale (acc:
 // gq + alpha * G * scale), and the sgrad partial of a block of kReduceRows rows
 // (ascending r).  Each thread owns 4 consecutive columns (16-byte loads and
 // stores); a block covers 1024 columns of kReduceRows rows, few enough rows
 // that a 2048 x 2048 reduce has 2048 blocks (several waves per SIMD to hide
 // the loads' latency), with its split loop unrolled.
-__global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ ws, int splits,
-                                                        const float *__restrict__ scale,
-                                                        const uint32_t *__restrict__ packed, int in,
-                                                        int out, int64_t wpr, float *__restrict__ gq,
-                                                        float *__restrict__ part, int acc, float alpha) {
-    const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+__device__ __forceinline__ void dw_reduce_block(const float *__restrict__ ws, int splits,
+                                                const float *__restrict__ scale,
+                                                const uint32_t *__restrict__ packed, int in, int out, int64_t wpr,
+                                                float *__restrict__ gq, float *__restrict__ part, int acc,
+                                                float alpha, int bx, int by) {
+    const int c = (bx * 256 + threadIdx.x) * 4;
     if (c >= out) return;
-    const int r0 = blockIdx.y * kReduceRows;
+    const int r0 = by * kReduceRows;
     const int r1 = min(in, r0 + kReduceRows);
     const f32x4 s = *(const f32x4 *)(scale + c);
     const int64_t plane = (int64_t)in * out;
@@ -1778,7 +1841,15 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
         p.z += gv.z * code_to_f32((word >> 4) & 3u);
         p.w += gv.w * code_to_f32((word >> 6) & 3u);
     }
-    *(f32x4 *)(part + (int64_t)blockIdx.y * out + c) = p;
+    *(f32x4 *)(part + (int64_t)by * out + c) = p;
+}
+
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict__ ws, int splits,
+                                                        const float *__restrict__ scale,
+                                                        const uint32_t *__restrict__ packed, int in,
+                                                        int out, int64_t wpr, float *__restrict__ gq,
+                                                        float *__restrict__ part, int acc, float alpha) {
+    dw_reduce_block(ws, splits, scale, packed, in, out, wpr, gq, part, acc, alpha, (int)blockIdx.x, (int)blockIdx.y);
 }
 
 // sgrad[c] = sum of the row-block partials in ascending order, in f64, as a
@@ -1786,12 +1857,11 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float *__restrict_
 // ascending order, then the 8 group sums in ascending order (acc: added, times
 // alpha, to the existing sgrad in f64).  A block of 256 threads serves 32
 // columns.
-__global__ __launch_bounds__(256) void sgrad_reduce_kernel(const float *__restrict__ part, int nparts,
-                                                           int out, float *__restrict__ sgrad, int acc,
-                                                           float alpha) {
+__device__ __forceinline__ void sgrad_reduce_block(const float *__restrict__ part, int nparts, int out,
+                                                   float *__restrict__ sgrad, int acc, float alpha, int bx) {
     __shared__ double red[8][32];
     const int cl = threadIdx.x & 31, grp = threadIdx.x >> 5;
-    const int c = blockIdx.x * 32 + cl;
+    const int c = bx * 32 + cl;
     const int chunk = (nparts + 7) / 8;
     const int p0 = grp * chunk, p1 = min(nparts, p0 + chunk);
     double a = 0.0;
@@ -1808,6 +1878,38 @@ __global__ __launch_bounds__(256) void sgrad_reduce_kernel(const float *__restri
         if (acc) s = (double)sgrad[c] + (double)alpha * s;
         sgrad[c] = (float)s;
     }
+}
+
+__global__ __launch_bounds__(256) void sgrad_reduce_kernel(const float *__restrict__ part, int nparts,
+                                                           int out, float *__restrict__ sgrad, int acc,
+                                                           float alpha) {
+    sgrad_reduce_block(part, nparts, out, sgrad, acc, alpha, (int)blockIdx.x);
+}
+
+// The dW finishing kernels of the projections of a layer, one launch each:
+// blockIdx.z is the projection; blocks past a projection's grid return.
+struct ReduceOne {
+    const float *ws;             // split partials (splits > 1)
+    const float *scale;
+    const uint32_t *packed;
+    float *gq, *part, *sgrad;
+    int in, out, splits, nparts;
+    int64_t wpr;
+};
+struct ReduceGroup {
+    int n;
+    ReduceOne r[kMaxGroup];
+};
+__global__ __launch_bounds__(256) void dw_reduce_group_kernel(ReduceGroup g) {
+    const ReduceOne &r = g.r[blockIdx.z];
+    if (r.splits < 2 || (int)blockIdx.y * kReduceRows >= r.in) return;
+    dw_reduce_block(r.ws, r.splits, r.scale, r.packed, r.in, r.out, r.wpr, r.gq, r.part, 0, 1.0f, (int)blockIdx.x,
+                    (int)blockIdx.y);
+}
+__global__ __launch_bounds__(256) void sgrad_reduce_group_kernel(ReduceGroup g) {
+    const ReduceOne &r = g.r[blockIdx.y];
+    if ((int)blockIdx.x * 32 >= r.out) return;
+    sgrad_reduce_block(r.part, r.nparts, r.out, r.sgrad, 0, 1.0f, (int)blockIdx.x);
 }
 
 // Zero fill in 16-byte units.
@@ -1839,6 +1941,21 @@ int device_cus() {
     return cache[dev];
 }
 
+template <int MODE>
+hipError_t launch_persistent(const GroupArgs &ga, hipStream_t st) {
+    const int64_t items = ga.start[ga.n];
+    if (items <= 0) return hipSuccess;
+    const int64_t cus = device_cus();
+    const dim3 pgrid((unsigned)(ga.dyn ? items : (items < cus ? items : cus))), block(dev::NT);
+    if constexpr (MODE == MODE_DW)
+        hipLaunchKernelGGL(dev::gemm_dw_kernel, pgrid, block, 0, st, ga);
+    else if (MODE == MODE_DX && ga.p[0].acc)
+        hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE_DX, true>), pgrid, block, 0, st, ga);
+    else
+        hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE>), pgrid, block, 0, st, ga);
+    return hipGetLastError();
+}
+
 template <bool BF, int MODE>
 hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)p.grid), block(dev::NT);
@@ -1847,16 +1964,14 @@ hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
         // (the exact two-term dX scale runs on the LDS-staged kernel)
         if (p.tile == TILE_256 && (MODE == MODE_DW ? a.M >= 256 && a.N >= 256 : a.K >= 32) &&
             !(MODE == MODE_DX && a.exact_scale)) {
-            // persistent: at most one workgroup per compute unit
-            const int64_t cus = device_cus();
-            const dim3 pgrid((unsigned)(p.grid < cus ? p.grid : cus));
-            if constexpr (MODE == MODE_DW)
-                hipLaunchKernelGGL(dev::gemm_dw_kernel, pgrid, block, 0, st, a);
-            else if (MODE == MODE_DX && a.acc)
-                hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE_DX, true>), pgrid, block, 0, st, a);
-            else
-                hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE>), pgrid, block, 0, st, a);
-            return hipGetLastError();
+            // persistent: at most one workgroup per compute unit, walking the
+            // items of a group of one problem
+            GroupArgs ga{};
+            ga.n = 1;
+            ga.start[0] = 0;
+            ga.start[1] = (int)(p.tiles_m * p.tiles_n * p.splits);
+            ga.p[0] = a;
+            return launch_persistent<MODE>(ga, st);
         }
     }
     switch (p.tile) {
@@ -1867,6 +1982,18 @@ hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 }  // namespace
+
+hipError_t launch_gemm_group(int mode, const GroupArgs &ga_in, hipStream_t st) {
+    if (ga_in.n < 1 || ga_in.n > kMaxGroup) return hipErrorInvalidValue;
+    GroupArgs ga = ga_in;
+    int64_t cost[kMaxGroup];
+    for (int p = 0; p < ga.n; p++)
+        cost[p] = mode == MODE_DW ? cdiv(ga.p[p].kps, dev::W_KC) : (int64_t)ga.p[p].nch;
+    ga.dyn = group_dynamic(ga, cost, device_cus()) ? 1 : 0;
+    if (mode == MODE_FWD) return launch_persistent<MODE_FWD>(ga, st);
+    if (mode == MODE_DX) return launch_persistent<MODE_DX>(ga, st);
+    return launch_persistent<MODE_DW>(ga, st);
+}
 
 hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStream_t st) {
     if (p.grid <= 0) return hipSuccess;
@@ -1882,12 +2009,12 @@ hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStrea
     return launch_mode<false, MODE_DW>(p, a, st);
 }
 
-hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int theta, bool vec,
-                              uint32_t *packed, hipStream_t st) {
+namespace {
+// Blocks of the materialize launch of one [in, out] matrix (0 if empty).
+int64_t mat_grid(int64_t in, int64_t out, dev::MatGrid &mg) {
     const PackedLayout L = packed_layout(in, out);
-    if (L.total == 0) return hipSuccess;
+    if (L.total == 0) return 0;
     const int64_t wpr = cdiv(out, 16);
-    dev::MatGrid mg;
     mg.nwords = in * wpr;
     mg.nfill = L.fwd_off;
     // forward operand: tiles over out, chunks over in; dX operand: the reverse
@@ -1898,16 +2025,87 @@ hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int thet
     const int64_t nb_canon = cdiv(mg.nfill, 256), ngf = cdiv(mg.nchf, dev::D_G), ngd = cdiv(mg.nchd, dev::D_G);
     const int64_t nb_fwd = cdiv(out, 256) * ngf, nb_dx = cdiv(in, 256) * ngd;
     const int64_t blocks = nb_canon + nb_fwd + nb_dx;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     mg.nb_canon = (int)nb_canon;
     mg.ngf = (int)ngf;
     mg.nb_fwd = (int)nb_fwd;
     mg.ngd = (int)ngd;
+    return blocks;
+}
+}  // namespace
+
+hipError_t launch_materialize(const int8_t *q, int64_t in, int64_t out, int theta, bool vec,
+                              uint32_t *packed, hipStream_t st) {
+    dev::MatGrid mg;
+    const int64_t blocks = mat_grid(in, out, mg);
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int64_t wpr = cdiv(out, 16);
     const dim3 grid((unsigned)blocks), block(256);
     if (vec)
         hipLaunchKernelGGL((dev::materialize_kernel<true>), grid, block, 0, st, q, in, out, wpr, theta, packed, mg);
     else
         hipLaunchKernelGGL((dev::materialize_kernel<false>), grid, block, 0, st, q, in, out, wpr, theta, packed, mg);
+    return hipGetLastError();
+}
+
+hipError_t launch_materialize_group(const MatOneHost *m, int n, int theta, hipStream_t st) {
+    if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
+    dev::MatGroup g{};
+    g.n = n;
+    g.theta = theta;
+    int64_t total = 0;
+    for (int i = 0; i < n; i++) {
+        dev::MatOne &o = g.m[i];
+        o.q = m[i].q;
+        o.packed = m[i].packed;
+        o.in = m[i].in;
+        o.out = m[i].out;
+        o.wpr = cdiv(m[i].out, 16);
+        o.vec = m[i].vec ? 1 : 0;
+        g.start[i] = (int)total;
+        total += mat_grid(m[i].in, m[i].out, o.mg);
+        if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    }
+    g.start[n] = (int)total;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(dev::materialize_group_kernel, dim3((unsigned)total), dim3(256), 0, st, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_dw_finish_group(const DwFinishHost *f, int n, hipStream_t st) {
+    if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
+    dev::ReduceGroup g{};
+    g.n = n;
+    int64_t gx = 0, gy = 0, sx = 0;
+    bool any_split = false;
+    for (int i = 0; i < n; i++) {
+        dev::ReduceOne &r = g.r[i];
+        r.ws = f[i].ws;
+        r.scale = f[i].scale;
+        r.packed = f[i].packed;
+        r.gq = f[i].gq;
+        r.part = f[i].part;
+        r.sgrad = f[i].sgrad;
+        r.in = (int)f[i].in;
+        r.out = (int)f[i].out;
+        r.splits = (int)f[i].splits;
+        r.nparts = (int)f[i].nparts;
+        r.wpr = cdiv(f[i].out, 16);
+        if (f[i].splits > 1) {
+            any_split = true;
+            gx = std::max<int64_t>(gx, cdiv(f[i].out, 1024));
+            gy = std::max<int64_t>(gy, cdiv(f[i].in, kReduceRows));
+        }
+        sx = std::max<int64_t>(sx, cdiv(f[i].out, 32));
+    }
+    if (any_split) {
+        hipLaunchKernelGGL(dev::dw_reduce_group_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)n), dim3(256), 0,
+                           st, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (sx == 0) return hipSuccess;
+    hipLaunchKernelGGL(dev::sgrad_reduce_group_kernel, dim3((unsigned)sx, (unsigned)n), dim3(256), 0, st, g);
     return hipGetLastError();
 }
 

@@ -106,6 +106,64 @@ GemmPlan plan_gemm(int mode, int64_t T, int64_t in, int64_t out, bool bf16, int6
     return p;
 }
 
+int64_t plan_layer_dw_splits(int64_t T, int64_t tiles, int64_t sum_in_out, bool bf16) {
+    const int64_t kstep = k_step(bf16);
+    const int64_t ksteps = cdiv(T, kstep);
+    int64_t max_s = ksteps / 8;
+    if (max_s < 1) max_s = 1;
+    if (max_s > 32) max_s = 32;
+    double best = -1.0;
+    int64_t best_kps = ksteps * kstep;
+    for (int64_t s = 1; s <= max_s; s *= 2) {
+        const int64_t kps = cdiv(ksteps, s) * kstep;
+        const int64_t real_s = cdiv(T, kps);
+        const int64_t items = tiles * real_s;
+        // rounds of items over the chip, each as long as one split's K steps,
+        // plus the prologue / epilogue of each item (about 2 K steps)
+        const double t_mma = double(cdiv(items, kCUs)) * double(kps / kstep + 2);
+        // split partials: written once and read once in fp32 (in K-step units
+        // of a 256 x 256 tile: 1 K step of 64 bf16 moves 64 KB at ~30 B/clk/CU,
+        // i.e. ~2000 clk; here the whole chip moves the partials at 5 TB/s)
+        const double step_s = 2000.0 / 2.1e9;
+        const double t_ws = real_s > 1 ? 2.0 * double(real_s) * double(sum_in_out) * 4.0 / 5.0e12 / step_s : 0.0;
+        const double score = 1.0 / (t_mma + t_ws);
+        if (score > best) {
+            best = score;
+            best_kps = kps;
+        }
+    }
+    return best_kps;
+}
+
+bool group_dynamic(const GroupArgs &ga, const int64_t *cost, int64_t cus) {
+    const int64_t items = ga.start[ga.n];
+    if (items <= cus || cus <= 0) return false;
+    // static makespan: workgroup w takes items w, w + G, w + 2G, ... (G = cus),
+    // each costing its problem's length plus about 2 chunks of prologue and
+    // epilogue that the persistent walk overlaps with the neighbours' work
+    int64_t worst = 0, total = 0;
+    for (int64_t w = 0; w < cus; w++) {
+        int64_t load = 0;
+        for (int p = 0; p < ga.n; p++) {
+            const int64_t s0 = ga.start[p], s1 = ga.start[p + 1];
+            // k with s0 <= w + k G < s1
+            const int64_t k0 = s0 > w ? (s0 - w + cus - 1) / cus : 0;
+            const int64_t k1 = s1 > w ? (s1 - w + cus - 1) / cus : 0;
+            if (k1 > k0) load += (k1 - k0) * cost[p];
+        }
+        worst = load > worst ? load : worst;
+        total += load;
+    }
+    // one workgroup per item, longest first, each started as a unit frees up
+    // (list scheduling): about the average load, or the longest item; the
+    // prologue and epilogue of every item (2 chunks) are no longer hidden
+    int64_t longest = 0;
+    for (int p = 0; p < ga.n; p++) longest = cost[p] > longest ? cost[p] : longest;
+    double dyn_est = double(total) / double(cus) + 2.0 * double(items) / double(cus);
+    if (dyn_est < double(longest + 2)) dyn_est = double(longest + 2);
+    return double(worst) > 1.08 * dyn_est;
+}
+
 bool dx_exact_scale(int64_t T, int64_t in, int64_t out) {
     return out < kFoldMinCols || T * in < kFoldMinOutputs;
 }

@@ -60,6 +60,33 @@ struct GemmArgs {
     int exact_scale;         // DX, bf16: the scale as the sum of two bf16 terms (two passes over K)
 };
 
+// Several independent problems of one mode in one persistent launch (the
+// projections of a layer): their work items (tiles, times splits for dW) form
+// one item space, problem by problem, and every workgroup walks it.
+constexpr int kMaxGroup = 8;
+struct GroupArgs {
+    int n;                          // problems
+    int start[kMaxGroup + 1];       // first item of each problem; start[n] = all items
+    int dyn;                        // 1: one workgroup per item (grid = items), items in order
+    GemmArgs p[kMaxGroup];
+};
+
+// Item walk of a group launch on `cus` compute units: persistent (the grid
+// walks the items round-robin, each workgroup taking every grid-th item) or,
+// when that leaves the work unbalanced, one workgroup per item in item order
+// (the dispatcher then starts each as a unit frees up: longest items first,
+// since problems are ordered by item length).  cost[p]: relative length of
+// problem p's items.  Returns true for one workgroup per item.
+bool group_dynamic(const GroupArgs &ga, const int64_t *cost, int64_t cus);
+
+// Tokens per split of the weight-gradient product shared by the problems of
+// a layer (all have K = T; the split count is cdiv(T, result)): the count
+// (a power of two within plan_gemm's limits: at least 8 K steps per split, at
+// most 32) that minimises rounds of items over the chip times their length
+// plus the traffic of the split partials.  tiles: the 256 x 256 tiles of all
+// problems together.
+int64_t plan_layer_dw_splits(int64_t T, int64_t tiles, int64_t sum_in_out, bool bf16);
+
 // dX with bf16 activations: does the scale go into the operand as the sum of
 // two bf16 terms (hi = bf16(scale), lo = bf16(scale - hi), two passes over K)
 // instead of one rounded term?  One rounded term has a relative error of up to

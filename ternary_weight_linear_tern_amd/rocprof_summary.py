@@ -49,7 +49,7 @@ def kernel_code_hash(*paths: str) -> str:
 
 def entry_of(kernel: str) -> str | None:
     k = kernel
-    if "materialize_kernel" in k or "derive_kernel" in k:
+    if "materialize_kernel" in k or "materialize_group_kernel" in k or "derive_kernel" in k:
         return "materialize"
     if "gemm_dw_kernel" in k:
         return "bwd_dw"

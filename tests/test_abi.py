@@ -299,3 +299,78 @@ def test_noalloc_rejects_before_any_hip_call(L):
     big = [P(k << 40) for k in range(1, 8)]   # far apart: no overlap at these sizes
     assert f(big[0], big[1], BF16, big[2], big[3], 64, 1 << 20, 1 << 14, big[4], F32, big[5], big[6], s) == -10
 
+
+def _projs(n, shapes, base=1 << 40):
+    """tern_proj_t array with every pointer in its own 1 GiB window."""
+    arr = (tl.TernProj * n)()
+    for i, (ni, no) in enumerate(shapes):
+        arr[i].in_, arr[i].out = ni, no
+        for j, f in enumerate(("q", "tern_packed", "scale", "X", "dY", "Y", "dX", "gq", "sgrad")):
+            setattr(arr[i], f, base + ((i * 16 + j) << 30))
+    return arr
+
+
+def test_layer_calls_reject(L):
+    """The layer calls check every projection and the aliasing across them
+    before any HIP call."""
+    s = P(0)
+    shapes = [(512, 512), (512, 2048), (2048, 512)]
+    a = _projs(3, shapes)
+    T = 2048
+    assert L.tern_layer_fwd(a, 0, T, BF16, F32, s) == SHAPE
+    assert L.tern_layer_fwd(a, 9, T, BF16, F32, s) == SHAPE
+    assert L.tern_layer_fwd(None, 3, T, BF16, F32, s) == NULL
+    assert L.tern_layer_fwd(a, 3, T, 5, F32, s) == DTYPE
+    assert L.tern_layer_fwd(a, 3, T, F32, BF16, s) == DTYPE
+    b = _projs(3, shapes)
+    b[1].out = 2044
+    assert L.tern_layer_fwd(b, 3, T, BF16, F32, s) == SHAPE
+    b = _projs(3, shapes)
+    b[2].X = None
+    assert L.tern_layer_fwd(b, 3, T, BF16, F32, s) == NULL
+    b = _projs(3, shapes)
+    b[2].Y = b[2].Y + 4
+    assert L.tern_layer_fwd(b, 3, T, BF16, F32, s) == ALIGN
+    b = _projs(3, shapes)
+    b[2].Y = b[0].X          # projection 2 writes over projection 0's input
+    assert L.tern_layer_fwd(b, 3, T, BF16, F32, s) == ALIAS
+    b = _projs(3, shapes)
+    b[1].Y = b[0].Y + 256    # two outputs overlap
+    assert L.tern_layer_fwd(b, 3, T, BF16, F32, s) == ALIAS
+    b = _projs(3, shapes)
+    b[1].X = b[0].X          # a shared input is fine: stops at the (absent) device, not at ALIAS
+    b[1].dX = b[1].dX + 4
+    assert L.tern_layer_bwd_dx(b, 3, T, BF16, s) == ALIGN
+    b = _projs(3, shapes)
+    b[0].dX = b[2].dY
+    assert L.tern_layer_bwd_dx(b, 3, T, BF16, s) == ALIAS
+    # dW: workspace size and overlap
+    need = L.tern_layer_bwd_dw_workspace_bytes(a, 3, T)
+    assert need > 0 and need % 256 == 0
+    ws = P(1 << 44)
+    assert L.tern_layer_bwd_dw(a, 3, T, BF16, None, need, s) == WORKSPACE
+    assert L.tern_layer_bwd_dw(a, 3, T, BF16, ws, need - 1, s) == WORKSPACE
+    assert L.tern_layer_bwd_dw(a, 3, T, BF16, P(a[0].X), need, s) == ALIAS   # workspace over an input
+    b = _projs(3, shapes)
+    b[1].sgrad = None
+    assert L.tern_layer_bwd_dw(b, 3, T, BF16, ws, need, s) == NULL
+    # materialize: theta, shared handles
+    assert L.tern_layer_materialize(a, 3, 0, s) == THETA
+    b = _projs(3, shapes)
+    b[1].tern_packed = b[0].tern_packed
+    assert L.tern_layer_materialize(b, 3, 2, s) == ALIAS
+    assert L.tern_layer_bwd_dw_workspace_bytes(a, 0, T) == 0
+
+
+def test_layer_workspace_covers_either_type(L):
+    """The layer workspace covers the grouped plan (bf16) and the per-projection
+    plans (fp32), and is at least the sum of the sgrad partial tables."""
+    for T, shapes in ((2048, [(512, 512)] * 4 + [(512, 2048), (2048, 512)]),
+                      (16384, [(2048, 2048)] * 4 + [(2048, 8192), (8192, 2048)]),
+                      (1000, [(64, 1024), (1024, 40), (256, 256)])):
+        a = _projs(len(shapes), shapes)
+        need = L.tern_layer_bwd_dw_workspace_bytes(a, len(shapes), T)
+        single = sum(tl.tern_linear_bwd_workspace_bytes(T, i, o) for i, o in shapes)
+        assert need >= min(single, sum(4 * o for _, o in shapes)), (T, need, single)
+        assert tl.tern_layer_bwd_dw_workspace_bytes(shapes, T) == need
+
