@@ -3,13 +3,15 @@
     python -m ternary_weight_linear_tern_amd.rocprof_summary stats  <kernel_stats.csv> [title]
     python -m ternary_weight_linear_tern_amd.rocprof_summary counters <counter_collection.csv> [title]
     python -m ternary_weight_linear_tern_amd.rocprof_summary ratios <counter_collection.csv> [title]
-    python -m ternary_weight_linear_tern_amd.rocprof_summary traffic <fetch_counter_collection.csv> \\
+    python -m ternary_weight_linear_tern_amd.rocprof_summary l2 <counter_collection.csv> [title]
+    python -m ternary_weight_linear_tern_amd.rocprof_summary traffic <reqsize_counter_collection.csv> \\
         <write_counter_collection.csv> <workload> <dispatch_steps> [sources ...]
 
-`traffic` attributes FETCH_SIZE / WRITE_SIZE (KiB per dispatch) to the library's
-entry points, scales both by what the same counters read for the calibration
+`traffic` attributes the read bytes (from TCC_EA0_RDREQ_{32B,64B,128B}) and
+WRITE_SIZE to the library's entry points, checks both against the calibration
 copy (bench.py --copy-calibration: 1 GiB read + 1 GiB written by one
-elementwise multiply-by-one kernel per copy), divides by the number of profiled steps, and writes
+elementwise multiply-by-one kernel per copy) and scales by it, divides by the
+number of profiled steps, and writes
 profiles/traffic_counters.json, which bench.py reports as roofline.traffic
 while the code of the kernels and of the planner (which sets their launch
 shapes) is unchanged.
@@ -34,9 +36,11 @@ def kernel_code_hash(*paths: str) -> str:
     given) with their comments and blank lines removed and each line's
     surrounding whitespace stripped, so that the hash names the code whose
     counters were taken, not its comments.  Without paths: the kernels and
-    the planner that sets their launch shapes (tile, split-K, reduce rows)."""
+    the planner and the layer calls that set their launch shapes (tile,
+    split-K, reduce rows, item walk)."""
     if not paths:
-        paths = tuple(os.path.join(PKG, "csrc", f) for f in ("tern_kernels.hip", "tern_plan.h", "tern_plan.cpp"))
+        paths = tuple(os.path.join(PKG, "csrc", f)
+                      for f in ("tern_kernels.hip", "tern_plan.h", "tern_plan.cpp", "tern_layer.cpp"))
     h = hashlib.sha256()
     for path in paths:
         text = open(path, encoding="utf-8").read()
@@ -87,8 +91,25 @@ def _counter_sums(path: str, counter: str):
     return per_kernel, per_kernel_n
 
 
-def traffic(fetch_csv: str, write_csv: str, workload: str, steps: int, kernel_src: str | None = None):
-    f, fn = _counter_sums(fetch_csv, "FETCH_SIZE")
+def read_kib_by_size(csv_path: str):
+    """Per kernel, the memory read bytes (KiB, summed over dispatches) from
+    the L2's read requests by size: 32 TCC_EA0_RDREQ_32B + 64 TCC_EA0_RDREQ_64B
+    + 128 TCC_EA0_RDREQ_128B.  (FETCH_SIZE weights every request that is not
+    32 bytes as 64 bytes, so it reads 128-byte requests at half their size.)"""
+    n32, cnt = _counter_sums(csv_path, "TCC_EA0_RDREQ_32B_sum")
+    n64, _ = _counter_sums(csv_path, "TCC_EA0_RDREQ_64B_sum")
+    n128, _ = _counter_sums(csv_path, "TCC_EA0_RDREQ_128B_sum")
+    out = {}
+    for k in set(n32) | set(n64) | set(n128):
+        out[k] = (32 * n32.get(k, 0.0) + 64 * n64.get(k, 0.0) + 128 * n128.get(k, 0.0)) / 1024.0
+    return out, cnt
+
+
+def traffic(read_csv: str, write_csv: str, workload: str, steps: int, kernel_src: str | None = None):
+    """HBM bytes per step of each entry point: reads from the request sizes
+    (read_kib_by_size), writes from WRITE_SIZE, each checked against the 1 GiB
+    calibration copies (and scaled by what they read, should it not be 1)."""
+    f, fn = read_kib_by_size(read_csv)
     w, wn = _counter_sums(write_csv, "WRITE_SIZE")
     copy_f = [v / fn[k] for k, v in f.items() if "MulFunctor" in k]
     copy_w = [v / wn[k] for k, v in w.items() if "MulFunctor" in k]
@@ -97,8 +118,9 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, steps: int, kernel_sr
     wscale = COPY_KIB / max(copy_w) if copy_w else 1.0
     ent = defaultdict(lambda: {"fetch_kib": 0.0, "write_kib": 0.0})
     lines = [f"# HBM traffic per step, {workload} ({steps} profiled steps)", "",
-             f"calibration: 1 GiB copy reads FETCH_SIZE x {fscale:.4f}, WRITE_SIZE x {wscale:.4f}", "",
-             "| kernel | dispatches | FETCH KiB/dispatch | WRITE KiB/dispatch |", "|---|---|---|---|"]
+             f"calibration: a 1 GiB copy reads {1 / fscale:.4f} GiB by request sizes and writes "
+             f"{1 / wscale:.4f} GiB by WRITE_SIZE; scale factors {fscale:.4f} / {wscale:.4f}", "",
+             "| kernel | dispatches | read KiB/dispatch | WRITE KiB/dispatch |", "|---|---|---|---|"]
     for k in sorted(set(f) | set(w)):
         lines.append(f"| {k[:80]} | {fn.get(k, 0)} | {f.get(k, 0)/max(fn.get(k, 1),1):.0f} | "
                      f"{w.get(k, 0)/max(wn.get(k, 1),1):.0f} |")
@@ -118,6 +140,24 @@ def traffic(fetch_csv: str, write_csv: str, workload: str, steps: int, kernel_sr
                                              "bytes_per_step": rd + wr}
         lines.append(f"| {e} | {rd/1e6:.1f} | {wr/1e6:.1f} |")
     return out, "\n".join(lines)
+
+
+def l2(path: str, title: str = "") -> str:
+    """Per kernel, over its dispatches: the L2 hit rate (TCC_HIT / (TCC_HIT +
+    TCC_MISS)) and the mean L1-to-L2 read latency in cycles
+    (TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ)."""
+    tot = defaultdict(lambda: defaultdict(float))
+    for r in csv.DictReader(open(path)):
+        tot[r["Kernel_Name"]][r["Counter_Name"]] += float(r["Counter_Value"])
+    out = [f"# {title}" if title else "# L2", "", "| kernel | L2 hit % | L1->L2 read latency (cycles) | L1->L2 reads |",
+           "|---|---|---|---|"]
+    for name, c in sorted(tot.items()):
+        h, m = c.get("TCC_HIT_sum", 0.0), c.get("TCC_MISS_sum", 0.0)
+        lat, req = c.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0), c.get("TCP_TCC_READ_REQ_sum", 0.0)
+        hit = f"{100 * h / (h + m):.1f}" if h + m else "-"
+        l = f"{lat / req:.0f}" if req else "-"
+        out.append(f"| {name[:70]} | {hit} | {l} | {req:.3g} |")
+    return "\n".join(out)
 
 
 XCDS = 8          # GRBM_GUI_ACTIVE is reported summed over the 8 XCD instances
@@ -197,11 +237,13 @@ if __name__ == "__main__":
         print(stats(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
     elif cmd == "ratios":
         print(ratios(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
+    elif cmd == "l2":
+        print(l2(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
     elif cmd == "counters":
         print(counters(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
     elif cmd == "traffic":
         src = sys.argv[6:] if len(sys.argv) > 6 else \
-            [os.path.join(PKG, "csrc", f) for f in ("tern_kernels.hip", "tern_plan.h", "tern_plan.cpp")]
+            [os.path.join(PKG, "csrc", f) for f in ("tern_kernels.hip", "tern_plan.h", "tern_plan.cpp", "tern_layer.cpp")]
         data, text = traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), src)
         print(text)
         dst = os.path.join(ROOT, "profiles", "traffic_counters.json")
