@@ -49,9 +49,12 @@ def parse():
     ap.add_argument("--streams", default="auto", choices=["auto", "1", "2", "3", "p3"],
                     help="graph branches of the recorded step: 1 = one chain; 2 = dW on its own branch; 3 = dX "
                          "and dW each on their own branch (after the materialize); p3 (single-projection "
-                         "calls only) = whole projections dealt over three branches; auto = 3 (layer calls) or "
-                         "p3 (single calls) when some projection's forward or dX has fewer 256 x 256 tiles "
-                         "than the GPU has compute units (small products, whose latencies then overlap), "
+                         "calls only) = whole projections dealt over three branches; auto: layer calls take 3 "
+                         "when the forward or dX product of the layer has fewer 256 x 256 tiles than the GPU "
+                         "has compute units (small products, whose latencies then overlap), 1 when those tiles "
+                         "do not divide evenly over the compute units (the planner balances such a product "
+                         "over all units, which a concurrent product would disturb), else 2; single calls "
+                         "take p3 when some projection's forward or dX has fewer tiles than compute units, "
                          "else 2")
     ap.add_argument("--api", default="layer", choices=["layer", "projection"],
                     help="layer (default): one call per product for all projections (tern_layer_*); "
@@ -203,6 +206,16 @@ def extras(a):
                       "launch": "eager", "entries": out}), flush=True)
 
 
+def ready_events(events, stream):
+    """Record every timing event once before a timed region: torch creates
+    the device event at its first record, and a creation that stalls the host
+    inside the region would count as GPU time of the part being enqueued."""
+    import torch
+    for e in events:
+        e.record(stream)
+    torch.cuda.synchronize()
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -298,12 +311,21 @@ def main():
     # timed region: events on the stream every kernel is launched on
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in projs] for _ in range(a.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(a.steps):
-        step(evs[k])
-    end.record(stream)
-    torch.cuda.synchronize()
+    ready_events([e for k in evs for j in k for e in j] + [start, end], stream)
+
+    def eager_region():
+        start.record(stream)
+        for k in range(a.steps):
+            step(evs[k])
+        end.record(stream)
+        torch.cuda.synchronize()
+
+    # The region runs twice and the second is kept: the first launches of a
+    # run that queues this many dispatches and events ahead of the GPU have
+    # stalled the host for 30-40 ms once (inside the second step, whatever
+    # the workload), which is runtime set-up, not the kernels' time.
+    eager_region()
+    eager_region()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / a.steps
 
@@ -381,8 +403,12 @@ def main():
     if a.streams == "auto":
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         tiles = lambda m, n: -(-m // 256) * -(-n // 256)
-        small = any(min(tiles(d["n_out"], w.T), tiles(d["n_in"], w.T)) < cus for d in projs)
-        mode = ("3" if small else "2") if layer else ("p3" if small else "2")
+        if layer:
+            items = (sum(tiles(d["n_out"], w.T) for d in projs), sum(tiles(d["n_in"], w.T) for d in projs))
+            mode = "3" if min(items) < cus else ("1" if any(i % cus for i in items) else "2")
+        else:
+            small = any(min(tiles(d["n_out"], w.T), tiles(d["n_in"], w.T)) < cus for d in projs)
+            mode = "p3" if small else "2"
     else:
         mode = a.streams
         if layer and mode.startswith("p"):
@@ -410,6 +436,7 @@ def main():
             g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(a.steps)]
+            ready_events([g0, g1] + [e for pair in rev for e in pair], gs)
             g0.record(gs)
             for k in range(a.steps):
                 rev[k][0].record(gs)

@@ -720,40 +720,9 @@ __device__ __forceinline__ void wait_vm0() {
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Persistent walk over the items of a group of problems: workgroup b, round j
-// -> logical item L (consecutive items go to one XCD), then its problem (the
-// one whose items start at or before L), its split and its tile, grouped 8
-// tiles along M within the problem so that the tiles resident on one XCD
-// share operand panels in its L2.
+// Item j of this workgroup in the walk of a group of problems (group_item).
 __device__ __forceinline__ bool g_item(const GroupArgs &ga, int j, int &pi, int &tm, int &tn, int &sp) {
-    const int G = gridDim.x, b = blockIdx.x;
-    int L;
-    if (ga.dyn) {
-        // one item per workgroup; within each full run of 256 consecutive
-        // workgroups (dispatched together, round-robin over the XCDs) the
-        // items of one XCD are consecutive
-        const int base = b & ~255, c = b & 255;
-        L = j * G + base + (base + 256 <= G ? (c & 7) * 32 + (c >> 3) : c);
-    } else {
-        L = (G & 7) == 0 ? j * G + (b & 7) * (G >> 3) + (b >> 3) : j * G + b;
-    }
-    if (L >= ga.start[ga.n]) return false;
-    int p = 0;
-    while (p + 1 < ga.n && L >= ga.start[p + 1]) p++;
-    pi = p;
-    const int tiles_m = ga.p[p].tiles_m, tiles_n = ga.p[p].tiles_n;
-    const int tiles = tiles_m * tiles_n;
-    const int local = L - ga.start[p];
-    sp = local / tiles;
-    const int t = local - sp * tiles;
-    constexpr int GM = 8;
-    const int group = t / (GM * tiles_n);
-    const int first = group * GM;
-    const int gs = min(tiles_m - first, GM);
-    const int within = t - group * GM * tiles_n;
-    tm = first + within % gs;
-    tn = within / gs;
-    return true;
+    return group_item(ga, (int)gridDim.x, (int)blockIdx.x, j, pi, tm, tn, sp);
 }
 
 // DMA of one chunk of a token-major operand: W_KC token rows x 256 features
@@ -1941,12 +1910,11 @@ int device_cus() {
     return cache[dev];
 }
 
+// grid: from plan_group_walk (the walk's workgroups)
 template <int MODE>
-hipError_t launch_persistent(const GroupArgs &ga, hipStream_t st) {
-    const int64_t items = ga.start[ga.n];
-    if (items <= 0) return hipSuccess;
-    const int64_t cus = device_cus();
-    const dim3 pgrid((unsigned)(ga.dyn ? items : (items < cus ? items : cus))), block(dev::NT);
+hipError_t launch_persistent(const GroupArgs &ga, int64_t grid, hipStream_t st) {
+    if (grid <= 0) return hipSuccess;
+    const dim3 pgrid((unsigned)grid), block(dev::NT);
     if constexpr (MODE == MODE_DW)
         hipLaunchKernelGGL(dev::gemm_dw_kernel, pgrid, block, 0, st, ga);
     else if (MODE == MODE_DX && ga.p[0].acc)
@@ -1971,7 +1939,8 @@ hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
             ga.start[0] = 0;
             ga.start[1] = (int)(p.tiles_m * p.tiles_n * p.splits);
             ga.p[0] = a;
-            return launch_persistent<MODE>(ga, st);
+            const int64_t items = ga.start[1], cus = device_cus();
+            return launch_persistent<MODE>(ga, items < cus ? items : cus, st);
         }
     }
     switch (p.tile) {
@@ -1989,10 +1958,10 @@ hipError_t launch_gemm_group(int mode, const GroupArgs &ga_in, hipStream_t st) {
     int64_t cost[kMaxGroup];
     for (int p = 0; p < ga.n; p++)
         cost[p] = mode == MODE_DW ? cdiv(ga.p[p].kps, dev::W_KC) : (int64_t)ga.p[p].nch;
-    ga.dyn = group_dynamic(ga, cost, device_cus()) ? 1 : 0;
-    if (mode == MODE_FWD) return launch_persistent<MODE_FWD>(ga, st);
-    if (mode == MODE_DX) return launch_persistent<MODE_DX>(ga, st);
-    return launch_persistent<MODE_DW>(ga, st);
+    const int64_t grid = plan_group_walk(ga, cost, device_cus());
+    if (mode == MODE_FWD) return launch_persistent<MODE_FWD>(ga, grid, st);
+    if (mode == MODE_DX) return launch_persistent<MODE_DX>(ga, grid, st);
+    return launch_persistent<MODE_DW>(ga, grid, st);
 }
 
 hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStream_t st) {

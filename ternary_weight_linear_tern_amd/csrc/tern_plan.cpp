@@ -135,12 +135,12 @@ int64_t plan_layer_dw_splits(int64_t T, int64_t tiles, int64_t sum_in_out, bool 
     return best_kps;
 }
 
-bool group_dynamic(const GroupArgs &ga, const int64_t *cost, int64_t cus) {
-    const int64_t items = ga.start[ga.n];
-    if (items <= cus || cus <= 0) return false;
-    // static makespan: workgroup w takes items w, w + G, w + 2G, ... (G = cus),
-    // each costing its problem's length plus about 2 chunks of prologue and
-    // epilogue that the persistent walk overlaps with the neighbours' work
+namespace {
+constexpr int64_t kItemOverhead = 2;   // prologue + epilogue of an item, in K steps
+}
+
+int64_t static_makespan(const GroupArgs &ga, const int64_t *cost, int64_t cus, int64_t *total_out) {
+    // workgroup w takes items w, w + G, w + 2G, ... (G = cus)
     int64_t worst = 0, total = 0;
     for (int64_t w = 0; w < cus; w++) {
         int64_t load = 0;
@@ -149,19 +149,116 @@ bool group_dynamic(const GroupArgs &ga, const int64_t *cost, int64_t cus) {
             // k with s0 <= w + k G < s1
             const int64_t k0 = s0 > w ? (s0 - w + cus - 1) / cus : 0;
             const int64_t k1 = s1 > w ? (s1 - w + cus - 1) / cus : 0;
-            if (k1 > k0) load += (k1 - k0) * cost[p];
+            if (k1 > k0) load += (k1 - k0) * (cost[p] + kItemOverhead);
         }
         worst = load > worst ? load : worst;
         total += load;
     }
+    if (total_out) *total_out = total;
+    return worst;
+}
+
+bool plan_classes(GroupArgs &ga, const int64_t *cost, int64_t cus, int64_t &makespan) {
+    struct Cls {
+        int64_t nwg, load;
+        int cnt[kMaxGroup];
+    };
+    Cls c[kMaxClass] = {};
+    int nc = 1;
+    c[0].nwg = cus;
+    // problems longest items first (stable), each item onto a least loaded
+    // workgroup; the workgroups of a class share their history, so a class
+    // whose turn takes fewer items than it has workgroups splits in two (the
+    // ones that took an item first)
+    int order[kMaxGroup];
+    for (int p = 0; p < ga.n; p++) order[p] = p;
+    for (int i = 1; i < ga.n; i++)
+        for (int j = i; j > 0 && cost[order[j]] > cost[order[j - 1]]; j--) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    for (int oi = 0; oi < ga.n; oi++) {
+        const int p = order[oi];
+        const int64_t len = cost[p] + kItemOverhead;
+        int64_t left = (int64_t)ga.start[p + 1] - ga.start[p];
+        while (left > 0) {
+            int k = 0;
+            for (int i = 1; i < nc; i++)
+                if (c[i].load < c[k].load) k = i;
+            if (left >= c[k].nwg) {
+                // every workgroup of the class takes one more item (in bulk
+                // while the class stays the least loaded)
+                int64_t rounds = left / c[k].nwg;
+                int64_t next = -1;   // the lowest load of the other classes
+                for (int i = 0; i < nc; i++)
+                    if (i != k && (next < 0 || c[i].load < next)) next = c[i].load;
+                if (next >= 0) {
+                    // rounds after which this class is no longer below `next`
+                    const int64_t r_max = (next - c[k].load) / len + 1;
+                    rounds = rounds < r_max ? rounds : r_max;
+                }
+                c[k].cnt[p] += (int)rounds;
+                c[k].load += rounds * len;
+                left -= rounds * c[k].nwg;
+            } else {
+                if (nc == kMaxClass) return false;
+                for (int i = nc; i > k; i--) c[i] = c[i - 1];
+                nc++;
+                c[k].nwg = left;
+                c[k].cnt[p] += 1;
+                c[k].load += len;
+                c[k + 1].nwg -= left;
+                left = 0;
+            }
+        }
+    }
+    makespan = 0;
+    int64_t wg = 0;
+    int base[kMaxGroup] = {};
+    ga.ncls = nc;
+    for (int k = 0; k < nc; k++) {
+        makespan = c[k].load > makespan ? c[k].load : makespan;
+        ga.cls_wg[k] = (int)wg;
+        for (int p = 0; p < ga.n; p++) {
+            ga.cls_cnt[k][p] = c[k].cnt[p];
+            ga.cls_base[k][p] = base[p];
+            base[p] += (int)(c[k].nwg * c[k].cnt[p]);
+        }
+        wg += c[k].nwg;
+    }
+    ga.cls_wg[nc] = (int)wg;
+    return true;
+}
+
+int64_t plan_group_walk(GroupArgs &ga, const int64_t *cost, int64_t cus) {
+    const int64_t items = ga.start[ga.n];
+    ga.walk = WALK_STATIC;
+    ga.ncls = 0;
+    if (items <= 0) return 0;
+    if (cus <= 0) cus = 1;
+    if (items <= cus) return items;   // one item per workgroup
+    int64_t total = 0;
+    const int64_t worst = static_makespan(ga, cost, cus, &total);
+    GroupArgs trial = ga;
+    int64_t cls = 0;
+    if (plan_classes(trial, cost, cus, cls) && cls < worst) {
+        ga = trial;
+        ga.walk = WALK_CLASSES;
+        return ga.cls_wg[ga.ncls];
+    }
     // one workgroup per item, longest first, each started as a unit frees up
     // (list scheduling): about the average load, or the longest item; the
-    // prologue and epilogue of every item (2 chunks) are no longer hidden
+    // prologue and epilogue of every item are no longer hidden
     int64_t longest = 0;
     for (int p = 0; p < ga.n; p++) longest = cost[p] > longest ? cost[p] : longest;
-    double dyn_est = double(total) / double(cus) + 2.0 * double(items) / double(cus);
-    if (dyn_est < double(longest + 2)) dyn_est = double(longest + 2);
-    return double(worst) > 1.08 * dyn_est;
+    double dyn_est = double(total) / double(cus) + double(kItemOverhead) * double(items) / double(cus);
+    if (dyn_est < double(longest + 2 * kItemOverhead)) dyn_est = double(longest + 2 * kItemOverhead);
+    if (double(worst) > 1.08 * dyn_est) {
+        ga.walk = WALK_DYNAMIC;
+        return items;
+    }
+    return cus;
 }
 
 bool dx_exact_scale(int64_t T, int64_t in, int64_t out) {

@@ -60,24 +60,103 @@ struct GemmArgs {
     int exact_scale;         // DX, bf16: the scale as the sum of two bf16 terms (two passes over K)
 };
 
+// Host and device: the item walk below is shared by the kernels and by the
+// planner's checks.
+#if defined(__HIPCC__)
+#define TERN_HD __host__ __device__
+#else
+#define TERN_HD
+#endif
+
 // Several independent problems of one mode in one persistent launch (the
 // projections of a layer): their work items (tiles, times splits for dW) form
-// one item space, problem by problem, and every workgroup walks it.
+// one item space, problem by problem, and the grid walks it in one of three
+// ways:
+//   WALK_STATIC   persistent grid, workgroup b takes items b, b + G, b + 2G, ...
+//   WALK_DYNAMIC  one workgroup per item, in item order (the dispatcher starts
+//                 each as a unit frees up: longest first)
+//   WALK_CLASSES  persistent grid in classes of workgroups: every workgroup of
+//                 class k takes cls_cnt[k][p] items of problem p (problems in
+//                 order), the class's items of p being cls_base[k][p] +
+//                 e * (class size) + slot (e-th item of the workgroup in slot
+//                 slot of its class).  The planner fills the classes longest
+//                 items first onto the least loaded workgroups, so a layer of
+//                 mixed reduction lengths keeps every unit busy to the end
+//                 without giving up the walk's prefetch across items.
 constexpr int kMaxGroup = 8;
+constexpr int kMaxClass = 8;
+enum GroupWalk : int { WALK_STATIC = 0, WALK_DYNAMIC = 1, WALK_CLASSES = 2 };
 struct GroupArgs {
     int n;                          // problems
     int start[kMaxGroup + 1];       // first item of each problem; start[n] = all items
-    int dyn;                        // 1: one workgroup per item (grid = items), items in order
+    int walk;                       // GroupWalk
+    int ncls;                       // WALK_CLASSES: classes of workgroups
+    int cls_wg[kMaxClass + 1];      // first workgroup of each class; cls_wg[ncls] = grid
+    int cls_cnt[kMaxClass][kMaxGroup];    // items of problem p per workgroup of class k
+    int cls_base[kMaxClass][kMaxGroup];   // first item of problem p (within it) taken by class k
     GemmArgs p[kMaxGroup];
 };
 
-// Item walk of a group launch on `cus` compute units: persistent (the grid
-// walks the items round-robin, each workgroup taking every grid-th item) or,
-// when that leaves the work unbalanced, one workgroup per item in item order
-// (the dispatcher then starts each as a unit frees up: longest items first,
-// since problems are ordered by item length).  cost[p]: relative length of
-// problem p's items.  Returns true for one workgroup per item.
-bool group_dynamic(const GroupArgs &ga, const int64_t *cost, int64_t cus);
+// Item j of workgroup b of a grid of G workgroups: its problem pi, tile
+// (tm, tn) and split sp; false once the workgroup's items run out.  Consecutive
+// items of a round go to one XCD (workgroups are dispatched round-robin over
+// the 8 XCDs), and within a problem the tiles are grouped 8 along M, so the
+// tiles resident on one XCD share operand panels in its L2.
+TERN_HD inline bool group_item(const GroupArgs &ga, int G, int b, int j, int &pi, int &tm, int &tn, int &sp) {
+    int L;
+    if (ga.walk == WALK_CLASSES) {
+        int k = 0;
+        while (k + 1 < ga.ncls && b >= ga.cls_wg[k + 1]) k++;
+        const int w0 = ga.cls_wg[k], m = ga.cls_wg[k + 1] - w0, r = b - w0;
+        int p = 0, e = j;
+        while (p < ga.n && e >= ga.cls_cnt[k][p]) {
+            e -= ga.cls_cnt[k][p];
+            p++;
+        }
+        if (p >= ga.n || r >= m) return false;
+        const int slot = ((m | w0) & 7) == 0 ? (r & 7) * (m >> 3) + (r >> 3) : r;
+        L = ga.start[p] + ga.cls_base[k][p] + e * m + slot;
+    } else if (ga.walk == WALK_DYNAMIC) {
+        // one item per workgroup; within each full run of 256 consecutive
+        // workgroups (dispatched together, round-robin over the XCDs) the
+        // items of one XCD are consecutive
+        const int base = b & ~255, c = b & 255;
+        L = j * G + base + (base + 256 <= G ? (c & 7) * 32 + (c >> 3) : c);
+    } else {
+        L = (G & 7) == 0 ? j * G + (b & 7) * (G >> 3) + (b >> 3) : j * G + b;
+    }
+    if (L >= ga.start[ga.n]) return false;
+    int p = 0;
+    while (p + 1 < ga.n && L >= ga.start[p + 1]) p++;
+    pi = p;
+    const int tiles_m = ga.p[p].tiles_m, tiles_n = ga.p[p].tiles_n;
+    const int tiles = tiles_m * tiles_n;
+    const int local = L - ga.start[p];
+    sp = local / tiles;
+    const int t = local - sp * tiles;
+    constexpr int GM = 8;
+    const int group = t / (GM * tiles_n);
+    const int first = group * GM;
+    const int gs = tiles_m - first < GM ? tiles_m - first : GM;
+    const int within = t - group * GM * tiles_n;
+    tm = first + within % gs;
+    tn = within / gs;
+    return true;
+}
+
+// Chooses the walk of a group launch on `cus` compute units and fills its
+// fields; returns the grid (0 for no items).  cost[p]: length of problem p's
+// items (K steps).  Each item also pays about 2 steps of prologue and
+// epilogue, which the persistent walks overlap with the neighbours' work.
+// Static when its makespan is the best; classes when they shorten it (and fit
+// in kMaxClass); one workgroup per item when neither is balanced.
+int64_t plan_group_walk(GroupArgs &ga, const int64_t *cost, int64_t cus);
+
+// The static walk's makespan and the classes' (WALK_CLASSES fields filled in
+// ga; false when more than kMaxClass classes would be needed), in cost units
+// with the 2-step overhead per item.  Exposed for the planner's checks.
+int64_t static_makespan(const GroupArgs &ga, const int64_t *cost, int64_t cus, int64_t *total = nullptr);
+bool plan_classes(GroupArgs &ga, const int64_t *cost, int64_t cus, int64_t &makespan);
 
 // Tokens per split of the weight-gradient product shared by the problems of
 // a layer (all have K = T; the split count is cdiv(T, result)): the count

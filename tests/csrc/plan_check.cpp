@@ -3,6 +3,8 @@
 // a missing operand or output is refused for every product.  Built with g++
 // against tern_plan.cpp alone; test infrastructure only.
 #include <cstdio>
+#include <cstdlib>
+#include <vector>
 
 #include "../../include/tern.h"
 #include "../../ternary_weight_linear_tern_amd/csrc/tern_plan.h"
@@ -29,6 +31,59 @@ static GemmArgs full_args() {
     a.out_ptr = out;
     a.part = (float *)part;
     return a;
+}
+
+
+// Every walk of a group visits every item exactly once: simulate group_item
+// for all workgroups of the planned grid.  Returns the walk's makespan in cost
+// units (with the 2-step overhead per item).
+struct Prob {
+    int tiles_m, tiles_n, splits;
+    long cost;
+};
+static long check_walk(const std::vector<Prob> &ps, long cus, int *walk_out = nullptr) {
+    GroupArgs ga{};
+    ga.n = (int)ps.size();
+    long cost[kMaxGroup];
+    int total = 0;
+    for (int i = 0; i < ga.n; i++) {
+        ga.start[i] = total;
+        ga.p[i].tiles_m = ps[i].tiles_m;
+        ga.p[i].tiles_n = ps[i].tiles_n;
+        ga.p[i].splits = ps[i].splits;
+        cost[i] = ps[i].cost;
+        total += ps[i].tiles_m * ps[i].tiles_n * ps[i].splits;
+    }
+    ga.start[ga.n] = total;
+    int64_t cost64[kMaxGroup];
+    for (int i = 0; i < ga.n; i++) cost64[i] = cost[i];
+    const int64_t stat = static_makespan(ga, cost64, cus);
+    const int64_t grid = plan_group_walk(ga, cost64, cus);
+    if (walk_out) *walk_out = ga.walk;
+    CHECK(grid > 0 && grid <= (total > cus && ga.walk != WALK_DYNAMIC ? cus : total));
+    std::vector<int> seen(total, 0);
+    long worst = 0;
+    for (int b = 0; b < grid; b++) {
+        long load = 0;
+        for (int j = 0;; j++) {
+            int pi = -1, tm = -1, tn = -1, sp = -1;
+            if (!group_item(ga, (int)grid, b, j, pi, tm, tn, sp)) break;
+            CHECK(pi >= 0 && pi < ga.n);
+            if (pi < 0 || pi >= ga.n) break;
+            const Prob &q = ps[pi];
+            CHECK(tm >= 0 && tm < q.tiles_m && tn >= 0 && tn < q.tiles_n && sp >= 0 && sp < q.splits);
+            if (!(tm >= 0 && tm < q.tiles_m && tn >= 0 && tn < q.tiles_n && sp >= 0 && sp < q.splits)) break;
+            seen[ga.start[pi] + (sp * q.tiles_n + tn) * q.tiles_m + tm]++;
+            load += q.cost + 2;
+            CHECK(j <= total);
+            if (j > total) break;
+        }
+        worst = load > worst ? load : worst;
+    }
+    for (int i = 0; i < total; i++) CHECK(seen[i] == 1);
+    if (ga.walk == WALK_CLASSES) CHECK(worst < stat);
+    if (ga.walk == WALK_STATIC && total > cus) CHECK(worst == stat);
+    return worst;
 }
 
 int main() {
@@ -91,6 +146,35 @@ int main() {
         CHECK(plan_bwd(s[0], s[1], s[2], true).total <= w && plan_bwd(s[0], s[1], s[2], false).total <= w);
         const size_t wa = bwd_workspace_bytes(s[0], s[1], s[2], true);
         CHECK(plan_bwd(s[0], s[1], s[2], true, true).total <= wa);
+    }
+    // item walks: a layer of mixed reduction lengths (d = 1024, ffn 4096,
+    // 8192 tokens: forward items of 128 and 32 chunks) takes the classes and
+    // reaches the balanced makespan; uniform layers stay static; random
+    // groups cover every walk
+    {
+        int walk = -1;
+        const long mid = check_walk({{4, 32, 1, 128}, {16, 32, 1, 32}, {4, 32, 1, 32}, {4, 32, 1, 32},
+                                     {4, 32, 1, 32}, {4, 32, 1, 32}}, 256, &walk);
+        CHECK(walk == WALK_CLASSES);
+        CHECK(mid == 204);
+        check_walk({{8, 64, 1, 256}, {32, 64, 1, 64}, {8, 64, 1, 64}, {8, 64, 1, 64}, {8, 64, 1, 64},
+                    {8, 64, 1, 64}}, 256, &walk);
+        CHECK(walk == WALK_STATIC);
+        check_walk({{4, 4, 1, 128}, {16, 4, 1, 128}}, 256, &walk);   // fewer items than units
+        CHECK(walk == WALK_STATIC);
+        std::srand(12345);
+        int walks[3] = {0, 0, 0};
+        for (int it = 0; it < 3000; it++) {
+            std::vector<Prob> ps;
+            const int n = 1 + std::rand() % kMaxGroup;
+            for (int i = 0; i < n; i++)
+                ps.push_back({1 + std::rand() % 40, 1 + std::rand() % 40, 1 + std::rand() % 3, 1 + std::rand() % 300});
+            const long cus_opts[] = {1, 7, 8, 80, 256, 304};
+            check_walk(ps, cus_opts[std::rand() % 6], &walk);
+            if (walk >= 0 && walk < 3) walks[walk]++;
+        }
+        CHECK(walks[WALK_STATIC] > 0 && walks[WALK_DYNAMIC] + walks[WALK_CLASSES] > 0 && walks[WALK_CLASSES] > 0);
+        std::printf("walks over random groups: static %d, dynamic %d, classes %d\n", walks[0], walks[1], walks[2]);
     }
     if (fails) {
         std::fprintf(stderr, "%d checks failed\n", fails);
