@@ -1309,11 +1309,15 @@ __device__ __forceinline__ uint32_t r_scaled_pair(uint32_t v, uint32_t q) {
     return (v ^ q) & __builtin_amdgcn_perm(0u, 0u, v);
 }
 
-template <int MODE, bool ACC = false>
+// YBF: bf16 Y (forward only; every problem of a launch has the same Y type)
+template <int MODE, bool ACC = false, bool YBF = false>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_rd_kernel(GroupArgs ga) {
     static_assert(MODE == MODE_FWD || MODE == MODE_DX, "forward and dX only");
     static_assert(!ACC || MODE == MODE_DX, "accumulation is a dX variant");
+    static_assert(!YBF || MODE == MODE_FWD, "bf16 output is a forward variant");
+    // operands swapped in the MFMAs (transposed accumulators, epilogue below)
+    constexpr bool SWAP = !ACC;
     constexpr int ES = 2;
     // vector memory operations per chunk issue: 8 activation + 1 fragment (+ 1 scale)
     constexpr int OPS = MODE == MODE_DX ? 10 : 9;
@@ -1489,67 +1493,80 @@ void gemm_rd_kernel(GroupArgs ga) {
 
     int sc = 0;   // LDS stage of the current chunk
 
-    // Epilogue of tile (ctm, ctn): 64 buffer stores per wave whatever the edges
+    // Epilogue of tile (ctm, ctn).  Every store is issued whatever the edges
     // (out-of-range stores get an out-of-range offset), so the vmcnt arithmetic
-    // of the main loop holds.  ACC (dX += ...): each store's 16 bytes of old
-    // values are loaded first (out-of-range offsets read zero; the compiler
-    // waits for them before the add, so they are done when the epilogue ends
-    // and the main loop's waits still count at most 64 stores).  bf16 Y
-    // stores straight from the MFMA layout: lane offsets cover the 4 columns n
-    // of the lane, the row block m goes in the scalar offset; M is a multiple
-    // of 8 and the 8-row groups are wave-uniform, so the m test is scalar.
+    // of the main loop holds; it counts at most 63, and any larger number of
+    // stores issued after a chunk's loads only makes its wait stricter.
+    //
+    // The forward and the plain dX run the MFMAs with the operands swapped
+    // (activations as A, ternary as B), which leaves the tile transposed in
+    // the accumulators: acc[fm][fn][i] is the output at token n = nw + 32 fn +
+    // 8 (i / 4) + 4 h + i % 4 and column m = mw + 32 fm + l32 (same products,
+    // same sums).  Then the 32 lanes of each half-wave hold 32 consecutive
+    // columns of one token row, and one 4-byte store per element writes whole
+    // 128-byte lines (two per instruction) straight from the registers:
+    // 256 stores per wave, no LDS round trip.  They carry the non-temporal
+    // hint (whole lines, read by a later kernel, so they need not displace the
+    // operand panels in L2).  bf16 Y: 2-byte stores, 64-byte halves of lines.
     auto epilogue = [&]() __attribute__((always_inline)) {
         const GemmArgs &g = ga.p[cpi];
         const int mw = ctm * 256 + wm * 128, nw = ctn * 256 + wn * 128;
         const int ldo = MODE == MODE_FWD ? g.out : g.in;
-        const bool obf = MODE == MODE_FWD && g.y_bf16;
+        constexpr bool obf = YBF;
         const int esz = obf ? 2 : 4;
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc((const char *)g.out_ptr + ((int64_t)nw * ldo + mw) * esz);
-        uint32_t vo[4];
-#pragma unroll
-        for (int fn = 0; fn < 4; fn++) {
-            const int nl = fn * 32 + l32;
-            vo[fn] = nw + nl < g.N ? (uint32_t)((nl * ldo + 4 * h) * esz) : OOB;
-        }
-        const float *esc = (const float *)(wl + R_NST * R_STAGE + (cj & 3) * 512) + 4 * h;
-        auto rows = [&](auto obf_c) __attribute__((always_inline)) {
-            constexpr bool OBF = decltype(obf_c)::value;
+        const float *esc = (const float *)(wl + R_NST * R_STAGE + (cj & 3) * 512);
+        // Each lane's column test and scale once per 32-column group fm; the
+        // row offsets (rows of ldo elements) in the scalar offset, computed
+        // per 32-row group fn from a row pitch the compiler cannot see through
+        // (an empty asm), so that it does not hoist all 64 of them at once.
+        auto rows_s = [&]() __attribute__((always_inline)) {
+            constexpr int EB = YBF ? 2 : 4;
+            float scl[4];
+            uint32_t vcol[4];
+            const uint32_t vb = (uint32_t)((4 * h * ldo + l32) * EB);
 #pragma unroll
             for (int fm = 0; fm < 4; fm++) {
-                // the four q pieces of each 128-byte row segment go out back to back
-                f32x4 scq[4];
-                bool mokq[4];
+                scl[fm] = MODE == MODE_FWD ? esc[fm * 32 + l32] : 1.0f;
+                vcol[fm] = mw + fm * 32 + l32 < g.M ? vb + (uint32_t)(fm * 32 * EB) : OOB;
+            }
+            const int rlim = g.N - nw - 4 * h;   // rows of this lane below N
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const int ml = fm * 32 + 8 * q;
-                    scq[q] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
-                    if constexpr (MODE == MODE_FWD) scq[q] = *(const f32x4 *)(esc + ml);
-                    mokq[q] = mw + ml < g.M;
-                }
+            for (int fn = 0; fn < 4; fn++) {
+                int pitch = ldo * EB;
+                asm volatile("" : "+s"(pitch) : : "memory");
 #pragma unroll
-                for (int fn = 0; fn < 4; fn++) {
+                for (int i = 0; i < 16; i++) {
+                    const int row = fn * 32 + 8 * (i >> 2) + (i & 3);   // less the lane's 4 h
+                    const int so = row * pitch;
+                    const bool rok = row < rlim;
 #pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const int so = (fm * 32 + 8 * q) * esz;
-                        f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
-                                   acc[fm][fn][4 * q + 3]};
-                        if constexpr (MODE == MODE_FWD) v = v * scq[q];
-                        const uint32_t off = mokq[q] ? vo[fn] : OOB;
-                        if constexpr (OBF) {
-                            const f32x2 a2 = {v.x, v.y}, b2 = {v.z, v.w};
-                            const u32x2 pk = {__builtin_bit_cast(uint32_t, __builtin_convertvector(a2, bf16x2)),
-                                              __builtin_bit_cast(uint32_t, __builtin_convertvector(b2, bf16x2))};
-                            __builtin_amdgcn_raw_buffer_store_b64(pk, ro, off, so, 0);
+                    for (int fm = 0; fm < 4; fm++) {
+                        const uint32_t off = rok ? vcol[fm] : OOB;
+                        float v = acc[fm][fn][i];
+                        if constexpr (MODE == MODE_FWD) {
+                            // read the accumulator out of its AGPR here: with
+                            // a VALU use in sight the allocator would move
+                            // accumulators into VGPRs for the whole loop
+                            float x;
+                            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(v));
+                            v = x * scl[fm];
+                        }
+                        if constexpr (YBF) {
+                            const f32x2 v2 = {v, 0.0f};
+                            const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2));
+                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w & 0xFFFFu), ro, off, so, 2);
                         } else {
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off, so, 0);
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro, off, so, 2);
                         }
                     }
                 }
             }
         };
 
-        // fp32 (ACC: with the old values added): each 32-row x 64-column piece of the
+        // The accumulating dX (operands in the usual order, the old values
+        // added): each 32-row x 64-column piece of the
         // wave's block passes through the LDS stage the last chunk consumed
         // (free until the next chunk's first issue), transposed so that every
         // store writes 4 rows x 256 contiguous bytes (whole 128-byte lines)
@@ -1592,7 +1609,6 @@ void gemm_rd_kernel(GroupArgs ga) {
                         for (int q = 0; q < 4; q++) {
                             f32x4 v = {acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
                                        acc[fm][fn][4 * q + 3]};
-                            if constexpr (MODE == MODE_FWD) v = v * *(const f32x4 *)(esc + fm * 32 + 8 * q);
                             const int slot = (8 * f2 + 2 * q + h) ^ (l32 & 15);
                             *(f32x4 *)(eb + l32 * 256 + slot * 16) = v;
                         }
@@ -1618,8 +1634,11 @@ void gemm_rd_kernel(GroupArgs ga) {
             }
         };
 
-        if (obf) rows(std::true_type{});
-        else rows_t();
+        if constexpr (SWAP) {
+            rows_s();
+        } else {
+            rows_t();
+        }
     };
 
     using I0 = std::integral_constant<int, 0>;
@@ -1649,8 +1668,8 @@ void gemm_rd_kernel(GroupArgs ga) {
             if (f == 4) {
                 // loads issued after the next chunk's: the chunk two ahead
                 // (OPS) and the 8 activation loads of the one three ahead, plus
-                // 64 epilogue stores in a tile's first two chunks (where 63
-                // waits for more than needed)
+                // the epilogue's stores (at least 64) in a tile's first two
+                // chunks (where 63 waits for more than needed)
                 wait_vm<63>();
                 if (!hist) wait_vm<OPS + 8>();
                 read_ahead((sc + 1) & 3, std::integral_constant<int, SL1>{});
@@ -1662,9 +1681,12 @@ void gemm_rd_kernel(GroupArgs ga) {
             u32x4 anx;
 #pragma unroll
             for (int fn = 0; fn < 4; fn++) {
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, acur), __builtin_bit_cast(bf16x8, f < 4 ? fb0[SL][fn] : fb1[fn]),
-                    acc[fm][fn], 0, 0, 0);
+                const bf16x8 xa = __builtin_bit_cast(bf16x8, f < 4 ? fb0[SL][fn] : fb1[fn]);
+                const bf16x8 xt = __builtin_bit_cast(bf16x8, acur);
+                if constexpr (SWAP)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, xt, acc[fm][fn], 0, 0, 0);
+                else
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xt, xa, acc[fm][fn], 0, 0, 0);
                 anx[fn] = f < 7 ? dec(fa[SL], p4[SL], f + 1, fn) : dec(fa[SL1], p4[SL1], 0, fn);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, DEC_OPS, 0);  // then the decode
@@ -1919,6 +1941,8 @@ hipError_t launch_persistent(const GroupArgs &ga, int64_t grid, hipStream_t st) 
         hipLaunchKernelGGL(dev::gemm_dw_kernel, pgrid, block, 0, st, ga);
     else if (MODE == MODE_DX && ga.p[0].acc)
         hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE_DX, true>), pgrid, block, 0, st, ga);
+    else if (MODE == MODE_FWD && ga.p[0].y_bf16)
+        hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE_FWD, false, true>), pgrid, block, 0, st, ga);
     else
         hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE>), pgrid, block, 0, st, ga);
     return hipGetLastError();
