@@ -1523,6 +1523,11 @@ void gemm_rd_kernel(GroupArgs ga) {
         // (an empty asm), so that it does not hoist all 64 of them at once.
         auto rows_s = [&]() __attribute__((always_inline)) {
             constexpr int EB = YBF ? 2 : 4;
+            // every load issued so far (the next tile's first three chunks and
+            // its scales) has landed before the first store: vmcnt counts in
+            // issue order, and the next two chunks then need no wait behind
+            // the 256 stores
+            wait_vm<0>();
             float scl[4];
             uint32_t vcol[4];
             const uint32_t vb = (uint32_t)((4 * h * ldo + l32) * EB);
@@ -1667,11 +1672,17 @@ void gemm_rd_kernel(GroupArgs ga) {
             }
             if (f == 4) {
                 // loads issued after the next chunk's: the chunk two ahead
-                // (OPS) and the 8 activation loads of the one three ahead, plus
-                // the epilogue's stores (at least 64) in a tile's first two
-                // chunks (where 63 waits for more than needed)
-                wait_vm<63>();
-                if (!hist) wait_vm<OPS + 8>();
+                // (OPS) and the 8 activation loads of the one three ahead.  In
+                // a tile's first two chunks: SWAP, none (the epilogue waited
+                // for every load before its stores, so those chunks' data is
+                // in LDS and the stores can drain meanwhile); otherwise its 64
+                // stores as well (where 63 waits for more than needed).
+                if constexpr (SWAP) {
+                    if (!hist) wait_vm<OPS + 8>();
+                } else {
+                    wait_vm<63>();
+                    if (!hist) wait_vm<OPS + 8>();
+                }
                 read_ahead((sc + 1) & 3, std::integral_constant<int, SL1>{});
                 __builtin_amdgcn_sched_barrier(0);
                 issue_part(sis, std::integral_constant<int, 4>{});
