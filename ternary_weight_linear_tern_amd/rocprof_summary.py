@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 output for the profiles/ folder.
 
     python -m ternary_weight_linear_tern_amd.rocprof_summary stats  <kernel_stats.csv> [title]
+    python -m ternary_weight_linear_tern_amd.rocprof_summary timed  <kernel_trace.csv> <last> [title]
     python -m ternary_weight_linear_tern_amd.rocprof_summary counters <counter_collection.csv> [title]
     python -m ternary_weight_linear_tern_amd.rocprof_summary ratios <counter_collection.csv> [title]
     python -m ternary_weight_linear_tern_amd.rocprof_summary l2 <counter_collection.csv> [title]
@@ -142,6 +143,25 @@ def traffic(read_csv: str, write_csv: str, workload: str, steps: int, kernel_src
     return out, "\n".join(lines)
 
 
+def timed(trace_csv: str, last: int, title: str = "") -> str:
+    """Per kernel, the mean duration of its last `last` dispatches in a
+    --kernel-trace CSV: the dispatches of the region bench.py keeps (its
+    eager region runs twice and reports the second), which are the ones its
+    events time, without the warm-up and first-region dispatches that the
+    --stats average includes."""
+    per = defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        per[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    out = [f"# {title}" if title else "# last dispatches", "",
+           f"| kernel | dispatches | mean of the last {last}, us |", "|---|---|---|"]
+    for name, ds in sorted(per.items(), key=lambda kv: -sum(e - s for s, e in kv[1])):
+        ds.sort()
+        tail = ds[-last:]
+        mean = sum(e - s for s, e in tail) / len(tail) / 1e3
+        out.append(f"| {name[:80]} | {len(ds)} | {mean:.1f} |")
+    return "\n".join(out)
+
+
 def l2(path: str, title: str = "") -> str:
     """Per kernel, over its dispatches: the L2 hit rate (TCC_HIT / (TCC_HIT +
     TCC_MISS)) and the mean L1-to-L2 read latency in cycles
@@ -235,6 +255,8 @@ if __name__ == "__main__":
     cmd = sys.argv[1]
     if cmd == "stats":
         print(stats(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
+    elif cmd == "timed":
+        print(timed(sys.argv[2], int(sys.argv[3]), sys.argv[4] if len(sys.argv) > 4 else ""))
     elif cmd == "ratios":
         print(ratios(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ""))
     elif cmd == "l2":
