@@ -10,6 +10,10 @@ against the single-projection calls and the oracle, through the C ABI.
   an empty projection) give the same results as the single calls.
 * A shared input (one X for three projections) and repeated calls (bitwise
   equal).
+* The d = 1024 block at 8192 tokens, whose forward and dX mix items of 128
+  and 32 chunks: the planner walks them in two classes of workgroups (the
+  planner check on the CPU pins that choice); the results equal the
+  single-projection calls bit for bit.
 """
 import numpy as np
 import pytest
@@ -172,3 +176,16 @@ def test_layer_empty_projection():
     _layer(projs)
     _compare(projs[:2], ref, "with empty")
     assert bool((projs[2]["Y"] == 0).all()) and bool((projs[2]["sgrad"] == 0).all())
+
+
+def test_layer_class_walk_mid_block():
+    """d = 1024, ffn 4096, 8192 tokens: four 1024 x 1024, 1024 -> 4096 and
+    4096 -> 1024.  The forward's 128 items of 4096-long reductions and 1024
+    of 1024 (dX the same) take the class-balanced walk."""
+    shapes = [(1024, 1024)] * 4 + [(1024, 4096), (4096, 1024)]
+    projs, host = _make(8192, shapes, config_id=1607)
+    ref = _single(projs)
+    _layer(projs)
+    _compare(projs, ref, "mid block")
+    _oracle_check(projs, host, "mid block", rows=12, cols=8)
+    log("  layer mid block (class walk): equal to the single calls, oracle gate met")
