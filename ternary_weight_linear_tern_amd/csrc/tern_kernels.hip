@@ -1528,6 +1528,11 @@ void gemm_rd_kernel(GroupArgs ga) {
             // issue order, and the next two chunks then need no wait behind
             // the 256 stores
             wait_vm<0>();
+            // the explicit AGPR reads below are inline asm, which the
+            // compiler's hazard tracking does not see: 24 wait states cover
+            // an MFMA result read by a VALU instruction (the tile's last MFMAs
+            // are far behind already)
+            if constexpr (MODE == MODE_FWD) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
             float scl[4];
             uint32_t vcol[4];
             const uint32_t vb = (uint32_t)((4 * h * ldo + l32) * EB);
