@@ -51,11 +51,10 @@ def parse():
                          "and dW each on their own branch (after the materialize); p3 (single-projection "
                          "calls only) = whole projections dealt over three branches; auto: layer calls take 3 "
                          "when the forward or dX product of the layer has fewer 256 x 256 tiles than the GPU "
-                         "has compute units (small products, whose latencies then overlap), 1 when those tiles "
-                         "do not divide evenly over the compute units (the planner balances such a product "
-                         "over all units, which a concurrent product would disturb), else 2; single calls "
-                         "take p3 when some projection's forward or dX has fewer tiles than compute units, "
-                         "else 2")
+                         "has compute units (small products, whose latencies then overlap), else 1 (every "
+                         "product fills the chip on its own, and a concurrent one only competes for its L2 "
+                         "and clock); single calls take p3 when some projection's forward or dX has fewer "
+                         "tiles than compute units, else 2")
     ap.add_argument("--api", default="layer", choices=["layer", "projection"],
                     help="layer (default): one call per product for all projections (tern_layer_*); "
                          "projection: the single-projection calls, one per projection and product")
@@ -405,7 +404,7 @@ def main():
         tiles = lambda m, n: -(-m // 256) * -(-n // 256)
         if layer:
             items = (sum(tiles(d["n_out"], w.T) for d in projs), sum(tiles(d["n_in"], w.T) for d in projs))
-            mode = "3" if min(items) < cus else ("1" if any(i % cus for i in items) else "2")
+            mode = "3" if min(items) < cus else "1"
         else:
             small = any(min(tiles(d["n_out"], w.T), tiles(d["n_in"], w.T)) < cus for d in projs)
             mode = "p3" if small else "2"

@@ -833,6 +833,7 @@ void gemm_dw_kernel(GroupArgs ga) {
     int64_t irem = 0;                          // token rows of the item from chunk ic on
     int64_t lda = 0, ldb = 0;                  // bytes per token row of the item's operands
     DmaTok da, db;
+    int tcx = 0, tcy = 0;                      // features of the item's X / dY panel inside M / N
     bool iv = g_item(ga, 0, ipi, itm, itn, isp);
     auto set_itile = [&]() __attribute__((always_inline)) {
         const GemmArgs &ig = ga.p[ipi];
@@ -845,6 +846,8 @@ void gemm_dw_kernel(GroupArgs ga) {
         ib = (const char *)ig.act1 + ikbeg * ldb + (int64_t)itn * 256 * ES;
         da.init(lda, ig.M - itm * 256, wave);
         db.init(ldb, ig.N - itn * 256, wave);
+        tcx = ig.M - itm * 256;
+        tcy = ig.N - itn * 256;
     };
     set_itile();
     // record count of rows bytes (rows of ld bytes), saturated to the 31-bit range
@@ -860,6 +863,7 @@ void gemm_dw_kernel(GroupArgs ga) {
 
     f32x16 acc[4][4];
     u32x4 f0a[2][4], f0b[2][4];   // K quarter 0 fragments of the current / next chunk
+    uint32_t tq[2][2] = {{0u, 0u}, {0u, 0u}}, tsink = 0u;   // warm-up loads per chunk slot
     int sc = 0;                   // LDS stage of the current chunk
 
     auto zero_acc = [&]() __attribute__((always_inline)) {
@@ -922,7 +926,8 @@ void gemm_dw_kernel(GroupArgs ga) {
     // first K quarter of a chunk: its 16 MFMAs with the dY half of the refill
     // begun in the previous chunk's last quarter (stage sc ^ 1, one load per
     // two MFMAs), then the issue side's step to the next chunk
-    auto p_mma_dmab = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) __attribute__((always_inline)) {
+    auto p_mma_dmab = [&](const u32x4 (&a)[4], const u32x4 (&b)[4], uint32_t &t0, uint32_t &t1)
+                          __attribute__((always_inline)) {
         char *st = w_lds + (sc ^ 1) * W_STAGE;
         const __amdgpu_buffer_rsrc_t rb = make_rsrc_n(ib, nrec(irem, ldb));
         auto one = [&](auto k_c) __attribute__((always_inline)) {
@@ -955,13 +960,32 @@ void gemm_dw_kernel(GroupArgs ga) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        {
+            // L2 warm-up of the chunk three beyond the one whose refill this
+            // quarter finishes: one 4-byte load per 128-byte line of its X and
+            // dY rows (lane: row 16 wave + lane / 4, line lane % 4).  Its L2
+            // misses, a fifth of the lines, are what the barrier waited on:
+            // their latency now runs under about two chunks of MFMAs, and its
+            // refill finds the lines in L2.  Lanes past the panel's columns and
+            // rows past the item read nothing (out-of-range offset, record
+            // counts of the remaining rows); the values go to a sink.
+            const int trow = wave * 16 + (lane >> 2), tcol = (lane & 3) * 128;
+            constexpr int64_t AHEAD = 3 * W_KC;
+            const __amdgpu_buffer_rsrc_t tx = make_rsrc_n(ia + AHEAD * lda, nrec(irem - AHEAD, lda));
+            const __amdgpu_buffer_rsrc_t ty = make_rsrc_n(ib + AHEAD * ldb, nrec(irem - AHEAD, ldb));
+            const uint32_t ox = tcol < 2 * tcx ? (uint32_t)(trow * lda + tcol) : OOB;
+            const uint32_t oy = tcol < 2 * tcy ? (uint32_t)(trow * ldb + tcol) : OOB;
+            t0 = __builtin_amdgcn_raw_buffer_load_b32(tx, ox, 0, 0);
+            t1 = __builtin_amdgcn_raw_buffer_load_b32(ty, oy, 0, 0);
+        }
         next_chunk();
     };
 
     // one chunk (fragment slot SL): run K quarters 0 .. W_Q - 2, reading each
     // next quarter's fragments during the current one's MFMAs (quarter 0 also
-    // issues the dY half of the previous chunk's refill); wait for the next
-    // chunk's loads in every wave (nothing was issued after them), pass the
+    // issues the dY half of the previous chunk's refill and the warm-up loads);
+    // wait for the next chunk's loads in every wave (only the two warm-up
+    // loads were issued after them), pass the
     // barrier, start the refill of this chunk's stage, read the next chunk's
     // quarter 0 fragments, and run the last quarter's MFMAs (its fragments are
     // already in registers).
@@ -974,7 +998,7 @@ void gemm_dw_kernel(GroupArgs ga) {
         for (int q = 0; q < W_Q - 1; q++) {
             w_read_q(st, qa[(q + 1) & 1], qb[(q + 1) & 1], wm, wn, lane, q + 1);
             if (q == 0) {
-                p_mma_dmab(f0a[SL], f0b[SL]);
+                p_mma_dmab(f0a[SL], f0b[SL], tq[SL][0], tq[SL][1]);
             } else {
                 p_mma(acc, qa[q & 1], qb[q & 1]);
                 // one MFMA, then one of the next quarter's 16 transposing reads:
@@ -987,7 +1011,11 @@ void gemm_dw_kernel(GroupArgs ga) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        w_barrier<0>();
+        // all but the two warm-up loads issued last
+        w_barrier<2>();
+        // the previous chunk's warm-up loads are older than this barrier's
+        // wait: folding them costs no wait
+        tsink ^= tq[SL1][0] ^ tq[SL1][1];
         // every wave has read all of this chunk's stage: its refill with the
         // chunk after the next one starts during the last quarter (the X half)
         const int sfree = sc;
@@ -1126,6 +1154,10 @@ void gemm_dw_kernel(GroupArgs ga) {
     // the last issues were out-of-range loads still writing zeros into the
     // stages: drain them before the workgroup ends
     wait_vm0();
+    // the warm-up values are never used; a store under a condition the
+    // compiler cannot decide (no group has a negative count) keeps the loads
+    tsink ^= tq[0][0] ^ tq[0][1] ^ tq[1][0] ^ tq[1][1];
+    if (ga.n < 0) ga.p[0].part[threadIdx.x] = __builtin_bit_cast(float, tsink);
 }
 
 // ---------------------------------------------------------------------------
