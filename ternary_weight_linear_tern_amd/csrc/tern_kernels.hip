@@ -29,6 +29,17 @@
 //     hardware deals workgroups round-robin over the 8 XCDs) and walks tiles in
 //     groups of 8 along M, so tiles resident on one XCD share operand panels in
 //     that XCD's L2.
+//   * The bf16 256 x 256 products run persistent kernels over a group of
+//     problems (all projections of a layer), walked statically or in balanced
+//     classes of workgroups (group_item, tern_plan.h):
+//     - gemm_rd_kernel (forward, dX): no workgroup barrier; each wave streams
+//       its activation rows through a private ring of four LDS stages, decodes
+//       the fp4 fragment copy of tern in registers, runs the MFMAs with the
+//       activations as A (the tile lands transposed in the accumulators) and
+//       stores whole lines straight from them;
+//     - gemm_dw_kernel (dW): two shared 64-token stages of X and dY with
+//       transposing LDS reads, one barrier per stage, and 4-byte L2 warm-up
+//       loads for the chunk three beyond each refill.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
