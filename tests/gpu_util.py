@@ -94,7 +94,11 @@ def check_elements(o, p, got, want, rows=None, cols=None, tag="", slack=None):
     operand it rounds:  |got - want| <= (u_op + 2 (K + 2) 2^-24) * S,  where
     S = sum |a| |b| over the element's products (the oracle's own product of
     the absolute values), K the length of that sum (in for Y, out for dX, T for
-    gq and sgrad) and u_op = 2^-8 for dX with bf16 activations (its scale is
+    gq and sgrad) plus the fp32 sums added on top of it: up to 32 split
+    partials of G (gq), and for sgrad also the in-tile sum over a 256-row tile
+    (64 sequential adds in a lane, then the lane pair and the two waves: 66,
+    counted as 33 since the formula doubles K), so K = T + 32 for gq and
+    T + 32 + 33 for sgrad; u_op = 2^-8 for dX with bf16 activations (its scale is
     rounded to bf16 inside the operand), else 0.  A misplaced or stale element
     is off by about sqrt(K) typical terms, far beyond this bound, even where
     one element barely moves the relative L2 norm.  slack: optional per-output
@@ -113,7 +117,7 @@ def check_elements(o, p, got, want, rows=None, cols=None, tag="", slack=None):
     if "gq" in got or "sgrad" in got:
         _, S["gq"], S["sgrad"] = o.linear_wgrad(aX, adY, aq, p.theta, asc, cols=cols)
     u_op = dict(Y=0.0, dX=2.0 ** -8 if p.act == "bf16" else 0.0, gq=0.0, sgrad=0.0)
-    K = dict(Y=n_in, dX=n_out, gq=T, sgrad=T)
+    K = dict(Y=n_in, dX=n_out, gq=T + 32, sgrad=T + 32 + 33)
     for k in [k for k in ("Y", "dX", "gq", "sgrad") if k in got]:
         err = np.abs(np.asarray(got[k], dtype=np.float64) - want[k])
         bound = (u_op[k] + 2.0 * (K[k] + 2) * 2.0 ** -24) * S[k] + 1e-30
