@@ -189,3 +189,24 @@ def test_layer_class_walk_mid_block():
     _compare(projs, ref, "mid block")
     _oracle_check(projs, host, "mid block", rows=12, cols=8)
     log("  layer mid block (class walk): equal to the single calls, oracle gate met")
+
+
+def test_layer_bf16_y():
+    """bf16 Y through the layer call (its own kernel instantiation, 2-byte
+    stores from the transposed accumulators) equals the single-projection
+    bf16 Y bit for bit, and the round-to-nearest-even of the fp32 Y."""
+    shapes = [(1032, 520), (520, 1032), (256, 256)]
+    projs, host = _make(1000, shapes, config_id=1608)
+    tl.tern_layer_materialize(projs, 2)
+    for d in projs:
+        d["Y"] = torch.empty((1000, d["n_out"]), dtype=torch.bfloat16, device="cuda")
+    tl.tern_layer_fwd(projs)
+    torch.cuda.synchronize()
+    for i, d in enumerate(projs):
+        yb = torch.empty_like(d["Y"])
+        tl.tern_linear_fwd(d["X"], d["packed"], d["scale"], yb)
+        yf = torch.empty((1000, d["n_out"]), device="cuda")
+        tl.tern_linear_fwd(d["X"], d["packed"], d["scale"], yf)
+        torch.cuda.synchronize()
+        assert torch.equal(d["Y"], yb), f"[{i}] layer bf16 Y differs from tern_linear_fwd"
+        assert torch.equal(d["Y"], yf.to(torch.bfloat16)), f"[{i}] bf16 Y is not the RNE of the fp32 Y"
