@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--cpu-cols", type=int, default=768, help="oracle sample: output columns per projection")
     ap.add_argument("--cpu-1t-div", type=int, default=16,
                     help="the 1-thread oracle runs on 1/N of the all-thread sample's rows and columns")
+    ap.add_argument("--no-vendor-gemm", action="store_true",
+                    help="skip the context line: dense bf16 torch.mm (hipBLASLt) on the same three products")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy a 1 GiB buffer 3 times (known bytes, for scaling "
                          "HBM traffic counters)")
@@ -508,6 +510,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    vendor = None if a.no_vendor_gemm else vendor_gemm(w, projs, peak)
+
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(w, projs, a.cpu_rows, a.cpu_cols, a.cpu_1t_div)
@@ -542,8 +546,68 @@ def main():
         "part_alg_hbm_gbs": {p: round(alg_bytes[p] / (part_ms[p] * 1e-3) / 1e9, 1) for p in PARTS},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "vendor_gemm": vendor,
     }
     print(json.dumps(line), flush=True)
+
+
+def vendor_gemm(w, projs, peak, reps=5):
+    """Context, not this library: the vendor's dense bf16 GEMM (torch.mm, which
+    dispatches to hipBLASLt) on the step's three products for every projection,
+    with a dense bf16 weight matrix W[r][c] = bf16(scale[c] * tern[r][c]) and
+    fp32 outputs like the library's: Y = X W, dX = dY W^T (W^T stored
+    contiguous), G = X^T dY (X^T a transposed view: both operands token-major,
+    as the library reads them).  No materialize, no scale epilogue, no gq or
+    sgrad.  Timed as one sequence of the three products per repetition, after
+    two untimed ones; each product's median over the repetitions."""
+    import torch
+
+    mats = []
+    for d in projs:
+        q = d["q"]
+        tern = (q >= d["theta"]).to(torch.float32) - (q <= -d["theta"]).to(torch.float32)
+        W = (tern * d["scale"][None, :]).to(torch.bfloat16)
+        mats.append((d["X"], d["dY"], W, W.t().contiguous()))
+        del tern
+    f32 = torch.float32
+
+    def fwd():
+        for X, dY, W, WT in mats:
+            torch.mm(X, W, out_dtype=f32)
+
+    def dx():
+        for X, dY, W, WT in mats:
+            torch.mm(dY, WT, out_dtype=f32)
+
+    def dw():
+        for X, dY, W, WT in mats:
+            torch.mm(X.t(), dY, out_dtype=f32)
+
+    parts = {"fwd": fwd, "bwd_dx": dx, "bwd_dw": dw}
+    try:
+        for _ in range(2):
+            for f in parts.values():
+                f()
+        torch.cuda.synchronize()
+    except RuntimeError as e:  # an mm with out_dtype the build does not offer
+        return {"error": str(e).splitlines()[0][:200]}
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+          for k in parts}
+    for i in range(reps):
+        for k, f in parts.items():
+            ev[k][i][0].record()
+            f()
+            ev[k][i][1].record()
+    torch.cuda.synchronize()
+    med = {k: statistics.median(a.elapsed_time(b) for a, b in ev[k]) for k in parts}
+    ms = sum(med.values())
+    tf = 3 * 2.0 * w.T * w.sum_in_out / (ms * 1e-3) / 1e12
+    del mats
+    torch.cuda.empty_cache()
+    return {"kind": "dense bf16 torch.mm (hipBLASLt), fp32 out, same shapes, context only",
+            "value": round(tf, 2), "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+            "ms_per_step": round(ms, 4), "part_ms_median": {k: round(v, 4) for k, v in med.items()},
+            "reps": reps}
 
 
 def algorithmic_bytes(part: str, T: int, n_in: int, n_out: int, es: int) -> float:
