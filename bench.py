@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--cpu-cols", type=int, default=768, help="oracle sample: output columns per projection")
     ap.add_argument("--cpu-1t-div", type=int, default=16,
                     help="the 1-thread oracle runs on 1/N of the all-thread sample's rows and columns")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the board-power window (the step repeated for about 1.5 s after the timed region "
+                         "while the board's power sensor is sampled)")
     ap.add_argument("--no-vendor-gemm", action="store_true",
                     help="skip the context line: dense bf16 torch.mm (hipBLASLt) on the same three products")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -447,8 +450,13 @@ def main():
             torch.cuda.synchronize()
             ms_per_step = g0.elapsed_time(g1) / a.steps
             step_ms = [e0.elapsed_time(e1) for e0, e1 in rev]
+            power = None if a.no_power else board_power(lambda: tl.tern_graph_launch(graph, gs), ms_per_step)
         finally:
             tl.tern_graph_destroy(graph)
+    elif not a.no_power:
+        power = board_power(step, ms_per_step)
+    else:
+        power = None
 
     # per step, summed over projections: the mean over the timed steps, and
     # each part's median over the steps
@@ -547,8 +555,67 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "vendor_gemm": vendor,
+        "power": power if power is None else dict(power, tflop_per_j=round(tflops / power["mean_w"], 4),
+                                                 j_per_step=round(power["mean_w"] * ms_per_step * 1e-3, 4)),
     }
     print(json.dumps(line), flush=True)
+
+
+def power_sensor():
+    """The board's power sensor (amdgpu hwmon power1_input, microwatts), or None."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input")):
+        try:
+            int(open(f).read())
+            return f
+        except (OSError, ValueError):
+            continue
+    return None
+
+
+def board_power(run_once, step_ms, seconds=1.5):
+    """Mean board power while the step repeats for about `seconds`: a host
+    thread reads the sensor every 5 ms; the first 30 % of the window, while the
+    clock settles, is left out.  Also the cap (power1_cap).  None without a
+    readable sensor."""
+    import threading
+
+    import torch
+
+    f = power_sensor()
+    if f is None:
+        return None
+    read = lambda: int(open(f).read()) / 1e6  # noqa: E731
+    try:
+        cap = int(open(f.replace("power1_input", "power1_cap")).read()) / 1e6
+    except (OSError, ValueError):
+        cap = None
+    torch.cuda.synchronize()
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            samples.append((time.time(), read()))
+            time.sleep(0.005)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    batch = max(1, int(50.0 / max(step_ms, 1e-3)))   # about 50 ms of steps per synchronisation
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < seconds:
+        for _ in range(batch):
+            run_once()
+        n += batch
+        torch.cuda.synchronize()
+    t1 = time.time()
+    stop.set()
+    th.join()
+    win = [v for t, v in samples if t0 + 0.3 * (t1 - t0) <= t <= t1]
+    if not win:
+        return None
+    return {"mean_w": round(statistics.mean(win), 1), "max_w": round(max(win), 1), "cap_w": cap,
+            "window_s": round(t1 - t0, 2), "steps": n, "samples": len(win), "sensor": f}
 
 
 def vendor_gemm(w, projs, peak, reps=5):
