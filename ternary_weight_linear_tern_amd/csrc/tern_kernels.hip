@@ -10,15 +10,20 @@
 // Design on CDNA4 (not a translation of the page's K80 kernels, which
 // materialise W_eff in fp32 and call cuBLAS):
 //   * tern is stored 2-bit packed (16 codes per u32) and is never expanded in
-//     HBM.  The GEMMs read the packed words, decode them in registers and stage
-//     the bf16 (or fp32) operand tile in LDS.
+//     HBM.  The GEMMs read the packed words (or a fragment-ordered copy of
+//     them) and decode them in registers: the generic kernel below stages the
+//     decoded bf16 (or fp32) operand tile in LDS, the persistent forward / dX
+//     kernel decodes straight into MFMA operand registers.
 //   * Forward: the scale multiplies the fp32 column sums in the epilogue.
 //     dX: the scale sits on the reduction index, so it is folded into the
 //     decoded operand as +-bf16(scale[c]) (fp32 path: exact +-scale[c]).
 //     dW: the epilogue writes gq = G * scale[c] and reduces G * tern over the
 //     tile's rows in a fixed order into per-row-tile partials; a second kernel
 //     sums the partials in ascending row-tile order (deterministic sgrad).
-//   * One GEMM template: 256 threads = 4 wave64s in 2 x 2, each wave owning a
+//   * One generic GEMM template (fp32, tiles below 256 x 256, and the bf16
+//     cases the persistent kernels do not take: K < 32, a dW side below 256,
+//     the two-term dX scale): 256 threads = 4 wave64s in 2 x 2, each wave
+//     owning a
 //     (BM/2) x (BN/2) block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, or
 //     v_mfma_f32_32x32x2_f32 for fp32).  Operands are staged through
 //     double-buffered LDS tiles whose rows are 128 bytes of K plus 16 bytes of
