@@ -9,6 +9,8 @@
   order, so the device results equal the oracle's f64 results bit for bit.
 * A non-finite activation in token row t + 1 leaves row t of Y (and of dX)
   untouched: the kernels read no activation bytes past the reduction length.
+* A NaN scale poisons its own columns of Y and gq and, in dX, what each path's
+  operand makes of NaN * tern (see test_nonfinite_scale).
 
 Shapes are chosen so that all three products run the 256 x 256 persistent
 kernels (ragged in every dimension, the dW product split over tokens) and, for
@@ -123,3 +125,38 @@ def test_nonfinite_next_row_does_not_leak():
     assert torch.equal(d.dX[keep], dX0[keep]), "a non-finite dY element changed another token row of dX"
     for t in rows:
         assert bool(torch.isfinite(d.Y[t]).all()) and bool(torch.isfinite(d.dX[t]).all())
+
+
+@pytest.mark.parametrize("T,n_in,n_out,act", [(1000, 1032, 1032, "bf16"), (300, 264, 136, "f32")])
+def test_nonfinite_scale(o, T, n_in, n_out, act):
+    """A NaN scale[c]: the forward multiplies column c's sums by it, so Y[:, c]
+    and gq[:, c] are NaN and every other column is unchanged; sgrad does not
+    involve the scale.  dX: the fp32 path multiplies the decoded code by the
+    scale, so W_eff[:, c] = NaN * tern is NaN even where the code is 0 and every
+    dX entry is NaN, as in the oracle; the bf16 persistent kernel builds its
+    operand as +-bf16(scale) selected by the code (a zero code gives an exact
+    0, NaN * 0 is never formed), so dX[t, r] is NaN where tern[r, c] != 0 and
+    bitwise unchanged where it is 0.  Non-finite inputs have no parity gate;
+    this pins what each path does."""
+    log(f"non-finite scale {T}x{n_in}x{n_out} {act}")
+    p = synth.make_inputs(T, n_in, n_out, act=act, config_id=1304)
+    d = DeviceProjection(p)
+    d.step()
+    r0 = d.results()
+    c = 37
+    d.scale[c] = float("nan")
+    d.step()
+    r = d.results()
+    other = [j for j in range(n_out) if j != c]
+    assert np.all(np.isnan(r["Y"][:, c])) and np.array_equal(r["Y"][:, other], r0["Y"][:, other])
+    assert np.all(np.isnan(r["gq"][:, c])) and np.array_equal(r["gq"][:, other], r0["gq"][:, other])
+    assert np.array_equal(r["sgrad"], r0["sgrad"]), "sgrad does not involve the scale"
+    nz = o.tern(p.q, p.theta)[:, c] != 0
+    assert nz.any() and (~nz).any()
+    assert np.all(np.isnan(r["dX"][:, nz])), "dX rows whose code meets the NaN scale must be NaN"
+    if act == "f32":
+        assert np.all(np.isnan(r["dX"])), "fp32 path: W_eff = NaN * tern poisons every dX entry"
+        assert np.all(np.isnan(o.linear_dx(p.dY, p.q, p.theta, np.where(np.arange(n_out) == c, np.nan,
+                                                                          p.scale).astype(np.float32))))
+    else:
+        assert np.array_equal(r["dX"][:, ~nz], r0["dX"][:, ~nz]), "bf16 fold: a zero code contributes exactly 0"
