@@ -37,11 +37,12 @@
 //   * The bf16 256 x 256 products run persistent kernels over a group of
 //     problems (all projections of a layer), walked statically or in balanced
 //     classes of workgroups (group_item, tern_plan.h):
-//     - gemm_rd_kernel (forward, dX): no workgroup barrier; each wave streams
-//       its activation rows through a private ring of four LDS stages, decodes
-//       the fp4 fragment copy of tern in registers, runs the MFMAs with the
-//       activations as A (the tile lands transposed in the accumulators) and
-//       stores whole lines straight from them;
+//     - gemm_rd_kernel (forward, dX): the two waves that read the same 128
+//       activation rows stream them through a shared ring of four LDS stages,
+//       each loading half, with one workgroup barrier per chunk; each wave
+//       decodes the fp4 fragment copy of tern in registers, runs the MFMAs
+//       with the activations as A (the tile lands transposed in the
+//       accumulators) and stores whole lines straight from them;
 //     - gemm_dw_kernel (dW): two shared 64-token stages of X and dY with
 //       transposing LDS reads, one barrier per stage, and 4-byte L2 warm-up
 //       loads for the chunk three beyond each refill.
@@ -1286,18 +1287,23 @@ __device__ __forceinline__ void derive_block(const int8_t *__restrict__ q, int64
 }
 
 // ---------------------------------------------------------------------------
-// Forward and dX GEMM without workgroup barriers (bf16, 256 x 256 tiles,
-// persistent).  Each wave computes its 128 x 128 block on its own:
-//   * its 128 activation rows (X or dY) stream into a private ring of four LDS
-//     stages, 32 K per chunk, with direct-to-LDS buffer loads issued three
-//     chunks ahead, together with the chunk's fragment words (and, for dX, the
-//     chunk's 32 scales);
+// Forward and dX GEMM (bf16, 256 x 256 tiles, persistent).  Each wave
+// computes its 128 x 128 block:
+//   * its 128 activation rows (X or dY) stream into a ring of four LDS stages,
+//     32 K per chunk, with direct-to-LDS buffer loads issued three chunks
+//     ahead, together with the wave's fragment words of the chunk (and, for dX,
+//     the chunk's 32 scales).  The two waves that read the same rows share
+//     their stages and each loads half of them (the swapped kernels below);
 //   * the ternary operand is decoded from the fragment words straight into
 //     MFMA operand registers: never staged as bf16;
-//   * a wave waits only on its own loads (vmcnt), never on another wave.
-// The two waves that share activation rows (or fragment words) load them from
-// L1.  The forward epilogue multiplies by scale[c] (staged in LDS when the tile
-// starts); the dX operand carries +-bf16(scale[c]).
+//   * each wave waits on its own loads (vmcnt); one workgroup barrier per
+//     chunk, right after that wait, makes the partner's half visible and, as
+//     every wave has finished reading the previous chunk's stage by then, frees
+//     that stage for the refill issued in the next chunk.
+// The two waves that share fragment words load them from L1.  The forward
+// epilogue multiplies by scale[c] (staged in LDS when the tile starts); the dX
+// operand carries +-bf16(scale[c]).  The accumulating dX keeps a private ring
+// per wave and no barrier (its epilogue transposes through a free stage).
 // ---------------------------------------------------------------------------
 constexpr int R_KC = 32;                         // K per chunk
 constexpr int R_NST = 4;                         // LDS stages per wave
@@ -1307,6 +1313,13 @@ constexpr int R_S = 256;                         // dX scales of a stage (one 4-
 constexpr int R_STAGE = R_B + R_A + R_S;         // 9472
 constexpr int R_ESC = 4 * 512;                   // forward: scales of four tiles x 128 rows
 constexpr int R_WAVE = R_NST * R_STAGE + R_ESC;  // 39936
+// Shared layout (the swapped kernels): the two waves that read the same 128
+// activation rows (same wn) share their stages, each loading 64 of the rows;
+// fragment words, dX scales and the epilogue's scales stay per wave.
+constexpr int R_PS = R_A + R_S;                      // per-wave part of a stage
+constexpr int R_SH_ACT = 2 * R_NST * R_B;            // 64 KB: two pairs x four stages
+constexpr int R_SH_WAVE = R_NST * R_PS + R_ESC;      // 7168
+static_assert(R_SH_ACT + 4 * R_SH_WAVE <= 4 * R_WAVE, "shared layout fits the LDS array");
 __shared__ __attribute__((aligned(16))) char r_lds[4 * R_WAVE];
 
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void *lds_wave_base, uint32_t voff) {
@@ -1367,12 +1380,23 @@ void gemm_rd_kernel(GroupArgs ga) {
     // operands swapped in the MFMAs (transposed accumulators, epilogue below)
     constexpr bool SWAP = !ACC;
     constexpr int ES = 2;
-    // vector memory operations per chunk issue: 8 activation + 1 fragment (+ 1 scale)
-    constexpr int OPS = MODE == MODE_DX ? 10 : 9;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
     char *wl = r_lds + wave * R_WAVE;
+    // SHARE: the swapped kernels share each pair's activation stages (one
+    // workgroup barrier per chunk orders the two halves); the accumulating dX
+    // keeps private stages (its epilogue transposes through a free stage).
+    constexpr bool SHARE = SWAP;
+    char *const a_base = SHARE ? r_lds + wn * (R_NST * R_B) : wl;    // activation rows of stage 0
+    constexpr int A_STRIDE = SHARE ? R_B : R_STAGE;
+    char *const p_base = SHARE ? r_lds + R_SH_ACT + wave * R_SH_WAVE : wl + R_B;   // fragment words of stage 0
+    constexpr int P_STRIDE = SHARE ? R_PS : R_STAGE;
+    char *const e_base = SHARE ? r_lds + R_SH_ACT + wave * R_SH_WAVE + R_NST * R_PS : wl + R_NST * R_STAGE;
+    constexpr int NACT = SHARE ? 4 : 8;   // activation loads of this wave per chunk
+    // vector memory operations per chunk issue: the activation loads + 1
+    // fragment (+ 1 scale)
+    constexpr int OPS = NACT + (MODE == MODE_DX ? 2 : 1);
     // slot of this lane's 16 bytes in every DMA row group, and its logical chunk
     const int cb = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
 
@@ -1417,8 +1441,8 @@ void gemm_rd_kernel(GroupArgs ga) {
         pf = g.frag + ((int64_t)itm * nch * 512 + wm * 256);
         nf = __builtin_amdgcn_readfirstlane(iv ? (uint32_t)(nch * 2048 - 1024) : 0u);
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int row = 16 * i + (lane >> 2);
+        for (int i = 0; i < NACT; i++) {
+            const int row = 16 * (SHARE ? 4 * wm + i : i) + (lane >> 2);
             boff[i] = (n0 + row < g.N ? (uint32_t)(row * ld) + (uint32_t)cb : OOB) - 1024u * (uint32_t)(i & 3);
         }
         if constexpr (MODE == MODE_DX) {
@@ -1427,7 +1451,7 @@ void gemm_rd_kernel(GroupArgs ga) {
             // this wave's 128 scales of the tile, for its epilogue
             const int mb = itm * 256 + wm * 128;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scale + mb);
-            char *esc = wl + R_NST * R_STAGE + (ij & 3) * 512;
+            char *esc = e_base + (ij & 3) * 512;
 #pragma unroll
             for (int q = 0; q < 2; q++)
                 dma4(rs, esc + q * 256, mb + 64 * q + lane < g.M ? (uint32_t)(64 * q + lane) * 4u : OOB);
@@ -1442,11 +1466,22 @@ void gemm_rd_kernel(GroupArgs ga) {
     // per four MFMAs per wave instead of a burst of ten.
     auto issue_part = [&](int s, auto p_c) __attribute__((always_inline)) {
         constexpr int P = decltype(p_c)::value;
-        char *st = wl + s * R_STAGE;
-        if constexpr (P < 4) {
+        char *ast = a_base + s * A_STRIDE;
+        char *pst = p_base + s * P_STRIDE;
+        if constexpr (P < 4 && SHARE) {
+            // one load of 16 rows: this wave's rows 16 (4 wm + P) .. + 15 of the pair's stage
             const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(pa, na);
             const int so = ic * R_KC * ES;
-            char *d = st + (P >> 1) * 4096;
+            uint32_t o0 = boff[P];
+            if (so + R_KC * ES > ld32) {
+                // a chunk reaching past K: lanes whose 16 bytes lie past K load nothing
+                if (so + cb >= ld32) o0 = OOB - 1024u * (uint32_t)P;
+            }
+            dma16_imm<P * 1024>(ra, ast + wm * 4096, o0, so);
+        } else if constexpr (P < 4) {
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(pa, na);
+            const int so = ic * R_KC * ES;
+            char *d = ast + (P >> 1) * 4096;
             uint32_t o0 = boff[2 * P], o1 = boff[2 * P + 1];
             if (so + R_KC * ES > ld32) {
                 // a chunk reaching past K (the ragged last one or the padding
@@ -1461,10 +1496,10 @@ void gemm_rd_kernel(GroupArgs ga) {
             dma16_imm<(P & 1) * 2048>(ra, d, o0, so);
             dma16_imm<(P & 1) * 2048 + 1024>(ra, d, o1, so);
         } else {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(pf, nf), (LDS_AS void *)(st + R_B), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(pf, nf), (LDS_AS void *)pst, 16,
                                                      (uint32_t)lane * 16u, ic * 2048, 0, 0);
             if constexpr (MODE == MODE_DX)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(i_scale, ns), (LDS_AS void *)(st + R_B + R_A), 4,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc_n(i_scale, ns), (LDS_AS void *)(pst + R_A), 4,
                                                          soff_lane, ic * R_KC * 4, 0, 0);
             if (++ic == i_nch2) {
                 ic = 0;
@@ -1508,11 +1543,11 @@ void gemm_rd_kernel(GroupArgs ga) {
     // fragment words, quarter-0 activation fragments and scales of stage S
     auto read_ahead = [&](int s, auto sl_c) __attribute__((always_inline)) {
         constexpr int SL = decltype(sl_c)::value;
-        const char *st = wl + s * R_STAGE;
-        fa[SL] = *(const u32x4 *)(st + R_B + lane * 16);
-        r_read_b(st, fb0[SL], l32, h, 0);
+        const char *pst = p_base + s * P_STRIDE;
+        fa[SL] = *(const u32x4 *)(pst + lane * 16);
+        r_read_b(a_base + s * A_STRIDE, fb0[SL], l32, h, 0);
         if constexpr (MODE == MODE_DX) {
-            const float *sc = (const float *)(st + R_B + R_A);
+            const float *sc = (const float *)(pst + R_A);
 #pragma unroll
             for (int kk = 0; kk < 2; kk++) {
                 const f32x4 lo = *(const f32x4 *)(sc + 16 * kk + 8 * h);
@@ -1564,7 +1599,7 @@ void gemm_rd_kernel(GroupArgs ga) {
         const int esz = obf ? 2 : 4;
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc((const char *)g.out_ptr + ((int64_t)nw * ldo + mw) * esz);
-        const float *esc = (const float *)(wl + R_NST * R_STAGE + (cj & 3) * 512);
+        const float *esc = (const float *)(e_base + (cj & 3) * 512);
         // Each lane's column test and scale once per 32-column group fm; the
         // row offsets (rows of ldo elements) in the scalar offset, computed
         // per 32-row group fn from a row pitch the compiler cannot see through
@@ -1711,7 +1746,7 @@ void gemm_rd_kernel(GroupArgs ga) {
     auto chunk = [&](auto sl_c) __attribute__((always_inline)) {
         constexpr int SL = decltype(sl_c)::value, SL1 = SL ^ 1;
         const int sis = (sc + 3) & 3;
-        r_read_b(wl + sc * R_STAGE, fb1, l32, h, 1);
+        r_read_b(a_base + sc * A_STRIDE, fb1, l32, h, 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int f = 0; f < 8; f++) {
@@ -1731,10 +1766,20 @@ void gemm_rd_kernel(GroupArgs ga) {
                 // in LDS and the stores can drain meanwhile); otherwise its 64
                 // stores as well (where 63 waits for more than needed).
                 if constexpr (SWAP) {
-                    if (!hist) wait_vm<OPS + 8>();
+                    if (!hist) wait_vm<OPS + NACT>();
                 } else {
                     wait_vm<63>();
-                    if (!hist) wait_vm<OPS + 8>();
+                    if (!hist) wait_vm<OPS + NACT>();
+                }
+                if constexpr (SHARE) {
+                    // the partner's half of the next chunk: it passed the same
+                    // wait before this barrier.  lgkmcnt(0): this wave's reads
+                    // of the stage the refill after the barrier overwrites
+                    // (the previous chunk's, read at its start) are complete.
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_waitcnt(0xC07F);
+                    __builtin_amdgcn_s_barrier();
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 read_ahead((sc + 1) & 3, std::integral_constant<int, SL1>{});
                 __builtin_amdgcn_sched_barrier(0);
@@ -1767,6 +1812,10 @@ void gemm_rd_kernel(GroupArgs ga) {
     issue(1);
     issue(2);
     wait_vm<2 * OPS>();
+    if constexpr (SHARE) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+    }
     read_ahead(0, I0{});
 #pragma unroll
     for (int j = 0; j < 4; j++) acur[j] = dec(fa[0], p4[0], 0, j);
