@@ -1,9 +1,11 @@
 """Many repetitions of the layer step stay bitwise equal, through the C ABI on the GPU.
 
-The forward / dX kernel has no workgroup barrier: each wave orders its own
-loads and stores by vmcnt arithmetic alone, and the dW kernel's refill runs
-ahead of a barrier.  A wait that came up short would read a stage before its
-data landed and change some outputs from one run to the next.  Every output
+The forward / dX kernel orders each wave's own loads and stores by vmcnt
+arithmetic and has one workgroup barrier per chunk, after which a wave reads
+the half of the shared activation stage that its partner loaded; the
+accumulating dX keeps a private ring and no barrier; the dW kernel's refill
+runs ahead of a barrier.  A wait that came up short would read a stage before
+its data landed and change some outputs from one run to the next.  Every output
 is deterministic (fixed tiles, fixed summation orders), so the step is
 repeated, eagerly and as one graph replay, with the outputs filled with NaN
 before every repetition, and each repetition must equal the first bit for bit.
