@@ -68,7 +68,7 @@ extern "C" {
  *   from word ceil(in*ceil(out/16) / 64) * 64: two fragment-ordered copies of
  *       the same codes, the forward operand (ceil(out/256) * ceil(in/32) * 512
  *       words) then the dX operand (ceil(in/256) * ceil(out/32) * 512 words),
- *       ordered for the loads of the 256 x 256 GEMM kernels.  They carry no
+ *       ordered for the loads of the GEMM kernels.  They carry no
  *       information beyond the canonical matrix. */
 int64_t tern_packed_words(int64_t in, int64_t out);
 

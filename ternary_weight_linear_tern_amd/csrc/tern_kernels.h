@@ -12,8 +12,10 @@ namespace tern {
 
 hipError_t launch_gemm(const GemmPlan &p, bool bf16, const GemmArgs &a, hipStream_t st);
 // One persistent launch over the items of several problems of one mode (bf16
-// activations, 256 x 256 tiles; each problem's arguments complete and checked,
-// forward / dX with K >= 32, dW with M, N >= 256).
+// activations; forward / dX on 512 x 128 tiles, the accumulating dX and dW on
+// 256 x 256 tiles, whatever tiles_m / tiles_n the problems carry; each
+// problem's arguments complete and checked, forward / dX with K >= 32, dW with
+// M, N >= 256).
 hipError_t launch_gemm_group(int mode, const GroupArgs &ga, hipStream_t st);
 // The whole packed handle (canonical words, padding, both fragment-ordered
 // copies; see PackedLayout) from q in one launch.

@@ -34,16 +34,17 @@
 //     hardware deals workgroups round-robin over the 8 XCDs) and walks tiles in
 //     groups of 8 along M, so tiles resident on one XCD share operand panels in
 //     that XCD's L2.
-//   * The bf16 256 x 256 products run persistent kernels over a group of
-//     problems (all projections of a layer), walked statically or in balanced
-//     classes of workgroups (group_item, tern_plan.h):
-//     - gemm_rd_kernel (forward, dX): the two waves that read the same 128
-//       activation rows stream them through a shared ring of four LDS stages,
-//       each loading half, with one workgroup barrier per chunk; each wave
-//       decodes the fp4 fragment copy of tern in registers, runs the MFMAs
-//       with the activations as A (the tile lands transposed in the
+//   * The bf16 products with full tiles run persistent kernels over a group
+//     of problems (all projections of a layer), walked statically or in
+//     balanced classes of workgroups (group_item, tern_plan.h):
+//     - gemm_rd_kernel (forward, dX): 512 x 128 tiles (output columns x
+//       tokens); the four waves, side by side along the columns, stream the
+//       tile's 128 activation rows through one shared ring of four LDS
+//       stages, each loading a quarter, with one workgroup barrier per chunk;
+//       each wave decodes the fp4 fragment copy of tern in registers, runs
+//       the MFMAs with the activations as A (the tile lands transposed in the
 //       accumulators) and stores whole lines straight from them;
-//     - gemm_dw_kernel (dW): two shared 64-token stages of X and dY with
+//     - gemm_dw_kernel (dW, 256 x 256 tiles): two shared 64-token stages of X and dY with
 //       transposing LDS reads, one barrier per stage, and 4-byte L2 warm-up
 //       loads for the chunk three beyond each refill.
 #include <hip/hip_runtime.h>
@@ -1287,13 +1288,13 @@ __device__ __forceinline__ void derive_block(const int8_t *__restrict__ q, int64
 }
 
 // ---------------------------------------------------------------------------
-// Forward and dX GEMM (bf16, 256 x 256 tiles, persistent).  Each wave
-// computes its 128 x 128 block:
+// Forward and dX GEMM (bf16, persistent; 512 x 128 tiles, the accumulating
+// dX 256 x 256).  Each wave computes its 128 x 128 block:
 //   * its 128 activation rows (X or dY) stream into a ring of four LDS stages,
 //     32 K per chunk, with direct-to-LDS buffer loads issued three chunks
 //     ahead, together with the wave's fragment words of the chunk (and, for dX,
-//     the chunk's 32 scales).  The two waves that read the same rows share
-//     their stages and each loads half of them (the swapped kernels below);
+//     the chunk's 32 scales).  In a 512 x 128 tile all four waves read the
+//     same rows: they share the stages and each loads a quarter of them;
 //   * the ternary operand is decoded from the fragment words straight into
 //     MFMA operand registers: never staged as bf16;
 //   * each wave waits on its own loads (vmcnt); one workgroup barrier per
@@ -1313,13 +1314,14 @@ constexpr int R_S = 256;                         // dX scales of a stage (one 4-
 constexpr int R_STAGE = R_B + R_A + R_S;         // 9472
 constexpr int R_ESC = 4 * 512;                   // forward: scales of four tiles x 128 rows
 constexpr int R_WAVE = R_NST * R_STAGE + R_ESC;  // 39936
-// Shared layout (the swapped kernels): the two waves that read the same 128
-// activation rows (same wn) share their stages, each loading 64 of the rows;
-// fragment words, dX scales and the epilogue's scales stay per wave.
+// Wide layout (the swapped kernels): a 512 x 128 tile (columns x tokens), the
+// four waves side by side along the columns, all reading the same 128
+// activation rows from one shared ring of stages, each wave loading 32 of the
+// rows; fragment words, dX scales and the epilogue's scales stay per wave.
 constexpr int R_PS = R_A + R_S;                      // per-wave part of a stage
-constexpr int R_SH_ACT = 2 * R_NST * R_B;            // 64 KB: two pairs x four stages
+constexpr int R_SH_ACT = R_NST * R_B;                // 32 KB: four stages of 128 rows
 constexpr int R_SH_WAVE = R_NST * R_PS + R_ESC;      // 7168
-static_assert(R_SH_ACT + 4 * R_SH_WAVE <= 4 * R_WAVE, "shared layout fits the LDS array");
+static_assert(R_SH_ACT + 4 * R_SH_WAVE <= 4 * R_WAVE, "wide layout fits the LDS array");
 __shared__ __attribute__((aligned(16))) char r_lds[4 * R_WAVE];
 
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void *lds_wave_base, uint32_t voff) {
@@ -1382,18 +1384,21 @@ void gemm_rd_kernel(GroupArgs ga) {
     constexpr int ES = 2;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, h = lane >> 5;
-    char *wl = r_lds + wave * R_WAVE;
-    // SHARE: the swapped kernels share each pair's activation stages (one
-    // workgroup barrier per chunk orders the two halves); the accumulating dX
-    // keeps private stages (its epilogue transposes through a free stage).
+    // SHARE: the swapped kernels run 512 x 128 tiles whose four waves share
+    // one ring of activation stages (one workgroup barrier per chunk orders
+    // the four quarters); the accumulating dX runs 256 x 256 tiles (2 x 2
+    // waves of 128 x 128) with private stages (its epilogue transposes through
+    // a free stage).  wm: the wave's 128 columns, wn: its 128 tokens.
     constexpr bool SHARE = SWAP;
-    char *const a_base = SHARE ? r_lds + wn * (R_NST * R_B) : wl;    // activation rows of stage 0
+    constexpr int TM = SHARE ? 512 : 256, TN = SHARE ? 128 : 256;   // tile: columns x tokens
+    const int wm = SHARE ? wave : wave >> 1, wn = SHARE ? 0 : wave & 1, l32 = lane & 31, h = lane >> 5;
+    char *wl = r_lds + wave * R_WAVE;
+    char *const a_base = SHARE ? r_lds : wl;    // activation rows of stage 0
     constexpr int A_STRIDE = SHARE ? R_B : R_STAGE;
     char *const p_base = SHARE ? r_lds + R_SH_ACT + wave * R_SH_WAVE : wl + R_B;   // fragment words of stage 0
     constexpr int P_STRIDE = SHARE ? R_PS : R_STAGE;
     char *const e_base = SHARE ? r_lds + R_SH_ACT + wave * R_SH_WAVE + R_NST * R_PS : wl + R_NST * R_STAGE;
-    constexpr int NACT = SHARE ? 4 : 8;   // activation loads of this wave per chunk
+    constexpr int NACT = SHARE ? 2 : 8;   // activation loads of this wave per chunk
     // vector memory operations per chunk issue: the activation loads + 1
     // fragment (+ 1 scale)
     constexpr int OPS = NACT + (MODE == MODE_DX ? 2 : 1);
@@ -1431,25 +1436,28 @@ void gemm_rd_kernel(GroupArgs ga) {
         const int64_t ld = (int64_t)g.K * ES;
         ld32 = g.K * ES;
         i_scale = g.scale;
-        const int n0 = itn * 256 + wn * 128;
+        const int n0 = itn * TN + wn * 128;
         // bytes from this wave's first row to the end of the tensor (integer
         // arithmetic only: the int64 min / max overloads go through f64)
         int64_t rem = (int64_t)(g.N - n0) * ld;
         rem = (!iv || rem < 0) ? 0 : (rem > 0x7FFFFFF0 ? 0x7FFFFFF0 : rem);
         pa = (const char *)g.act0 + (int64_t)n0 * ld;
         na = __builtin_amdgcn_readfirstlane((uint32_t)rem);
-        pf = g.frag + ((int64_t)itm * nch * 512 + wm * 256);
-        nf = __builtin_amdgcn_readfirstlane(iv ? (uint32_t)(nch * 2048 - 1024) : 0u);
+        // the fragment copy is cut in 256-column tiles: this wave's 128
+        // columns are half hf of tile ft, which exists if it starts below M
+        const int ft = (itm * TM + wm * 128) >> 8, hf = wm & 1;
+        pf = g.frag + ((int64_t)ft * nch * 512 + hf * 256);
+        nf = __builtin_amdgcn_readfirstlane(iv && ft * 256 < g.M ? (uint32_t)(nch * 2048 - 1024) : 0u);
 #pragma unroll
         for (int i = 0; i < NACT; i++) {
-            const int row = 16 * (SHARE ? 4 * wm + i : i) + (lane >> 2);
+            const int row = 16 * (SHARE ? NACT * wave + i : i) + (lane >> 2);
             boff[i] = (n0 + row < g.N ? (uint32_t)(row * ld) + (uint32_t)cb : OOB) - 1024u * (uint32_t)(i & 3);
         }
         if constexpr (MODE == MODE_DX) {
             ns = __builtin_amdgcn_readfirstlane(iv ? (uint32_t)g.K * 4u : 0u);
         } else if (iv) {
             // this wave's 128 scales of the tile, for its epilogue
-            const int mb = itm * 256 + wm * 128;
+            const int mb = itm * TM + wm * 128;
             const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.scale + mb);
             char *esc = e_base + (ij & 3) * 512;
 #pragma unroll
@@ -1459,17 +1467,19 @@ void gemm_rd_kernel(GroupArgs ga) {
     };
     set_itile();
 
-    // Part p of the issue of chunk ic into stage s: parts 0-3 are two
-    // activation loads each (8 in all), part 4 the fragment words (and, dX,
-    // the scales) and the step to the next chunk.  The chunk loop spreads the
-    // parts over its first five fragments, so the texture unit sees two loads
-    // per four MFMAs per wave instead of a burst of ten.
+    // Part p of the issue of chunk ic into stage s: parts 0-3 are the
+    // activation loads (wide tiles: one each in parts 0 and 1, 32 rows per
+    // wave; private stages: two each, 8 in all), part 4 the fragment words
+    // (and, dX, the scales) and the step to the next chunk.  The chunk loop
+    // spreads the parts over its first five fragments, so the texture unit
+    // sees the loads between the MFMAs instead of in one burst.
     auto issue_part = [&](int s, auto p_c) __attribute__((always_inline)) {
         constexpr int P = decltype(p_c)::value;
         char *ast = a_base + s * A_STRIDE;
         char *pst = p_base + s * P_STRIDE;
         if constexpr (P < 4 && SHARE) {
-            // one load of 16 rows: this wave's rows 16 (4 wm + P) .. + 15 of the pair's stage
+            if constexpr (P >= NACT) return;   // wide tiles: parts 2 and 3 issue nothing
+            // one load of 16 rows: rows 16 (NACT wave + P) .. + 15 of the shared stage
             const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(pa, na);
             const int so = ic * R_KC * ES;
             uint32_t o0 = boff[P];
@@ -1477,7 +1487,7 @@ void gemm_rd_kernel(GroupArgs ga) {
                 // a chunk reaching past K: lanes whose 16 bytes lie past K load nothing
                 if (so + cb >= ld32) o0 = OOB - 1024u * (uint32_t)P;
             }
-            dma16_imm<P * 1024>(ra, ast + wm * 4096, o0, so);
+            dma16_imm<P * 1024>(ra, ast + wave * (NACT * 1024), o0, so);
         } else if constexpr (P < 4) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(pa, na);
             const int so = ic * R_KC * ES;
@@ -1593,7 +1603,7 @@ void gemm_rd_kernel(GroupArgs ga) {
     // operand panels in L2).  bf16 Y: 2-byte stores, 64-byte halves of lines.
     auto epilogue = [&]() __attribute__((always_inline)) {
         const GemmArgs &g = ga.p[cpi];
-        const int mw = ctm * 256 + wm * 128, nw = ctn * 256 + wn * 128;
+        const int mw = ctm * TM + wm * 128, nw = ctn * TN + wn * 128;
         const int ldo = MODE == MODE_FWD ? g.out : g.in;
         constexpr bool obf = YBF;
         const int esz = obf ? 2 : 4;
@@ -2076,6 +2086,7 @@ hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
             ga.start[0] = 0;
             ga.start[1] = (int)(p.tiles_m * p.tiles_n * p.splits);
             ga.p[0] = a;
+            if (MODE != MODE_DW && !rd_items(ga)) return hipErrorInvalidValue;
             const int64_t items = ga.start[1], cus = device_cus();
             return launch_persistent<MODE>(ga, items < cus ? items : cus, st);
         }
@@ -2092,6 +2103,8 @@ hipError_t launch_mode(const GemmPlan &p, const GemmArgs &a, hipStream_t st) {
 hipError_t launch_gemm_group(int mode, const GroupArgs &ga_in, hipStream_t st) {
     if (ga_in.n < 1 || ga_in.n > kMaxGroup) return hipErrorInvalidValue;
     GroupArgs ga = ga_in;
+    // the forward / dX items follow the kernel's tile, whatever the caller cut
+    if (mode != MODE_DW && !rd_items(ga)) return hipErrorInvalidValue;
     int64_t cost[kMaxGroup];
     for (int p = 0; p < ga.n; p++)
         cost[p] = mode == MODE_DW ? cdiv(ga.p[p].kps, dev::W_KC) : (int64_t)ga.p[p].nch;

@@ -3,8 +3,9 @@
 // all weight gradients (declared in include/tern.h, tern_layer_*).
 //
 // The page's trainer runs every projection's kernels one after another and is
-// launch-bound; here the work items of all projections of one product (256 x
-// 256 output tiles, times the splits over tokens for dW) form one item space
+// launch-bound; here the work items of all projections of one product (output
+// tiles: 512 x 128 for the forward and dX, 256 x 256 times the splits over
+// tokens for dW) form one item space
 // that a persistent grid walks, so small projections fill the chip together
 // and pay one launch.  A projection that the grouped kernels do not take
 // (fp32 activations, a reduction shorter than 32, a dX whose scale is carried
@@ -193,14 +194,13 @@ int tern_layer_fwd(const tern_proj_t *p, int32_t n, int64_t T, int32_t act_dtype
         a.scale = q.scale;
         a.out_ptr = q.Y;
         a.M = (int)q.out; a.N = (int)T; a.K = (int)q.in;
-        a.tiles_m = (int)cdiv(q.out, 256); a.tiles_n = (int)cdiv(T, 256);
         a.splits = 1; a.kps = (int)q.in;
         a.in = (int)q.in; a.out = (int)q.out; a.wpr = (int)cdiv(q.out, 16); a.T = (int)T;
         a.y_bf16 = y_dtype == TERN_BF16;
         a.nch = (int)cdiv(q.in, kFragChunk);
     }
     if (m > 0) {
-        if (!finish_group(ga)) return TERN_ERR_SHAPE;
+        if (!rd_items(ga)) return TERN_ERR_SHAPE;
         rc = hip_status(launch_gemm_group(MODE_FWD, ga, st));
         if (rc) return rc;
     }
@@ -253,13 +253,12 @@ int tern_layer_bwd_dx(const tern_proj_t *p, int32_t n, int64_t T, int32_t act_dt
         a.scale = q.scale;
         a.out_ptr = q.dX;
         a.M = (int)q.in; a.N = (int)T; a.K = (int)q.out;
-        a.tiles_m = (int)cdiv(q.in, 256); a.tiles_n = (int)cdiv(T, 256);
         a.splits = 1; a.kps = (int)q.out;
         a.in = (int)q.in; a.out = (int)q.out; a.wpr = (int)cdiv(q.out, 16); a.T = (int)T;
         a.nch = (int)cdiv(q.out, kFragChunk);
     }
     if (m > 0) {
-        if (!finish_group(ga)) return TERN_ERR_SHAPE;
+        if (!rd_items(ga)) return TERN_ERR_SHAPE;
         rc = hip_status(launch_gemm_group(MODE_DX, ga, st));
         if (rc) return rc;
     }

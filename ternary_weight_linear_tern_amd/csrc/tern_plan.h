@@ -144,6 +144,28 @@ TERN_HD inline bool group_item(const GroupArgs &ga, int G, int b, int j, int &pi
     return true;
 }
 
+// Items of the persistent forward / dX kernels: 512 x 128 tiles (output
+// columns x tokens) for the plain products, 256 x 256 for the accumulating dX
+// (every problem of a launch is one or the other, as p[0].acc says); fills
+// each problem's tiles_m / tiles_n and the item starts.  False when the items
+// do not fit the walk's int range.
+inline bool rd_items(GroupArgs &ga) {
+    const bool wide = !ga.p[0].acc;
+    int64_t total = 0;
+    for (int i = 0; i < ga.n; i++) {
+        GemmArgs &a = ga.p[i];
+        const int64_t bm = wide ? 512 : 256, bn = wide ? 128 : 256;
+        const int64_t tm = (a.M + bm - 1) / bm, tn = (a.N + bn - 1) / bn;
+        ga.start[i] = (int)total;
+        total += tm * tn * a.splits;
+        if (total > (int64_t(1) << 30)) return false;
+        a.tiles_m = (int)tm;
+        a.tiles_n = (int)tn;
+    }
+    ga.start[ga.n] = (int)total;
+    return true;
+}
+
 // Chooses the walk of a group launch on `cus` compute units and fills its
 // fields; returns the grid (0 for no items).  cost[p]: length of problem p's
 // items (K steps).  Each item also pays about 2 steps of prologue and
@@ -219,8 +241,9 @@ int validate_shape(int64_t T, int64_t in, int64_t out);
 // matrix comes first; two fragment-ordered copies of it follow, one for the
 // forward operand (rows m = output columns, K = input rows) and one for the dX
 // operand (rows m = input rows, K = output columns).  Each copy holds, per
-// tile of 256 rows and chunk of 32 K, 512 words in the order the 256 x 256
-// GEMMs load them (one 16-byte load per lane and chunk).
+// tile of 256 rows and chunk of 32 K, 512 words in the order the persistent
+// GEMMs load them (one 16-byte load per lane and chunk; a 512-column tile of
+// the forward / dX kernel reads two such tiles).
 constexpr int64_t kFragTileRows = 256;
 constexpr int64_t kFragChunk = 32;
 constexpr int64_t kFragWords = 512;   // words per (tile, chunk)

@@ -176,6 +176,30 @@ int main() {
         CHECK(walks[WALK_STATIC] > 0 && walks[WALK_DYNAMIC] + walks[WALK_CLASSES] > 0 && walks[WALK_CLASSES] > 0);
         std::printf("walks over random groups: static %d, dynamic %d, classes %d\n", walks[0], walks[1], walks[2]);
     }
+    // forward / dX items: 512 x 128 tiles (columns x tokens), 256 x 256 for
+    // the accumulating dX; ragged edges round up; too many items are refused
+    {
+        GroupArgs ga{};
+        ga.n = 2;
+        ga.p[0].M = 1032; ga.p[0].N = 4000; ga.p[0].splits = 1;
+        ga.p[1].M = 512; ga.p[1].N = 128; ga.p[1].splits = 1;
+        CHECK(rd_items(ga));
+        CHECK(ga.p[0].tiles_m == 3 && ga.p[0].tiles_n == 32 && ga.p[1].tiles_m == 1 && ga.p[1].tiles_n == 1);
+        CHECK(ga.start[0] == 0 && ga.start[1] == 96 && ga.start[2] == 97);
+        ga.p[0].acc = ga.p[1].acc = 1;
+        CHECK(rd_items(ga));
+        CHECK(ga.p[0].tiles_m == 5 && ga.p[0].tiles_n == 16 && ga.p[1].tiles_m == 2 && ga.p[1].tiles_n == 1);
+        CHECK(ga.start[1] == 80 && ga.start[2] == 82);
+        ga.n = 1;
+        ga.p[0].acc = 0; ga.p[0].M = 1 << 20; ga.p[0].N = 2147483647;
+        CHECK(!rd_items(ga));
+        // the mid layer's forward on these tiles (d = 1024: 2 x 64 items; ffn
+        // 8 x 64 and 2 x 64 with 128 chunks) walks every item once
+        int walk = -1;
+        check_walk({{2, 64, 1, 128}, {8, 64, 1, 32}, {2, 64, 1, 32}, {2, 64, 1, 32}, {2, 64, 1, 32},
+                    {2, 64, 1, 32}}, 256, &walk);
+        CHECK(walk == WALK_CLASSES || walk == WALK_STATIC);
+    }
     if (fails) {
         std::fprintf(stderr, "%d checks failed\n", fails);
         return 1;

@@ -29,8 +29,7 @@ def test_planner_launch_checks(tmp_path):
            os.path.join(ROOT, "ternary_weight_linear_tern_amd", "csrc", "tern_plan.cpp"), "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
-    env = dict(os.environ)
-    env.pop("LD_PRELOAD", None)
+    env = dict(os.environ, ASAN_OPTIONS="verify_asan_link_order=0")
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
 
