@@ -50,7 +50,7 @@ def parse():
                     help="graph branches of the recorded step: 1 = one chain; 2 = dW on its own branch; 3 = dX "
                          "and dW each on their own branch (after the materialize); p3 (single-projection "
                          "calls only) = whole projections dealt over three branches; auto: layer calls take 3 "
-                         "when the forward or dX product of the layer has fewer 256 x 256 tiles than the GPU "
+                         "when the forward or dX product of the layer has fewer 512 x 128 tiles than the GPU "
                          "has compute units (small products, whose latencies then overlap), else 1 (every "
                          "product fills the chip on its own, and a concurrent one only competes for its L2 "
                          "and clock); single calls take p3 when some projection's forward or dX has fewer "
@@ -406,7 +406,7 @@ def main():
     step_ms = [evs[k][0][0].elapsed_time(evs[k][last][4]) for k in range(a.steps)]
     if a.streams == "auto":
         cus = torch.cuda.get_device_properties(0).multi_processor_count
-        tiles = lambda m, n: -(-m // 256) * -(-n // 256)
+        tiles = lambda m, n: -(-m // 512) * -(-n // 128)   # the forward / dX kernels' items
         if layer:
             items = (sum(tiles(d["n_out"], w.T) for d in projs), sum(tiles(d["n_in"], w.T) for d in projs))
             mode = "3" if min(items) < cus else "1"

@@ -12,7 +12,7 @@
 * A NaN scale poisons its own columns of Y and gq and, in dX, what each path's
   operand makes of NaN * tern (see test_nonfinite_scale).
 
-Shapes are chosen so that all three products run the 256 x 256 persistent
+Shapes are chosen so that all three products run the persistent
 kernels (ragged in every dimension, the dW product split over tokens) and, for
 comparison, the fp32 path.
 """

@@ -226,7 +226,7 @@ def sampled_case(o, wname, proj):
     check_elements(o, p, got, want, rows=rows, cols=cols, tag=f"{wname}/{name}")
 
 
-# Shapes on which every product takes the 256 x 256 kernels with ragged edges:
+# Shapes on which every product takes the persistent kernels with ragged edges:
 # M and N off the tile grid, K off the 32-wide chunk grid with an odd chunk
 # count (the padding chunk), and a token count off the 64-token dW chunk.
 @pytest.mark.parametrize("T,n_in,n_out", [(4000, 1032, 4104), (4000, 4104, 1032)])
@@ -275,7 +275,7 @@ def test_parity_largest_sampled(o, proj):
 def test_parity_operands_beyond_4gib(o):
     """X of 4 GiB (T = 262144 tokens x 8192 bf16) and dX of 8 GiB: tile base
     offsets far past 2^32 bytes, through the same kernels as the benchmark
-    (the 256 x 256 forward / dX and the split-K dW); sampled rows and columns
+    (the 512 x 128 forward / dX and the split-K 256 x 256 dW); sampled rows and columns
     against the oracle."""
     T, n_in, n_out = 262144, 8192, 256
     log(f"parity beyond 4 GiB: T={T} in={n_in} out={n_out}")

@@ -10,7 +10,7 @@ sign, so every output must still meet the oracle:
   bf16 pattern for tern = -1, which must not assume a positive scale;
 * gq = G * scale[c] and sgrad, which does not depend on scale at all.
 
-Shapes cover the persistent 256 x 256 kernels (ragged, dW split over tokens),
+Shapes cover the persistent kernels (ragged, dW split over tokens),
 the two-term dX scale (few columns), the fp32 path and the layer calls.
 Columns with scale 0 give exactly zero Y and gq columns and no dX
 contribution.

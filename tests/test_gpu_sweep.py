@@ -9,8 +9,8 @@ a bf16 Y on some bf16 problems.  Each is materialised, run forward and
 backward, and compared with the oracle: the handle bit for bit, every output
 within the gate, and every fp32 output within its per-element rounding bound.
 Sizes that no hand-picked list contains (tiny T, one 8-wide tile, K not a
-multiple of any chunk) land on every kernel path: the persistent 256 x 256
-kernels, the smaller tiles, the two-term dX scale and the fp32 kernels.
+multiple of any chunk) land on every kernel path: the persistent kernels,
+the smaller tiles, the two-term dX scale and the fp32 kernels.
 Then the problems with equal T go through the layer calls as well, and eight
 larger random ragged shapes run the persistent kernels, compared on sampled
 rows and columns.
@@ -94,7 +94,7 @@ def _big_cases(n=8, seed=2025):
 
 @pytest.mark.parametrize("case", _big_cases(), ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}")
 def test_sweep_large_sampled(o, case):
-    """Random ragged shapes large enough for the persistent 256 x 256 kernels
+    """Random ragged shapes large enough for the persistent kernels
     (T up to 4096, in and out up to 2048, bf16), compared on sampled rows of
     Y and dX and sampled columns of gq and sgrad, each sampled element within
     its rounding bound."""
