@@ -1314,14 +1314,15 @@ constexpr int R_S = 256;                         // dX scales of a stage (one 4-
 constexpr int R_STAGE = R_B + R_A + R_S;         // 9472
 constexpr int R_ESC = 4 * 512;                   // forward: scales of four tiles x 128 rows
 constexpr int R_WAVE = R_NST * R_STAGE + R_ESC;  // 39936
-// Wide layout (the swapped kernels): a 512 x 128 tile (columns x tokens), the
-// four waves side by side along the columns, all reading the same 128
-// activation rows from one shared ring of stages, each wave loading 32 of the
-// rows; fragment words, dX scales and the epilogue's scales stay per wave.
+// Shared layouts (the swapped kernels).  Wide: a 512 x 128 tile (columns x
+// tokens), the four waves side by side along the columns, all reading the
+// same 128 activation rows from one shared ring of stages, each wave loading
+// 32 of the rows.  Pairs: a 256 x 256 tile, 2 x 2 waves; the two waves that
+// read the same 128 rows share a ring, each loading 64 of them.  Fragment
+// words, dX scales and the epilogue's scales stay per wave.
 constexpr int R_PS = R_A + R_S;                      // per-wave part of a stage
-constexpr int R_SH_ACT = R_NST * R_B;                // 32 KB: four stages of 128 rows
 constexpr int R_SH_WAVE = R_NST * R_PS + R_ESC;      // 7168
-static_assert(R_SH_ACT + 4 * R_SH_WAVE <= 4 * R_WAVE, "wide layout fits the LDS array");
+static_assert(2 * R_NST * R_B + 4 * R_SH_WAVE <= 4 * R_WAVE, "shared layouts fit the LDS array");
 __shared__ __attribute__((aligned(16))) char r_lds[4 * R_WAVE];
 
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void *lds_wave_base, uint32_t voff) {
@@ -1372,8 +1373,9 @@ __device__ __forceinline__ uint32_t r_scaled_pair(uint32_t v, uint32_t q) {
     return (v ^ q) & __builtin_amdgcn_perm(0u, 0u, v);
 }
 
-// YBF: bf16 Y (forward only; every problem of a launch has the same Y type)
-template <int MODE, bool ACC = false, bool YBF = false>
+// YBF: bf16 Y (forward only; every problem of a launch has the same Y type).
+// WIDE: 512 x 128 tiles, else 256 x 256 (the accumulating dX: always).
+template <int MODE, bool ACC = false, bool YBF = false, bool WIDE = true>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_rd_kernel(GroupArgs ga) {
     static_assert(MODE == MODE_FWD || MODE == MODE_DX, "forward and dX only");
@@ -1384,21 +1386,27 @@ void gemm_rd_kernel(GroupArgs ga) {
     constexpr int ES = 2;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    // SHARE: the swapped kernels run 512 x 128 tiles whose four waves share
-    // one ring of activation stages (one workgroup barrier per chunk orders
-    // the four quarters); the accumulating dX runs 256 x 256 tiles (2 x 2
-    // waves of 128 x 128) with private stages (its epilogue transposes through
-    // a free stage).  wm: the wave's 128 columns, wn: its 128 tokens.
+    // SHARE: the swapped kernels share their activation stages (one
+    // workgroup barrier per chunk orders the loaders' parts): WIDE, 512 x 128
+    // tiles whose four waves share one ring; else 256 x 256 tiles (2 x 2 waves
+    // of 128 x 128) whose wave pairs with the same rows share a ring.  The
+    // accumulating dX runs 256 x 256 tiles with private stages (its epilogue
+    // transposes through a free stage).  wm: the wave's 128 columns, wn: its
+    // 128 tokens.
     constexpr bool SHARE = SWAP;
-    constexpr int TM = SHARE ? 512 : 256, TN = SHARE ? 128 : 256;   // tile: columns x tokens
-    const int wm = SHARE ? wave : wave >> 1, wn = SHARE ? 0 : wave & 1, l32 = lane & 31, h = lane >> 5;
+    constexpr bool W4 = SHARE && WIDE;
+    constexpr int TM = W4 ? 512 : 256, TN = W4 ? 128 : 256;   // tile: columns x tokens
+    const int wm = W4 ? wave : wave >> 1, wn = W4 ? 0 : wave & 1, l32 = lane & 31, h = lane >> 5;
     char *wl = r_lds + wave * R_WAVE;
-    char *const a_base = SHARE ? r_lds : wl;    // activation rows of stage 0
+    constexpr int SH_ACT = (W4 ? 1 : 2) * R_NST * R_B;   // the shared rings
+    char *const a_base = !SHARE ? wl : r_lds + wn * (R_NST * R_B);    // activation rows of stage 0
     constexpr int A_STRIDE = SHARE ? R_B : R_STAGE;
-    char *const p_base = SHARE ? r_lds + R_SH_ACT + wave * R_SH_WAVE : wl + R_B;   // fragment words of stage 0
+    char *const p_base = SHARE ? r_lds + SH_ACT + wave * R_SH_WAVE : wl + R_B;   // fragment words of stage 0
     constexpr int P_STRIDE = SHARE ? R_PS : R_STAGE;
-    char *const e_base = SHARE ? r_lds + R_SH_ACT + wave * R_SH_WAVE + R_NST * R_PS : wl + R_NST * R_STAGE;
-    constexpr int NACT = SHARE ? 2 : 8;   // activation loads of this wave per chunk
+    char *const e_base = SHARE ? r_lds + SH_ACT + wave * R_SH_WAVE + R_NST * R_PS : wl + R_NST * R_STAGE;
+    // activation loads of this wave per chunk, and its first row in the stage
+    constexpr int NACT = !SHARE ? 8 : W4 ? 2 : 4;
+    const int arow0 = !SHARE ? 0 : W4 ? 32 * wave : 64 * wm;
     // vector memory operations per chunk issue: the activation loads + 1
     // fragment (+ 1 scale)
     constexpr int OPS = NACT + (MODE == MODE_DX ? 2 : 1);
@@ -1450,7 +1458,7 @@ void gemm_rd_kernel(GroupArgs ga) {
         nf = __builtin_amdgcn_readfirstlane(iv && ft * 256 < g.M ? (uint32_t)(nch * 2048 - 1024) : 0u);
 #pragma unroll
         for (int i = 0; i < NACT; i++) {
-            const int row = 16 * (SHARE ? NACT * wave + i : i) + (lane >> 2);
+            const int row = arow0 + 16 * i + (lane >> 2);
             boff[i] = (n0 + row < g.N ? (uint32_t)(row * ld) + (uint32_t)cb : OOB) - 1024u * (uint32_t)(i & 3);
         }
         if constexpr (MODE == MODE_DX) {
@@ -1479,7 +1487,7 @@ void gemm_rd_kernel(GroupArgs ga) {
         char *pst = p_base + s * P_STRIDE;
         if constexpr (P < 4 && SHARE) {
             if constexpr (P >= NACT) return;   // wide tiles: parts 2 and 3 issue nothing
-            // one load of 16 rows: rows 16 (NACT wave + P) .. + 15 of the shared stage
+            // one load of 16 rows: rows arow0 + 16 P .. + 15 of the shared stage
             const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(pa, na);
             const int so = ic * R_KC * ES;
             uint32_t o0 = boff[P];
@@ -1487,7 +1495,7 @@ void gemm_rd_kernel(GroupArgs ga) {
                 // a chunk reaching past K: lanes whose 16 bytes lie past K load nothing
                 if (so + cb >= ld32) o0 = OOB - 1024u * (uint32_t)P;
             }
-            dma16_imm<P * 1024>(ra, ast + wave * (NACT * 1024), o0, so);
+            dma16_imm<P * 1024>(ra, ast + arow0 * 64, o0, so);
         } else if constexpr (P < 4) {
             const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(pa, na);
             const int so = ic * R_KC * ES;
@@ -2064,10 +2072,14 @@ hipError_t launch_persistent(const GroupArgs &ga, int64_t grid, hipStream_t st) 
         hipLaunchKernelGGL(dev::gemm_dw_kernel, pgrid, block, 0, st, ga);
     else if (MODE == MODE_DX && ga.p[0].acc)
         hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE_DX, true>), pgrid, block, 0, st, ga);
+    else if (MODE == MODE_FWD && ga.p[0].y_bf16 && ga.rd_wide)
+        hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE_FWD, false, true, true>), pgrid, block, 0, st, ga);
     else if (MODE == MODE_FWD && ga.p[0].y_bf16)
-        hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE_FWD, false, true>), pgrid, block, 0, st, ga);
+        hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE_FWD, false, true, false>), pgrid, block, 0, st, ga);
+    else if (ga.rd_wide)
+        hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE, false, false, true>), pgrid, block, 0, st, ga);
     else
-        hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE>), pgrid, block, 0, st, ga);
+        hipLaunchKernelGGL((dev::gemm_rd_kernel<MODE, false, false, false>), pgrid, block, 0, st, ga);
     return hipGetLastError();
 }
 

@@ -94,6 +94,7 @@ struct GroupArgs {
     int cls_wg[kMaxClass + 1];      // first workgroup of each class; cls_wg[ncls] = grid
     int cls_cnt[kMaxClass][kMaxGroup];    // items of problem p per workgroup of class k
     int cls_base[kMaxClass][kMaxGroup];   // first item of problem p (within it) taken by class k
+    int rd_wide;                    // forward / dX: 512 x 128 tiles (else 256 x 256), set by rd_items
     GemmArgs p[kMaxGroup];
 };
 
@@ -144,13 +145,27 @@ TERN_HD inline bool group_item(const GroupArgs &ga, int G, int b, int j, int &pi
     return true;
 }
 
-// Items of the persistent forward / dX kernels: 512 x 128 tiles (output
-// columns x tokens) for the plain products, 256 x 256 for the accumulating dX
-// (every problem of a launch is one or the other, as p[0].acc says); fills
-// each problem's tiles_m / tiles_n and the item starts.  False when the items
-// do not fit the walk's int range.
+// Items of the persistent forward / dX kernels, one tile shape per launch:
+// 512 x 128 tiles (output columns x tokens) for the plain products unless
+// their padding makes the launch's multiply-adds more than 3 % above those of
+// 256 x 256 tiles (columns off the 512 grid: 768 columns pad to 1024, against
+// 768), 256 x 256 then and for the accumulating dX (every problem of a launch
+// is plain or accumulating, as p[0].acc says).  Sets rd_wide, each problem's
+// tiles_m / tiles_n and the item starts.  False when the items do not fit the
+// walk's int range.
 inline bool rd_items(GroupArgs &ga) {
-    const bool wide = !ga.p[0].acc;
+    bool wide = !ga.p[0].acc;
+    if (wide) {
+        double w = 0.0, q = 0.0;
+        for (int i = 0; i < ga.n; i++) {
+            const GemmArgs &a = ga.p[i];
+            const int64_t m = a.M, n = a.N;
+            w += double((m + 511) / 512 * 512) * double((n + 127) / 128 * 128) * double(a.K);
+            q += double((m + 255) / 256 * 256) * double((n + 255) / 256 * 256) * double(a.K);
+        }
+        wide = w <= 1.03 * q;
+    }
+    ga.rd_wide = wide ? 1 : 0;
     int64_t total = 0;
     for (int i = 0; i < ga.n; i++) {
         GemmArgs &a = ga.p[i];

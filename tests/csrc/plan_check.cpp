@@ -176,20 +176,31 @@ int main() {
         CHECK(walks[WALK_STATIC] > 0 && walks[WALK_DYNAMIC] + walks[WALK_CLASSES] > 0 && walks[WALK_CLASSES] > 0);
         std::printf("walks over random groups: static %d, dynamic %d, classes %d\n", walks[0], walks[1], walks[2]);
     }
-    // forward / dX items: 512 x 128 tiles (columns x tokens), 256 x 256 for
+    // forward / dX items: 512 x 128 tiles (columns x tokens) unless their
+    // column padding costs more than 3 % over 256 x 256 tiles, 256 x 256 for
     // the accumulating dX; ragged edges round up; too many items are refused
     {
         GroupArgs ga{};
         ga.n = 2;
-        ga.p[0].M = 1032; ga.p[0].N = 4000; ga.p[0].splits = 1;
-        ga.p[1].M = 512; ga.p[1].N = 128; ga.p[1].splits = 1;
+        ga.p[0].M = 2048; ga.p[0].N = 4000; ga.p[0].K = 2048; ga.p[0].splits = 1;
+        ga.p[1].M = 512; ga.p[1].N = 128; ga.p[1].K = 512; ga.p[1].splits = 1;
         CHECK(rd_items(ga));
-        CHECK(ga.p[0].tiles_m == 3 && ga.p[0].tiles_n == 32 && ga.p[1].tiles_m == 1 && ga.p[1].tiles_n == 1);
-        CHECK(ga.start[0] == 0 && ga.start[1] == 96 && ga.start[2] == 97);
-        ga.p[0].acc = ga.p[1].acc = 1;
+        CHECK(ga.rd_wide == 1);
+        CHECK(ga.p[0].tiles_m == 4 && ga.p[0].tiles_n == 32 && ga.p[1].tiles_m == 1 && ga.p[1].tiles_n == 1);
+        CHECK(ga.start[0] == 0 && ga.start[1] == 128 && ga.start[2] == 129);
+        ga.p[0].M = 1032;   // 1536 padded columns against 1280: square tiles
         CHECK(rd_items(ga));
+        CHECK(ga.rd_wide == 0);
         CHECK(ga.p[0].tiles_m == 5 && ga.p[0].tiles_n == 16 && ga.p[1].tiles_m == 2 && ga.p[1].tiles_n == 1);
         CHECK(ga.start[1] == 80 && ga.start[2] == 82);
+        ga.p[0].M = 768; ga.p[0].K = 1;   // 768 columns pad to 1024 wide, but that problem is light
+        ga.p[1].M = 4096; ga.p[1].N = 8192; ga.p[1].K = 4096;
+        CHECK(rd_items(ga));
+        CHECK(ga.rd_wide == 1);
+        ga.p[0].M = 2048; ga.p[0].K = 2048;
+        ga.p[0].acc = ga.p[1].acc = 1;
+        CHECK(rd_items(ga));
+        CHECK(ga.rd_wide == 0 && ga.p[0].tiles_m == 8 && ga.p[0].tiles_n == 16);
         ga.n = 1;
         ga.p[0].acc = 0; ga.p[0].M = 1 << 20; ga.p[0].N = 2147483647;
         CHECK(!rd_items(ga));
