@@ -722,10 +722,6 @@ constexpr int W_STAGE = 2 * W_OP;
 __shared__ __attribute__((aligned(16))) char w_lds[W_NST * W_STAGE];
 __shared__ float w_red[2 * 256];         // cross-wave sgrad partials of a tile
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void *lds_wave_base, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void *)lds_wave_base, 16, voff, 0, 0, 0);
-}
-
 // 16 bytes per lane to LDS at lds + IMM + 16 lane from voff + soff + IMM; the
 // immediate moves both addresses and is covered by the range check.
 template <int IMM>
